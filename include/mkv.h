@@ -1,0 +1,175 @@
+/*
+ * mkv.h -- C ABI of a MosaicKV-style compressed KV cache for AMD MI355X (gfx950).
+ *
+ * Method: arXiv 2607.00760, "MosaicKV: Serving Long-Context LLM with Dynamic Two-D KV Cache Compression".
+ *   - dynamic two-D compression (section 1, Observation & Approach 1): keys and values are rotated by an SVD
+ *     basis, every KV vector keeps its own most important channels, and the cache is cut into segments that
+ *     each get their own compression strategy;
+ *   - compact sparse attention (section 1, Observation & Approach 2): the sparse cache is packed into a dense
+ *     format in GPU memory and attention runs on it without unpacking;
+ *   - query-aware token selection at run time (section 1, the paragraph on prior sequence compression), kept
+ *     together with channel compression through selection and attention (section 1, Challenge 1).
+ * The pages fix no numbers for segments, strategies or budgets; this library takes: 64-token segments, kept
+ * channel counts {128, 64, 32} chosen per segment as the smallest count that keeps >= 90% of every vector's
+ * squared L2 norm, equal magnitudes broken toward the lower channel index, and a per-request token budget T.
+ *
+ * Conventions for every call:
+ *   - [host] pointers are CPU memory read during the call only; [dev] pointers are HIP device memory of the
+ *     current device.
+ *   - The caller allocates all device memory (store, scratch, workspace, outputs); the library never calls
+ *     hipMalloc/hipFree.  Sizes come from the *_bytes calls.
+ *   - Device work is enqueued on the given stream and is asynchronous unless a call says it synchronises.
+ *   - Every argument check runs on the host before anything is enqueued; on failure nothing is launched, the
+ *     call returns MKV_E_ARG or MKV_E_UNSUPPORTED and mkv_last_error() says why.  A failed launch returns
+ *     MKV_E_DEVICE.  No C++ exception crosses this boundary.
+ *   - Preconditions not checked: finite inputs (NaN/Inf give unspecified results) and an orthonormal basis.
+ */
+#ifndef MKV_H
+#define MKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* mkv_stream_t; /* a hipStream_t; NULL is the legacy default stream */
+
+typedef enum {
+    MKV_OK = 0,
+    MKV_E_ARG = 1,          /* invalid argument, shape, or undersized buffer */
+    MKV_E_UNSUPPORTED = 2,  /* valid but not supported by this build (e.g. head_dim != 128) */
+    MKV_E_DEVICE = 3        /* a HIP call or kernel launch failed */
+} mkv_status;
+
+typedef enum { MKV_FP32 = 0, MKV_BF16 = 1 } mkv_dtype;
+
+#define MKV_HEAD_DIM 128
+#define MKV_SEG_LEN 64
+#define MKV_MAX_KEEP 4
+#define MKV_MAX_GROUP 8        /* query heads per KV head */
+
+/* Compression strategy set (the pages' "compression strategy" per KV-cache segment).
+ * keep[0..n_keep) are kept-channel counts, strictly decreasing, keep[0] == 128, each in {128, 64, 32, 16}.
+ * A vector admits count c when the sum of squares of its c largest-magnitude stored values is
+ * >= energy_frac * (sum of squares of all its stored values), both sums in float64.  A segment takes the
+ * smallest count every vector in it admits; its code is that count's index in keep[]. */
+typedef struct {
+    int32_t seg_len;      /* must be 64 */
+    int32_t n_keep;       /* 1..4 */
+    int32_t keep[MKV_MAX_KEEP];
+    double energy_frac;   /* in (0, 1]; default 0.9 */
+} mkv_seg_policy;
+
+/* Shape of a batch of per-request KV caches for one layer. */
+typedef struct {
+    int32_t batch;               /* requests, >= 1 */
+    int32_t n_kv_heads;          /* >= 1 */
+    int32_t head_dim;            /* must be 128 */
+    mkv_dtype dtype;             /* storage dtype of K, V, q and of the packed values */
+    const int64_t* cu_seqlens;   /* [host] [batch+1], cu_seqlens[0] == 0, non-decreasing; request r owns tokens
+                                    [cu_seqlens[r], cu_seqlens[r+1]) (a request may be empty) */
+    const void* K;               /* [dev] [cu_seqlens[batch]][n_kv_heads][128] token-major, contiguous */
+    const void* V;               /* [dev] same layout as K */
+} mkv_kv_desc;
+
+typedef struct mkv_store mkv_store;   /* opaque host handle */
+
+/* Fills *policy with the default strategy set: seg_len 64, keep {128, 64, 32}, energy_frac 0.9. */
+void mkv_default_policy(mkv_seg_policy* policy);
+
+/* Worst-case store size (every segment at 128 channels) and the scratch size mkv_compress needs.
+ * Host-only; enqueues nothing. */
+mkv_status mkv_compress_bytes(const mkv_kv_desc* kv, const mkv_seg_policy* policy,
+                              size_t* store_bytes, size_t* scratch_bytes);
+
+/* Dynamic two-D compression of K and V (section 1, Observation & Approach 1 of the pages).
+ *   basis   [dev] float32 [batch][n_kv_heads][2][128][128] (index 2: 0 = K basis, 1 = V basis), row-major,
+ *           columns are basis vectors: a stored vector is round_dtype(x @ B).  NULL: K and V are already rotated
+ *           (they are stored as given) and decode applies no query/output rotation.  The store keeps a copy.
+ *   store_buf [dev] >= store_bytes from mkv_compress_bytes, 256-byte aligned; the handle points into it, so it
+ *           must outlive the handle.  scratch [dev] >= scratch_bytes, 256-byte aligned, free after the call.
+ *   On success *out receives a new handle (release with mkv_store_destroy).  The packing runs asynchronously on
+ *   `stream`; decode calls enqueued after it on the same stream see the finished store.
+ * Store layout (all offsets from store_buf, see mkv_store_view): a segment is 64 consecutive tokens of one
+ * (request r, KV head h, tensor X) stream from token 0 on, the last one shorter when n_r % 64 != 0.  Segments
+ * are numbered X*S + n_kv_heads*seg_base[r] + h*S_r + s with S_r = ceil(n_r/64), seg_base[r] = sum_{r'<r} S_r',
+ * S = n_kv_heads * sum_r S_r.  Segment g has a uint8 code (index into policy.keep, c = keep[code]) and a uint64
+ * byte offset into the payload; its payload is [n_s][c] values of the storage dtype, followed, when c < 128, by
+ * [n_s][c] uint8 channel indices; each token's channels are in ascending order and values follow that order. */
+mkv_status mkv_compress(const mkv_kv_desc* kv, const float* basis, const mkv_seg_policy* policy,
+                        void* store_buf, size_t store_bytes, void* scratch, size_t scratch_bytes,
+                        mkv_stream_t stream, mkv_store** out);
+
+/* Wraps a handle around a store buffer that already holds a store of the documented layout for this shape
+ * (e.g. one restored from a file or written by a test).  kv->K and kv->V are ignored.  has_basis says whether
+ * the buffer's basis region is valid.  Enqueues nothing. */
+mkv_status mkv_store_attach(const mkv_kv_desc* kv, const mkv_seg_policy* policy, int32_t has_basis,
+                            void* store_buf, size_t store_bytes, mkv_store** out);
+
+typedef struct {
+    int32_t batch, n_kv_heads, head_dim;
+    mkv_dtype dtype;
+    mkv_seg_policy policy;
+    int32_t has_basis;
+    int64_t total_tokens;        /* cu_seqlens[batch] */
+    int64_t segments_per_tensor; /* S above */
+    const int64_t* cu_seqlens;   /* [host] owned by the handle */
+    void* codes;                 /* [dev] uint8 [2][S] */
+    void* seg_off;               /* [dev] uint64 [2][S], byte offsets into payload */
+    void* basis;                 /* [dev] float32 [batch][n_kv_heads][2][128][128], or NULL */
+    void* payload;               /* [dev] */
+    void* payload_total;         /* [dev] uint64: payload bytes in use, written by mkv_compress */
+    uint64_t payload_capacity;   /* bytes available at payload */
+    uint64_t store_bytes;        /* bytes of the whole store buffer */
+} mkv_store_info;
+
+/* Device addresses and host metadata of a store (for tests, export, and custom consumers). */
+mkv_status mkv_store_view(const mkv_store* store, mkv_store_info* info);
+
+/* Payload bytes in use (sum over all segments of both tensors).  SYNCHRONISES `stream`. */
+mkv_status mkv_store_payload_bytes(const mkv_store* store, mkv_stream_t stream, uint64_t* bytes);
+
+/* Frees the host handle only (the store buffer stays the caller's). NULL is accepted. */
+mkv_status mkv_store_destroy(mkv_store* store);
+
+/* Workspace bytes mkv_decode_attn needs for this store, query head count and budgets T [host] [batch]. */
+mkv_status mkv_decode_workspace_bytes(const mkv_store* store, int32_t n_q_heads, const int32_t* T,
+                                      size_t* ws_bytes);
+
+/* One decode step of attention over the compressed store (section 1 of the pages: query-aware token
+ * selection, then compact sparse attention without unpacking).  For request r and KV head g:
+ *   q'_h = q_h @ B_K for the query heads h of group g (h / (n_q_heads/n_kv_heads) == g);
+ *   Qbar = sum of the group's q'_h;  score_j = sum over token j's stored channels i of Qbar_i * k_j,i;
+ *   Sel = the min(T[r], n_r) tokens of largest score (equal scores: lower token index first);
+ *   out_h = (sum_{j in Sel} softmax_j(q'_h . k_j / sqrt(128)) * v_j) @ B_V^T  (dropped channels count as 0).
+ *   q    [dev] [batch][n_q_heads][128] in the store's dtype; n_q_heads a multiple of n_kv_heads, group <= 8.
+ *   T    [host] [batch], each >= 1 (values above n_r select every token).
+ *   out  [dev] float32 [batch][n_q_heads][128]; an empty request (n_r == 0) gets zeros.
+ *   sel  [dev] int32 [batch][n_kv_heads][sel_stride] or NULL: the selected token indices of each (r, g) in
+ *        ascending order, -1 after the first min(T[r], n_r) entries; sel_stride >= max_r min(T[r], n_r).
+ *   ws   [dev] >= mkv_decode_workspace_bytes, 256-byte aligned; contents are scratch.
+ * Concurrent calls on different streams may share one store if each has its own workspace. */
+mkv_status mkv_decode_attn(const mkv_store* store, const void* q, int32_t n_q_heads, const int32_t* T,
+                           float* out, int32_t* sel, int32_t sel_stride, void* ws, size_t ws_bytes,
+                           mkv_stream_t stream);
+
+/* Text of the last error on the calling thread; valid until the next call on that thread. */
+const char* mkv_last_error(void);
+
+/* ---- kernel timing (for benchmarks) --------------------------------------------------------------------
+ * While profiling is on, every kernel the library launches is bracketed by two HIP events recorded on the
+ * launch stream.  mkv_profile_stop synchronises those events and returns, per kernel id, the summed
+ * duration in milliseconds and the launch count (arrays of MKV_PROFILE_KERNELS entries), then clears them.
+ * At most max_launches launches are timed per session (later launches run untimed).  Not thread-safe with
+ * respect to concurrent library calls from other threads. */
+#define MKV_PROFILE_KERNELS 16
+mkv_status mkv_profile_start(int32_t max_launches);
+mkv_status mkv_profile_stop(double* total_ms, int32_t* launches);
+const char* mkv_kernel_name(int32_t kernel_id);   /* NULL when the id is unused */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MKV_H */

@@ -1,0 +1,535 @@
+// Host entry points of the compressed KV cache library: argument checks, buffer layouts, the store handle,
+// launch orchestration and optional kernel timing.  No device memory is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/mkv.h"
+#include "kernels.h"
+
+using namespace mkv;
+
+namespace {
+
+thread_local std::string g_err;
+
+mkv_status fail(mkv_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+constexpr uint64_t kAlign = 256;
+inline uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---- kernel timing --------------------------------------------------------------------------------------
+enum KernelId {
+    K_UPLOAD = 0, K_CMP_DECIDE, K_CMP_SCAN, K_CMP_PACK, K_DEC_PREP, K_SCORE, K_SEL_COUNT, K_SEL_WRITE,
+    K_SEL_FINAL, K_ATTEND, K_COMBINE, K_COUNT
+};
+const char* kKernelNames[K_COUNT] = {"upload", "compress_decide", "compress_scan", "compress_pack", "decode_prep",
+                                     "score", "select_count", "select_write", "select_final", "attend", "combine"};
+
+struct Profiler {
+    std::mutex mu;
+    bool on = false;
+    int max_launches = 0;
+    struct Rec { int kid; hipEvent_t a, b; };
+    std::vector<Rec> recs;
+    std::vector<hipEvent_t> pool;   // created events, reused across sessions
+    size_t used = 0;
+} g_prof;
+
+struct Timed {
+    int kid;
+    hipStream_t s;
+    hipEvent_t a = nullptr, b = nullptr;
+    Timed(int k, hipStream_t st) : kid(k), s(st) {
+        if (!g_prof.on) return;
+        std::lock_guard<std::mutex> lk(g_prof.mu);
+        if ((int)g_prof.recs.size() >= g_prof.max_launches) return;
+        while (g_prof.pool.size() < g_prof.used + 2) {
+            hipEvent_t e;
+            if (hipEventCreate(&e) != hipSuccess) return;
+            g_prof.pool.push_back(e);
+        }
+        a = g_prof.pool[g_prof.used++];
+        b = g_prof.pool[g_prof.used++];
+        (void)hipEventRecord(a, s);
+    }
+    ~Timed() {
+        if (!a) return;
+        (void)hipEventRecord(b, s);
+        std::lock_guard<std::mutex> lk(g_prof.mu);
+        g_prof.recs.push_back({kid, a, b});
+    }
+};
+
+template <class F>
+mkv_status run(int kid, hipStream_t s, F&& f) {
+    hipError_t e;
+    {
+        Timed t(kid, s);
+        e = f();
+    }
+    if (e != hipSuccess) return fail(MKV_E_DEVICE, "launch of %s failed: %s", kKernelNames[kid], hipGetErrorString(e));
+    return MKV_OK;
+}
+
+// Uploads int32 words to device memory through kernel arguments (no host-to-device copy).
+mkv_status upload_words(int32_t* dst, const std::vector<int32_t>& w, size_t from, hipStream_t s) {
+    for (size_t i = from; i < w.size(); i += kUploadWords) {
+        Upload u;
+        u.dst = dst + i;
+        u.n = (int32_t)std::min<size_t>(kUploadWords, w.size() - i);
+        std::memcpy(u.w, w.data() + i, sizeof(int32_t) * u.n);
+        mkv_status st = run(K_UPLOAD, s, [&] { return launch_upload(u, s); });
+        if (st != MKV_OK) return st;
+    }
+    return MKV_OK;
+}
+
+// ---- argument checks ------------------------------------------------------------------------------------
+int dtype_bytes(mkv_dtype d) { return d == MKV_BF16 ? 2 : 4; }
+
+mkv_status check_policy(const mkv_seg_policy* p, mkv_dtype dt) {
+    if (!p) return fail(MKV_E_ARG, "policy is NULL");
+    if (p->seg_len != MKV_SEG_LEN) return fail(MKV_E_UNSUPPORTED, "seg_len must be %d (got %d)", MKV_SEG_LEN, p->seg_len);
+    if (p->n_keep < 1 || p->n_keep > MKV_MAX_KEEP) return fail(MKV_E_ARG, "n_keep must be in [1, %d] (got %d)", MKV_MAX_KEEP, p->n_keep);
+    if (p->keep[0] != MKV_HEAD_DIM) return fail(MKV_E_ARG, "keep[0] must be %d (got %d)", MKV_HEAD_DIM, p->keep[0]);
+    for (int k = 0; k < p->n_keep; ++k) {
+        const int c = p->keep[k];
+        if (c != 128 && c != 64 && c != 32 && c != 16) return fail(MKV_E_UNSUPPORTED, "keep[%d] = %d: supported counts are 128, 64, 32, 16", k, c);
+        if (k > 0 && c >= p->keep[k - 1]) return fail(MKV_E_ARG, "keep[] must be strictly decreasing");
+    }
+    if (dt == MKV_FP32 && p->n_keep > 3) return fail(MKV_E_UNSUPPORTED, "fp32 stores support at most 3 kept counts");
+    if (!(p->energy_frac > 0.0 && p->energy_frac <= 1.0)) return fail(MKV_E_ARG, "energy_frac must be in (0, 1] (got %g)", p->energy_frac);
+    return MKV_OK;
+}
+
+struct Shape {
+    int32_t B = 0, Hkv = 0;
+    mkv_dtype dtype = MKV_BF16;
+    std::vector<int64_t> cu;
+    int64_t total = 0;
+    int64_t S = 0;                 // segments per tensor
+    std::vector<int32_t> segbase;  // per request
+};
+
+mkv_status check_kv(const mkv_kv_desc* kv, bool need_data, Shape* sh) {
+    if (!kv) return fail(MKV_E_ARG, "kv descriptor is NULL");
+    if (kv->batch < 1) return fail(MKV_E_ARG, "batch must be >= 1 (got %d)", kv->batch);
+    if (kv->n_kv_heads < 1) return fail(MKV_E_ARG, "n_kv_heads must be >= 1 (got %d)", kv->n_kv_heads);
+    if (kv->head_dim != MKV_HEAD_DIM) return fail(MKV_E_UNSUPPORTED, "head_dim must be %d (got %d)", MKV_HEAD_DIM, kv->head_dim);
+    if (kv->dtype != MKV_BF16 && kv->dtype != MKV_FP32) return fail(MKV_E_ARG, "unknown dtype %d", (int)kv->dtype);
+    if (!kv->cu_seqlens) return fail(MKV_E_ARG, "cu_seqlens is NULL");
+    if (kv->cu_seqlens[0] != 0) return fail(MKV_E_ARG, "cu_seqlens[0] must be 0");
+    sh->B = kv->batch;
+    sh->Hkv = kv->n_kv_heads;
+    sh->dtype = kv->dtype;
+    sh->cu.assign(kv->cu_seqlens, kv->cu_seqlens + kv->batch + 1);
+    sh->segbase.resize(kv->batch);
+    int64_t segs = 0;
+    for (int r = 0; r < kv->batch; ++r) {
+        const int64_t n = sh->cu[r + 1] - sh->cu[r];
+        if (n < 0) return fail(MKV_E_ARG, "cu_seqlens must be non-decreasing (request %d)", r);
+        sh->segbase[r] = (int32_t)segs;
+        segs += cdiv(n, MKV_SEG_LEN);
+    }
+    sh->total = sh->cu[kv->batch];
+    if (sh->total * (int64_t)sh->Hkv >= (int64_t)INT32_MAX)
+        return fail(MKV_E_UNSUPPORTED, "total tokens x KV heads must stay below 2^31 (got %lld)", (long long)(sh->total * sh->Hkv));
+    sh->S = segs * sh->Hkv;
+    if (need_data && sh->total > 0 && (!kv->K || !kv->V)) return fail(MKV_E_ARG, "K and V must be non-NULL");
+    return MKV_OK;
+}
+
+struct StoreLayout {
+    uint64_t codes, seg_off, basis, payload, capacity, bytes;
+};
+
+StoreLayout store_layout(const Shape& sh) {
+    StoreLayout L;
+    L.codes = kAlign;   // first 256 bytes: header (payload bytes in use)
+    L.seg_off = align_up(L.codes + 2 * (uint64_t)sh.S);
+    L.basis = align_up(L.seg_off + 16 * (uint64_t)sh.S);
+    L.payload = align_up(L.basis + (uint64_t)sh.B * sh.Hkv * 2 * MKV_HEAD_DIM * MKV_HEAD_DIM * sizeof(float));
+    L.capacity = 2ull * sh.Hkv * (uint64_t)sh.total * MKV_HEAD_DIM * dtype_bytes(sh.dtype);
+    L.bytes = L.payload + L.capacity;
+    return L;
+}
+
+struct ScratchLayout {
+    uint64_t tab, thr, bytes;
+};
+ScratchLayout scratch_layout(const Shape& sh) {
+    ScratchLayout L;
+    L.tab = 0;
+    L.thr = align_up(sizeof(int32_t) * (4ull * sh.B + 1));
+    L.bytes = L.thr + 2ull * sh.total * sh.Hkv * 4 * sizeof(uint16_t);
+    return L;
+}
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) % kAlign) == 0; }
+
+}  // namespace
+
+struct mkv_store {
+    Shape sh;
+    mkv_seg_policy policy;
+    int32_t has_basis = 0;
+    StoreLayout lay;
+    uint8_t* base = nullptr;
+};
+
+// ======================================================================================================
+extern "C" {
+
+void mkv_default_policy(mkv_seg_policy* p) {
+    if (!p) return;
+    std::memset(p, 0, sizeof *p);
+    p->seg_len = MKV_SEG_LEN;
+    p->n_keep = 3;
+    p->keep[0] = 128;
+    p->keep[1] = 64;
+    p->keep[2] = 32;
+    p->energy_frac = 0.9;
+}
+
+const char* mkv_last_error(void) { return g_err.c_str(); }
+
+mkv_status mkv_compress_bytes(const mkv_kv_desc* kv, const mkv_seg_policy* policy, size_t* store_bytes,
+                              size_t* scratch_bytes) {
+    Shape sh;
+    mkv_status st = check_kv(kv, false, &sh);
+    if (st) return st;
+    if ((st = check_policy(policy, sh.dtype))) return st;
+    if (!store_bytes || !scratch_bytes) return fail(MKV_E_ARG, "output pointers are NULL");
+    *store_bytes = store_layout(sh).bytes;
+    *scratch_bytes = scratch_layout(sh).bytes;
+    return MKV_OK;
+}
+
+static mkv_status make_handle(const Shape& sh, const mkv_seg_policy* policy, int32_t has_basis, void* buf,
+                              mkv_store** out) {
+    mkv_store* h = new (std::nothrow) mkv_store;
+    if (!h) return fail(MKV_E_ARG, "out of host memory");
+    h->sh = sh;
+    h->policy = *policy;
+    h->has_basis = has_basis;
+    h->lay = store_layout(sh);
+    h->base = static_cast<uint8_t*>(buf);
+    *out = h;
+    return MKV_OK;
+}
+
+mkv_status mkv_compress(const mkv_kv_desc* kv, const float* basis, const mkv_seg_policy* policy, void* store_buf,
+                        size_t store_bytes, void* scratch, size_t scratch_bytes, mkv_stream_t stream_,
+                        mkv_store** out) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    Shape sh;
+    mkv_status st = check_kv(kv, true, &sh);
+    if (st) return st;
+    if ((st = check_policy(policy, sh.dtype))) return st;
+    if (!out) return fail(MKV_E_ARG, "out is NULL");
+    if (!store_buf || !scratch) return fail(MKV_E_ARG, "store_buf and scratch must be non-NULL");
+    if (!aligned(store_buf) || !aligned(scratch)) return fail(MKV_E_ARG, "store_buf and scratch must be 256-byte aligned");
+    const StoreLayout L = store_layout(sh);
+    const ScratchLayout SL = scratch_layout(sh);
+    if (store_bytes < L.bytes) return fail(MKV_E_ARG, "store_bytes %zu < required %llu", store_bytes, (unsigned long long)L.bytes);
+    if (scratch_bytes < SL.bytes) return fail(MKV_E_ARG, "scratch_bytes %zu < required %llu", scratch_bytes, (unsigned long long)SL.bytes);
+
+    uint8_t* base = static_cast<uint8_t*>(store_buf);
+    uint8_t* scr = static_cast<uint8_t*>(scratch);
+    // workgroup chunking: about 4096 workgroups over both tensors
+    const int64_t spw = std::max<int64_t>(1, std::min<int64_t>(64, (2 * sh.S) / 4096));
+    std::vector<int32_t> tab(4 * sh.B + 1);
+    int64_t nblk = 0;
+    for (int r = 0; r < sh.B; ++r) {
+        const int64_t n = sh.cu[r + 1] - sh.cu[r];
+        tab[r] = (int32_t)sh.cu[r];
+        tab[sh.B + r] = (int32_t)n;
+        tab[2 * sh.B + r] = sh.segbase[r];
+        tab[3 * sh.B + r] = (int32_t)nblk;
+        nblk += (int64_t)sh.Hkv * cdiv(cdiv(n, MKV_SEG_LEN), spw);
+    }
+    tab[4 * sh.B] = (int32_t)nblk;
+    if (2 * nblk > INT32_MAX) return fail(MKV_E_UNSUPPORTED, "too many workgroups");
+
+    if ((st = upload_words(reinterpret_cast<int32_t*>(scr + SL.tab), tab, 0, stream))) return st;
+    const float* bcopy = nullptr;
+    if (basis) {
+        const size_t bb = (size_t)sh.B * sh.Hkv * 2 * MKV_HEAD_DIM * MKV_HEAD_DIM * sizeof(float);
+        hipError_t e = hipMemcpyAsync(base + L.basis, basis, bb, hipMemcpyDeviceToDevice, stream);
+        if (e != hipSuccess) return fail(MKV_E_DEVICE, "basis copy failed: %s", hipGetErrorString(e));
+        bcopy = reinterpret_cast<const float*>(base + L.basis);
+    }
+    CmpArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.K = kv->K;
+    a.V = kv->V;
+    a.basis = bcopy;
+    a.tab = reinterpret_cast<const int32_t*>(scr + SL.tab);
+    a.B = sh.B;
+    a.Hkv = sh.Hkv;
+    a.spw = (int32_t)spw;
+    a.nblk = (int32_t)nblk;
+    a.S = sh.S;
+    a.total_tokens = sh.total;
+    a.codes = base + L.codes;
+    a.seg_off = reinterpret_cast<uint64_t*>(base + L.seg_off);
+    a.payload = base + L.payload;
+    a.thr = reinterpret_cast<uint16_t*>(scr + SL.thr);
+    for (int k = 0; k < 4; ++k) a.keep[k] = k < policy->n_keep ? policy->keep[k] : 0;
+    a.n_keep = policy->n_keep;
+    a.frac = policy->energy_frac;
+    const int dt = sh.dtype == MKV_BF16 ? 1 : 0;
+    uint64_t* total = reinterpret_cast<uint64_t*>(base);
+    if ((st = run(K_CMP_DECIDE, stream, [&] { return launch_cmp_decide(a, dt, stream); }))) return st;
+    if ((st = run(K_CMP_SCAN, stream, [&] { return launch_cmp_scan(a.seg_off, 2 * sh.S, total, stream); }))) return st;
+    if ((st = run(K_CMP_PACK, stream, [&] { return launch_cmp_pack(a, dt, stream); }))) return st;
+    return make_handle(sh, policy, basis ? 1 : 0, store_buf, out);
+}
+
+mkv_status mkv_store_attach(const mkv_kv_desc* kv, const mkv_seg_policy* policy, int32_t has_basis, void* store_buf,
+                            size_t store_bytes, mkv_store** out) {
+    Shape sh;
+    mkv_status st = check_kv(kv, false, &sh);
+    if (st) return st;
+    if ((st = check_policy(policy, sh.dtype))) return st;
+    if (!out || !store_buf) return fail(MKV_E_ARG, "store_buf and out must be non-NULL");
+    if (!aligned(store_buf)) return fail(MKV_E_ARG, "store_buf must be 256-byte aligned");
+    const StoreLayout L = store_layout(sh);
+    if (store_bytes < L.bytes) return fail(MKV_E_ARG, "store_bytes %zu < required %llu", store_bytes, (unsigned long long)L.bytes);
+    return make_handle(sh, policy, has_basis ? 1 : 0, store_buf, out);
+}
+
+mkv_status mkv_store_view(const mkv_store* s, mkv_store_info* info) {
+    if (!s || !info) return fail(MKV_E_ARG, "store and info must be non-NULL");
+    std::memset(info, 0, sizeof *info);
+    info->batch = s->sh.B;
+    info->n_kv_heads = s->sh.Hkv;
+    info->head_dim = MKV_HEAD_DIM;
+    info->dtype = s->sh.dtype;
+    info->policy = s->policy;
+    info->has_basis = s->has_basis;
+    info->total_tokens = s->sh.total;
+    info->segments_per_tensor = s->sh.S;
+    info->cu_seqlens = s->sh.cu.data();
+    info->codes = s->base + s->lay.codes;
+    info->seg_off = s->base + s->lay.seg_off;
+    info->basis = s->has_basis ? s->base + s->lay.basis : nullptr;
+    info->payload = s->base + s->lay.payload;
+    info->payload_total = s->base;
+    info->payload_capacity = s->lay.capacity;
+    info->store_bytes = s->lay.bytes;
+    return MKV_OK;
+}
+
+mkv_status mkv_store_payload_bytes(const mkv_store* s, mkv_stream_t stream, uint64_t* bytes) {
+    if (!s || !bytes) return fail(MKV_E_ARG, "store and bytes must be non-NULL");
+    hipError_t e = hipMemcpyAsync(bytes, s->base, sizeof(uint64_t), hipMemcpyDeviceToHost, reinterpret_cast<hipStream_t>(stream));
+    if (e == hipSuccess) e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(MKV_E_DEVICE, "payload size read failed: %s", hipGetErrorString(e));
+    return MKV_OK;
+}
+
+mkv_status mkv_store_destroy(mkv_store* s) {
+    delete s;
+    return MKV_OK;
+}
+
+// ---- decode ------------------------------------------------------------------------------------------------
+namespace {
+
+struct DecPlan {
+    int32_t G = 0, Hq = 0, spw = 0, max_T = 0;
+    std::vector<int32_t> tab;    // n | segbase | tokbase | T | sblk | kblk | ablk
+    int64_t n_sblk = 0, n_kblk = 0, n_ablk = 0;
+    uint64_t o_tab, o_state, o_hist, o_qp, o_qbar, o_keys, o_bcnt, o_L, o_sel, o_part, bytes;
+};
+
+mkv_status plan_decode(const mkv_store* s, int32_t n_q_heads, const int32_t* T, DecPlan* P) {
+    if (!s) return fail(MKV_E_ARG, "store is NULL");
+    if (!T) return fail(MKV_E_ARG, "T is NULL");
+    const Shape& sh = s->sh;
+    if (n_q_heads < 1 || n_q_heads % sh.Hkv != 0) return fail(MKV_E_ARG, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)", n_q_heads, sh.Hkv);
+    P->G = n_q_heads / sh.Hkv;
+    if (P->G != 1 && P->G != 2 && P->G != 4 && P->G != 8) return fail(MKV_E_UNSUPPORTED, "query heads per KV head must be 1, 2, 4 or 8 (got %d)", P->G);
+    P->Hq = n_q_heads;
+    const int B = sh.B;
+    P->spw = (int32_t)std::max<int64_t>(4, std::min<int64_t>(64, sh.S / 2048));
+    P->tab.assign(7 * B + 3, 0);
+    int32_t* tn = P->tab.data();
+    int32_t* tseg = tn + B;
+    int32_t* ttok = tseg + B;
+    int32_t* tT = ttok + B;
+    int32_t* tsb = tT + B;
+    int32_t* tkb = tsb + B + 1;
+    int32_t* tab_ = tkb + B + 1;
+    int64_t sb = 0, kb = 0, ab = 0;
+    for (int r = 0; r < B; ++r) {
+        if (T[r] < 1) return fail(MKV_E_ARG, "T[%d] = %d must be >= 1", r, T[r]);
+        const int64_t n = sh.cu[r + 1] - sh.cu[r];
+        const int64_t te = std::min<int64_t>(T[r], n);
+        tn[r] = (int32_t)n;
+        tseg[r] = sh.segbase[r];
+        ttok[r] = (int32_t)sh.cu[r];
+        tT[r] = (int32_t)te;
+        tsb[r] = (int32_t)sb;
+        tkb[r] = (int32_t)kb;
+        tab_[r] = (int32_t)ab;
+        sb += (int64_t)sh.Hkv * cdiv(cdiv(n, MKV_SEG_LEN), P->spw);
+        kb += (int64_t)sh.Hkv * cdiv(n, kKeysPerBlock);
+        ab += (int64_t)sh.Hkv * cdiv(te, kAttnChunk);
+        P->max_T = std::max<int32_t>(P->max_T, (int32_t)te);
+    }
+    tsb[B] = (int32_t)sb;
+    tkb[B] = (int32_t)kb;
+    tab_[B] = (int32_t)ab;
+    P->n_sblk = sb;
+    P->n_kblk = kb;
+    P->n_ablk = ab;
+    if (sb > INT32_MAX || kb > INT32_MAX || ab > INT32_MAX) return fail(MKV_E_UNSUPPORTED, "too many workgroups");
+    const uint64_t streams = (uint64_t)B * sh.Hkv;
+    const uint64_t th = (uint64_t)sh.total * sh.Hkv;
+    uint64_t o = 0;
+    P->o_tab = o; o = align_up(o + 4 * P->tab.size());
+    P->o_state = o; o = align_up(o + 4 * streams * kStateWords);
+    P->o_hist = o; o = align_up(o + 4 * streams * kHistBins);
+    P->o_qp = o; o = align_up(o + 4ull * B * n_q_heads * MKV_HEAD_DIM);
+    P->o_qbar = o; o = align_up(o + 4 * streams * MKV_HEAD_DIM);
+    P->o_keys = o; o = align_up(o + 4 * th);
+    P->o_bcnt = o; o = align_up(o + 4 * (uint64_t)std::max<int64_t>(kb, 1));
+    P->o_L = o; o = align_up(o + 8 * th);
+    P->o_sel = o; o = align_up(o + 4 * streams * (uint64_t)std::max<int32_t>(P->max_T, 1));
+    P->o_part = o; o = align_up(o + 4ull * std::max<int64_t>(ab, 1) * P->G * (MKV_HEAD_DIM + 2));
+    P->bytes = o;
+    return MKV_OK;
+}
+
+}  // namespace
+
+mkv_status mkv_decode_workspace_bytes(const mkv_store* s, int32_t n_q_heads, const int32_t* T, size_t* ws_bytes) {
+    DecPlan P;
+    mkv_status st = plan_decode(s, n_q_heads, T, &P);
+    if (st) return st;
+    if (!ws_bytes) return fail(MKV_E_ARG, "ws_bytes is NULL");
+    *ws_bytes = P.bytes;
+    return MKV_OK;
+}
+
+mkv_status mkv_decode_attn(const mkv_store* s, const void* q, int32_t n_q_heads, const int32_t* T, float* out,
+                           int32_t* sel, int32_t sel_stride, void* ws, size_t ws_bytes, mkv_stream_t stream_) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    DecPlan P;
+    mkv_status st = plan_decode(s, n_q_heads, T, &P);
+    if (st) return st;
+    if (!q || !out) return fail(MKV_E_ARG, "q and out must be non-NULL");
+    if (!ws) return fail(MKV_E_ARG, "ws is NULL");
+    if (!aligned(ws)) return fail(MKV_E_ARG, "ws must be 256-byte aligned");
+    if (ws_bytes < P.bytes) return fail(MKV_E_ARG, "ws_bytes %zu < required %llu", ws_bytes, (unsigned long long)P.bytes);
+    if (sel && sel_stride < P.max_T) return fail(MKV_E_ARG, "sel_stride %d < largest selection %d", sel_stride, P.max_T);
+    const Shape& sh = s->sh;
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    DecArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.B = sh.B;
+    a.Hkv = sh.Hkv;
+    a.G = P.G;
+    a.dtype = sh.dtype == MKV_BF16 ? 1 : 0;
+    a.S = sh.S;
+    a.codes = s->base + s->lay.codes;
+    a.seg_off = reinterpret_cast<const uint64_t*>(s->base + s->lay.seg_off);
+    a.payload = s->base + s->lay.payload;
+    a.basis = s->has_basis ? reinterpret_cast<const float*>(s->base + s->lay.basis) : nullptr;
+    for (int k = 0; k < 4; ++k) a.keep[k] = k < s->policy.n_keep ? s->policy.keep[k] : 0;
+    a.q = q;
+    a.out = out;
+    a.sel = sel;
+    a.sel_stride = sel_stride;
+    a.sel_int = reinterpret_cast<int32_t*>(w + P.o_sel);
+    a.sel_int_stride = std::max<int32_t>(P.max_T, 1);
+    const int32_t* tb = reinterpret_cast<const int32_t*>(w + P.o_tab);
+    a.t_n = tb;
+    a.t_segbase = tb + sh.B;
+    a.t_tokbase = tb + 2 * sh.B;
+    a.t_T = tb + 3 * sh.B;
+    a.t_sblk = tb + 4 * sh.B;
+    a.t_kblk = tb + 5 * sh.B + 1;
+    a.t_ablk = tb + 6 * sh.B + 2;
+    a.spw = P.spw;
+    a.qp = reinterpret_cast<float*>(w + P.o_qp);
+    a.qbar = reinterpret_cast<float*>(w + P.o_qbar);
+    a.keys = reinterpret_cast<uint32_t*>(w + P.o_keys);
+    a.hist = reinterpret_cast<uint32_t*>(w + P.o_hist);
+    a.state = reinterpret_cast<uint32_t*>(w + P.o_state);
+    a.bcnt = reinterpret_cast<uint32_t*>(w + P.o_bcnt);
+    a.L = reinterpret_cast<uint2*>(w + P.o_L);
+    a.part = reinterpret_cast<float*>(w + P.o_part);
+
+    // per-request tables: the first kUploadWords words ride on the prep kernel, the rest on upload launches
+    int32_t* tdst = reinterpret_cast<int32_t*>(w + P.o_tab);
+    if ((st = upload_words(tdst, P.tab, kUploadWords, stream))) return st;
+    Upload first;
+    first.dst = tdst;
+    first.n = (int32_t)std::min<size_t>(kUploadWords, P.tab.size());
+    std::memcpy(first.w, P.tab.data(), sizeof(int32_t) * first.n);
+    if ((st = run(K_DEC_PREP, stream, [&] { return launch_dec_prep(a, first, stream); }))) return st;
+    if ((st = run(K_SCORE, stream, [&] { return launch_score(a, (int)P.n_sblk, stream); }))) return st;
+    if ((st = run(K_SEL_COUNT, stream, [&] { return launch_sel_count(a, (int)P.n_kblk, stream); }))) return st;
+    if ((st = run(K_SEL_WRITE, stream, [&] { return launch_sel_write(a, (int)P.n_kblk, stream); }))) return st;
+    if ((st = run(K_SEL_FINAL, stream, [&] { return launch_sel_final(a, stream); }))) return st;
+    if ((st = run(K_ATTEND, stream, [&] { return launch_attend(a, (int)P.n_ablk, stream); }))) return st;
+    if ((st = run(K_COMBINE, stream, [&] { return launch_combine(a, stream); }))) return st;
+    return MKV_OK;
+}
+
+// ---- profiling --------------------------------------------------------------------------------------------
+mkv_status mkv_profile_start(int32_t max_launches) {
+    if (max_launches < 0) return fail(MKV_E_ARG, "max_launches must be >= 0");
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    g_prof.recs.clear();
+    g_prof.used = 0;
+    g_prof.max_launches = max_launches;
+    g_prof.on = true;
+    return MKV_OK;
+}
+
+mkv_status mkv_profile_stop(double* total_ms, int32_t* launches) {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    g_prof.on = false;
+    if (total_ms) for (int i = 0; i < MKV_PROFILE_KERNELS; ++i) total_ms[i] = 0.0;
+    if (launches) for (int i = 0; i < MKV_PROFILE_KERNELS; ++i) launches[i] = 0;
+    mkv_status st = MKV_OK;
+    for (const auto& r : g_prof.recs) {
+        float ms = 0.f;
+        hipError_t e = hipEventSynchronize(r.b);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+        if (e != hipSuccess) { st = fail(MKV_E_DEVICE, "event timing failed: %s", hipGetErrorString(e)); continue; }
+        if (total_ms) total_ms[r.kid] += ms;
+        if (launches) launches[r.kid] += 1;
+    }
+    g_prof.recs.clear();
+    g_prof.used = 0;
+    return st;
+}
+
+const char* mkv_kernel_name(int32_t id) {
+    if (id < 0 || id >= K_COUNT) return nullptr;
+    return kKernelNames[id];
+}
+
+}  // extern "C"

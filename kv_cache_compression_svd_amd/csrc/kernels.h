@@ -1,0 +1,88 @@
+// Internal interface between the host entry points (api.cpp) and the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mkv {
+
+constexpr int kUploadWords = 448;       // int32 words a table upload carries in its kernel arguments
+constexpr int kHistBins = 4096;         // first radix level of the top-T select: key bits [31:20]
+constexpr int kStateWords = 16;         // per (request, KV head) selection state
+constexpr int kKeysPerBlock = 4096;     // keys per workgroup in the selection passes
+constexpr int kAttnChunk = 256;         // selected tokens per attention workgroup
+
+// selection state words
+enum { ST_DONE = 0, ST_P1 = 1, ST_NGT = 2, ST_NCAND = 3, ST_NEED = 4 };
+
+struct Upload {
+    int32_t* dst;
+    int32_t n;
+    int32_t w[kUploadWords];
+};
+
+// ---- compression --------------------------------------------------------------------------------------
+struct CmpArgs {
+    const void* K;
+    const void* V;
+    const float* basis;         // [B][Hkv][2][128][128] or null (inputs already rotated)
+    const int32_t* tab;         // tok_base[B] | n[B] | seg_base[B] | cblk_base[B+1]
+    int32_t B, Hkv, spw, nblk;  // spw: segments per workgroup; nblk: workgroups per tensor
+    int64_t S;                  // segments per tensor
+    int64_t total_tokens;
+    uint8_t* codes;             // [2][S]
+    uint64_t* seg_off;          // [2][S]: segment sizes after the decide pass, byte offsets after the scan
+    uint8_t* payload;
+    uint16_t* thr;              // [2][total_tokens][Hkv][4] per-vector magnitude thresholds (scratch)
+    int32_t keep[4];
+    int32_t n_keep;
+    double frac;
+};
+
+hipError_t launch_upload(const Upload& u, hipStream_t s);
+hipError_t launch_cmp_decide(const CmpArgs& a, int dtype, hipStream_t s);
+hipError_t launch_cmp_scan(uint64_t* seg_off, int64_t count, uint64_t* total, hipStream_t s);
+hipError_t launch_cmp_pack(const CmpArgs& a, int dtype, hipStream_t s);
+
+// ---- decode -------------------------------------------------------------------------------------------
+struct DecArgs {
+    int32_t B, Hkv, G, dtype;
+    int64_t S;
+    const uint8_t* codes;
+    const uint64_t* seg_off;
+    const uint8_t* payload;
+    const float* basis;         // store's copy or null
+    int32_t keep[4];
+    const void* q;
+    float* out;
+    int32_t* sel;               // user buffer or null
+    int32_t sel_stride;
+    int32_t* sel_int;           // internal selection lists [B*Hkv][sel_int_stride]
+    int32_t sel_int_stride;
+    // per-request tables (device): n | seg_base | tok_base | T_eff | sblk_base | kblk_base | ablk_base
+    const int32_t* t_n;
+    const int32_t* t_segbase;
+    const int32_t* t_tokbase;
+    const int32_t* t_T;
+    const int32_t* t_sblk;
+    const int32_t* t_kblk;
+    const int32_t* t_ablk;
+    int32_t spw;                // segments per score workgroup
+    float* qp;                  // [B][Hq][128]
+    float* qbar;                // [B][Hkv][128]
+    uint32_t* keys;             // [total_tokens*Hkv]
+    uint32_t* hist;             // [B*Hkv][4096]
+    uint32_t* state;            // [B*Hkv][16]
+    uint32_t* bcnt;             // [n_kblk]
+    uint2* L;                   // [total_tokens*Hkv] (token index, key)
+    float* part;                // [n_ablk][G][130]
+};
+
+hipError_t launch_dec_prep(const DecArgs& a, const Upload& tab, hipStream_t s);
+hipError_t launch_score(const DecArgs& a, int n_blocks, hipStream_t s);
+hipError_t launch_sel_count(const DecArgs& a, int n_blocks, hipStream_t s);
+hipError_t launch_sel_write(const DecArgs& a, int n_blocks, hipStream_t s);
+hipError_t launch_sel_final(const DecArgs& a, hipStream_t s);
+hipError_t launch_attend(const DecArgs& a, int n_blocks, hipStream_t s);
+hipError_t launch_combine(const DecArgs& a, hipStream_t s);
+
+}  // namespace mkv

@@ -1,0 +1,156 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol include/mkv.h declares, and rejects
+bad arguments on the host before enqueueing anything."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import kv_cache_compression_svd_amd as mkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mkv.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mkv_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = mkv.lib()
+    names = _declared()
+    assert "mkv_compress" in names and "mkv_decode_attn" in names
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(mkv.SIGNATURES), "binding and header disagree"
+
+
+def test_default_policy():
+    p = mkv.mkv_default_policy()
+    assert (p.seg_len, p.keeps(), p.energy_frac) == (64, (128, 64, 32), 0.9)
+
+
+def _desc(batch=1, heads=8, dim=128, dtype=mkv.MKV_BF16, cu=(0, 100)):
+    cu = np.asarray(cu, dtype=np.int64)
+    d = mkv.KVDesc()
+    d.batch, d.n_kv_heads, d.head_dim, d.dtype = batch, heads, dim, dtype
+    d.cu_seqlens = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    return d, cu
+
+
+def _bytes(d, p):
+    sb, tb = ctypes.c_size_t(), ctypes.c_size_t()
+    return mkv.lib().mkv_compress_bytes(ctypes.byref(d), ctypes.byref(p), ctypes.byref(sb), ctypes.byref(tb)), sb, tb
+
+
+def test_sizes_match_layout():
+    d, cu = _desc(batch=2, cu=(0, 100, 300))
+    st, sb, tb = _bytes(d, mkv.mkv_default_policy())
+    assert st == mkv.MKV_OK
+    S = 8 * (2 + 4)                     # segments per tensor: ceil(100/64) + ceil(200/64) per head
+    payload = 2 * 8 * 300 * 128 * 2     # worst case: every segment keeps 128 channels
+    basis = 2 * 8 * 2 * 128 * 128 * 4
+    align = lambda x: (x + 255) // 256 * 256   # noqa: E731
+    codes = 256
+    seg_off = align(codes + 2 * S)
+    b = align(seg_off + 16 * S)
+    p = align(b + basis)
+    assert sb.value == p + payload
+    assert tb.value == align(4 * (4 * 2 + 1)) + 2 * 300 * 8 * 4 * 2
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 64, mkv.MKV_E_UNSUPPORTED), ("batch", 0, mkv.MKV_E_ARG), ("n_kv_heads", 0, mkv.MKV_E_ARG),
+    ("dtype", 7, mkv.MKV_E_ARG)])
+def test_bad_shapes_rejected(field, value, code):
+    d, cu = _desc()
+    setattr(d, field, value)
+    st, _, _ = _bytes(d, mkv.mkv_default_policy())
+    assert st == code
+    assert mkv.mkv_last_error()
+
+
+def test_bad_cu_seqlens_rejected():
+    d, cu = _desc(batch=2, cu=(0, 100, 50))
+    st, _, _ = _bytes(d, mkv.mkv_default_policy())
+    assert st == mkv.MKV_E_ARG and "non-decreasing" in mkv.mkv_last_error()
+    d, cu = _desc(batch=1, cu=(5, 100))
+    assert _bytes(d, mkv.mkv_default_policy())[0] == mkv.MKV_E_ARG
+
+
+@pytest.mark.parametrize("keep,frac,seg,code", [
+    ((64, 32), 0.9, 64, mkv.MKV_E_ARG), ((128, 64, 64), 0.9, 64, mkv.MKV_E_ARG),
+    ((128, 48), 0.9, 64, mkv.MKV_E_UNSUPPORTED), ((128, 64), 0.0, 64, mkv.MKV_E_ARG),
+    ((128, 64), 1.5, 64, mkv.MKV_E_ARG), ((128, 64), 0.9, 32, mkv.MKV_E_UNSUPPORTED)])
+def test_bad_policies_rejected(keep, frac, seg, code):
+    d, cu = _desc()
+    p = mkv.SegPolicy.make(keep, frac, seg)
+    assert _bytes(d, p)[0] == code
+
+
+def test_compress_rejects_missing_buffers_before_any_launch():
+    d, cu = _desc()
+    d.K = ctypes.c_void_p(256)     # never dereferenced: the call must fail on its host checks first
+    d.V = ctypes.c_void_p(512)
+    p = mkv.mkv_default_policy()
+    h = ctypes.c_void_p()
+    st = mkv.lib().mkv_compress(ctypes.byref(d), None, ctypes.byref(p), None, 0, None, 0, None, ctypes.byref(h))
+    assert st == mkv.MKV_E_ARG and not h.value
+    # undersized store buffer
+    st = mkv.lib().mkv_compress(ctypes.byref(d), None, ctypes.byref(p), ctypes.c_void_p(4096), 10,
+                                ctypes.c_void_p(8192), 1 << 30, None, ctypes.byref(h))
+    assert st == mkv.MKV_E_ARG and "store_bytes" in mkv.mkv_last_error()
+    # misaligned
+    st = mkv.lib().mkv_compress(ctypes.byref(d), None, ctypes.byref(p), ctypes.c_void_p(4100), 1 << 40,
+                                ctypes.c_void_p(8192), 1 << 30, None, ctypes.byref(h))
+    assert st == mkv.MKV_E_ARG and "aligned" in mkv.mkv_last_error()
+
+
+def _attached(cu=(0, 100, 0 + 100), heads=2):
+    d, cu = _desc(batch=len(cu) - 1, heads=heads, cu=cu)
+    p = mkv.mkv_default_policy()
+    st, sb, _ = _bytes(d, p)
+    h = ctypes.c_void_p()
+    # attach only records pointers: a fake aligned address is never touched by the host checks below
+    st = mkv.lib().mkv_store_attach(ctypes.byref(d), ctypes.byref(p), 0, ctypes.c_void_p(1 << 20), sb, ctypes.byref(h))
+    assert st == mkv.MKV_OK
+    return h, cu
+
+
+def test_decode_argument_checks():
+    h, cu = _attached(cu=(0, 100, 200), heads=2)
+    L = mkv.lib()
+    T = (ctypes.c_int32 * 2)(10, 0)
+    ws = ctypes.c_size_t()
+    assert L.mkv_decode_workspace_bytes(h, 8, T, ctypes.byref(ws)) == mkv.MKV_E_ARG      # T[1] = 0
+    T[1] = 5
+    assert L.mkv_decode_workspace_bytes(h, 8, T, ctypes.byref(ws)) == mkv.MKV_OK
+    assert L.mkv_decode_workspace_bytes(h, 7, T, ctypes.byref(ws)) == mkv.MKV_E_ARG      # not a multiple
+    assert L.mkv_decode_workspace_bytes(h, 6, T, ctypes.byref(ws)) == mkv.MKV_E_UNSUPPORTED  # group 3
+    assert L.mkv_decode_workspace_bytes(None, 8, T, ctypes.byref(ws)) == mkv.MKV_E_ARG
+    need = ws.value
+    fake = ctypes.c_void_p(1 << 24)
+    assert L.mkv_decode_attn(h, fake, 8, T, fake, None, 0, fake, need - 1, None) == mkv.MKV_E_ARG
+    assert "ws_bytes" in mkv.mkv_last_error()
+    assert L.mkv_decode_attn(h, fake, 8, T, fake, fake, 4, fake, need, None) == mkv.MKV_E_ARG   # stride < 10
+    assert "sel_stride" in mkv.mkv_last_error()
+    assert L.mkv_decode_attn(h, None, 8, T, fake, None, 0, fake, need, None) == mkv.MKV_E_ARG
+    assert L.mkv_store_destroy(h) == mkv.MKV_OK
+
+
+def test_view_reports_layout():
+    h, cu = _attached(cu=(0, 100, 300), heads=2)
+    info = mkv.StoreInfo()
+    assert mkv.lib().mkv_store_view(h, ctypes.byref(info)) == mkv.MKV_OK
+    assert info.segments_per_tensor == 2 * (2 + 4) and info.total_tokens == 300
+    assert info.codes == (1 << 20) + 256 and info.basis is None
+    assert [info.cu_seqlens[i] for i in range(3)] == [0, 100, 300]
+    mkv.lib().mkv_store_destroy(h)
+
+
+def test_kernel_names():
+    names = [mkv.mkv_kernel_name(i) for i in range(mkv.PROFILE_KERNELS)]
+    assert "score" in names and "attend" in names and names[-1] is None
