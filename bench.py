@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of compressed decode attention on one MI355X.
+
+A step is one decode-attention call over a compressed store (query rotation, score estimate over every stored
+key, top-T selection, exact sparse attention, output rotation) for one layer of the workload.  The store is
+built once per run by the library's compression call, which is timed as its own leg and reported under
+"compress".  The printed JSON line reports context tokens per second (sum of the requests' contexts divided by
+the step time), the roofline of the dominant kernel (the score gather-dot, HBM-bound) from HIP events recorded
+around its launches inside the timed region, and the CPU oracle timed on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload batch8_128k] [--cpu-seconds 12]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+METRIC = "compressed decode-attn context tokens/s per layer; achieved HBM GB/s vs peak"
+KERNEL_SOURCES = ["kv_cache_compression_svd_amd/csrc/decode.hip", "kv_cache_compression_svd_amd/csrc/common.cuh"]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="batch8_128k", choices=W.ORDER)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workers", type=int, default=min(16, os.cpu_count() or 1))
+    return ap.parse_args()
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per score launch from the committed rocprofv3 counter summary, when it was taken on the
+    current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"score_{workload}_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256_16") != source_hash():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_dispatch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def store_bytes(codes: np.ndarray, cu, Hkv: int, keep, bv: int):
+    """Per-segment payload sizes of both tensors from the strategy codes: (K sizes, V sizes, n_s per segment)."""
+    n = np.diff(np.asarray(cu, dtype=np.int64))
+    S_r = (n + 63) // 64
+    S = int(S_r.sum()) * Hkv
+    ns = np.zeros(S, dtype=np.int64)
+    pos = 0
+    for r in range(len(n)):
+        seg = np.minimum(64, n[r] - 64 * np.arange(S_r[r]))
+        for _ in range(Hkv):
+            ns[pos:pos + S_r[r]] = seg
+            pos += S_r[r]
+    keep = np.asarray(keep)
+    c = keep[codes.astype(np.int64)]
+    row = c * (bv + (c < 128))
+    return row[:S], row[S:], ns, S
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+              f"run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    w = W.get(args.workload)
+    t_gen = time.time()
+    inp = W.generate(w, basis="svd", workers=args.workers)
+    t_gen = time.time() - t_gen
+
+    import torch
+    import kv_cache_compression_svd_amd as mkv
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from _helpers import inputs_to_torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    K, V, q, basis = inputs_to_torch(inp, dev)
+    bv = 2 if w.dtype == "bf16" else 4
+    policy = mkv.mkv_default_policy()
+    keep = policy.keeps()
+
+    # ---- compress leg (timed on its own) ----
+    sb, tb = mkv.mkv_compress_bytes(K, V, inp.cu_seqlens, policy)
+    store_buf = torch.empty(sb, dtype=torch.uint8, device=dev)
+    scratch = torch.empty(tb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    store = mkv.mkv_compress(K, V, inp.cu_seqlens, basis, policy, store_buf=store_buf, scratch=scratch)
+    torch.cuda.synchronize()
+    c_reps = 3
+    mkv.mkv_profile_start()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(c_reps):
+        store.close()
+        store = mkv.mkv_compress(K, V, inp.cu_seqlens, basis, policy, store_buf=store_buf, scratch=scratch)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    c_kern = mkv.mkv_profile_stop()
+    compress_ms = e0.elapsed_time(e1) / c_reps
+    payload = store.payload_bytes()
+    info = store.view()
+    S = int(info.segments_per_tensor)
+    base = store_buf.data_ptr()
+    codes = store_buf[info.codes - base: info.codes - base + 2 * S].cpu().numpy()
+    k_rows, v_rows, ns, S = store_bytes(codes, inp.cu_seqlens, w.n_kv_heads, keep, bv)
+    k_payload = int((k_rows * ns).sum())
+    total_tokens = int(inp.cu_seqlens[-1])
+    dense = 2 * total_tokens * w.n_kv_heads * 128 * bv
+    n_basis_bytes = w.batch * w.n_kv_heads * 2 * 128 * 128 * 4
+    compress_alg_bytes = dense + payload + 9 * 2 * S + n_basis_bytes
+    rot_flops = 2.0 * 2 * total_tokens * w.n_kv_heads * 128 * 128
+
+    # ---- decode: warmup, then exactly K timed steps ----
+    T = inp.T
+    out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+    te = np.minimum(T, np.diff(inp.cu_seqlens))
+    sel = torch.empty((w.batch, w.n_kv_heads, int(te.max())), dtype=torch.int32, device=dev)
+    ws = torch.empty(mkv.mkv_decode_workspace_bytes(store, w.n_q_heads, T), dtype=torch.uint8, device=dev)
+
+    def step():
+        mkv.mkv_decode_attn(store, q, T, out=out, sel=sel, ws=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # unprofiled region (reported as an extra)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    clean_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    # timed region with kernel events
+    torch.cuda.synchronize()
+    mkv.mkv_profile_start()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    kern = mkv.mkv_profile_stop()
+
+    sel_np = sel.cpu().numpy()
+    # V payload actually gathered: rows of the selected tokens
+    n = np.diff(inp.cu_seqlens)
+    S_r = (n + 63) // 64
+    seg_base = np.concatenate([[0], np.cumsum(S_r)[:-1]])
+    v_sel_bytes = 0
+    v_segs = 0
+    for r in range(w.batch):
+        for h in range(w.n_kv_heads):
+            j = sel_np[r, h, :te[r]]
+            gs = w.n_kv_heads * seg_base[r] + h * S_r[r] + (j >> 6)
+            v_sel_bytes += int(v_rows[gs].sum())
+            v_segs += int(np.unique(gs).size)
+    q_bytes = w.batch * w.n_q_heads * 128 * bv
+    out_bytes = w.batch * w.n_q_heads * 128 * 4
+    step_alg = k_payload + v_sel_bytes + 9 * (S + v_segs) + q_bytes + out_bytes + n_basis_bytes
+    score_ms, score_n = kern.get("score", (float("nan"), 0))
+    score_avg = score_ms / max(score_n, 1)
+    score_alg = k_payload + 9 * S + w.batch * w.n_kv_heads * 128 * 4
+    achieved = score_alg / (score_avg * 1e-3) / 1e9
+    traffic = read_traffic(args.workload)
+
+    result = {
+        "metric": METRIC,
+        "value": total_tokens / (ms * 1e-3),
+        "unit": "context tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "fp32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "context": list(w.ctx) if w.batch <= 4 else
+                   f"{w.batch} x {w.ctx[0]}" if len(set(w.ctx)) == 1 else list(w.ctx),
+                   "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": 128,
+                   "T": int(w.T[0]) if len(set(w.T)) == 1 else list(w.T), "seg_len": 64, "keep": list(keep),
+                   "energy_frac": 0.9, "accumulate": "fp32", "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "score", "achieved": achieved, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic, "alg_bytes_per_launch": score_alg,
+                     "avg_launch_ms": score_avg},
+        "step_alg_bytes": step_alg,
+        "step_alg_GBps": step_alg / (ms * 1e-3) / 1e9,
+        "step_frac_of_hbm_peak": step_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "ms_per_step_unprofiled": clean_ms,
+        "kernels_avg_ms": {k: v[0] / max(v[1], 1) for k, v in kern.items()},
+        "store": {"payload_bytes": payload, "dense_kv_bytes": dense, "compression_ratio": dense / payload,
+                  "k_payload_bytes": k_payload, "v_selected_bytes": v_sel_bytes},
+        "compress": {"ms": compress_ms, "context_tokens_per_s": total_tokens / (compress_ms * 1e-3),
+                     "alg_bytes": compress_alg_bytes, "alg_GBps": compress_alg_bytes / (compress_ms * 1e-3) / 1e9,
+                     "rotation_TFLOPs": rot_flops / (compress_ms * 1e-3) / 1e12,
+                     "rotation_frac_of_bf16_mfma_peak": rot_flops / (compress_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                     "kernels_avg_ms": {k: v[0] / max(v[1], 1) for k, v in c_kern.items()}},
+        "input_generation_s": t_gen,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(inp, seconds: float):
+    """The oracle's decode step on one (request 0, KV head 0) unit, repeated for about ``seconds``; its store is
+    built by the oracle first (untimed).  Context tokens/s of a full layer = n_0 / (n_kv_heads * t_unit)."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    w = inp.workload
+    units = [(0, 0)]
+    streams = oracle.compress_all(inp, units=units)
+    reps, t = 0, 0.0
+    while t < seconds or reps < 1:
+        t0 = time.perf_counter()
+        oracle.decode_all(inp, streams, units=units)
+        t += time.perf_counter() - t0
+        reps += 1
+    n0 = int(inp.cu_seqlens[1] - inp.cu_seqlens[0])
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": n0 * reps / (w.n_kv_heads * t), "unit": "context tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle decode of request 0 / KV head 0 ({n0} tokens, T={int(inp.T[0])}) "
+                      f"repeated {reps}x in {t:.1f}s; its store compressed by the oracle beforehand, untimed; "
+                      f"a layer has {w.n_kv_heads} KV heads, so tokens/s = n0*reps/({w.n_kv_heads}*t); "
+                      f"BLAS threads {threads}, host cpu_count {os.cpu_count()}"}
+
+
+if __name__ == "__main__":
+    main()

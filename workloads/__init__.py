@@ -107,9 +107,9 @@ def scaled(w: Workload, ctx_div: int = 1, ctx=None, T=None, name=None) -> Worklo
 
 def f32_to_bf16_bits(x32: np.ndarray) -> np.ndarray:
     """Round float32 values to bf16 (nearest, ties to even); returns the 16-bit patterns."""
-    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return r.astype(np.uint16)
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32)
+    r = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))   # no overflow for finite values
+    return (r >> np.uint32(16)).astype(np.uint16)
 
 
 def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
@@ -167,51 +167,90 @@ def _sperm_basis(rng: np.random.Generator) -> np.ndarray:
     return b
 
 
-def generate(w: Workload, basis: str = "svd", heads=None) -> Inputs:
+def _draw_request(w: Workload, rng, r: int, t0: int, n: int, K, V, q, sig, bas, basis: str, brng, heads):
+    """Draws request r's K, V, q (and bases) from ``rng`` in the recipe's order, writing into the arrays."""
+    G = w.group
+    for h in range(w.n_kv_heads):
+        perm = rng.permutation(HEAD_DIM)
+        sigma = (perm + 1.0) ** -0.5
+        out = rng.choice(HEAD_DIM, _N_OUTLIERS, replace=False)
+        sigma[out] *= _OUTLIER_GAIN
+        sig[r, h] = sigma
+        for slot, dst in ((0, K), (1, V)):
+            x = rng.standard_normal((n, HEAD_DIM)) * sigma
+            xs = _store(x, w.dtype)
+            if heads is None or h in heads:
+                dst[t0:t0 + n, h, :] = xs
+            if bas is not None:
+                if basis == "svd":
+                    bas[r, h, slot] = _svd_basis(to_f64(xs, w.dtype)) if (heads is None or h in heads) \
+                        else np.eye(HEAD_DIM, dtype=np.float32)
+                elif basis == "sperm":
+                    bas[r, h, slot] = _sperm_basis(brng)
+                else:
+                    raise ValueError(basis)
+        qq = rng.standard_normal((G, HEAD_DIM)) * sigma
+        q[r, h * G:(h + 1) * G, :] = _store(qq, w.dtype)
+
+
+def _shared_array(shape, dtype):
+    import mmap
+    nbytes = int(np.prod(shape)) * np.dtype(dtype).itemsize
+    buf = mmap.mmap(-1, max(nbytes, 1))   # anonymous shared mapping: forked workers write into it
+    return np.frombuffer(buf, dtype=dtype, count=int(np.prod(shape))).reshape(shape)
+
+
+_FORK_STATE = None
+
+
+def _fork_worker(r):
+    from threadpoolctl import threadpool_limits
+    w, cu, K, V, q, sig, bas, basis, heads = _FORK_STATE
+    rng = np.random.default_rng(w.seed + r)
+    brng = np.random.default_rng([w.seed, 7, r])
+    with threadpool_limits(1):
+        _draw_request(w, rng, r, int(cu[r]), int(cu[r + 1] - cu[r]), K, V, q, sig, bas, basis, brng, heads)
+    return r
+
+
+def generate(w: Workload, basis: str = "svd", heads=None, workers: int = 1) -> Inputs:
     """Draw the inputs of workload ``w``.  ``basis`` is "svd", "sperm" or "none".  ``heads`` restricts the
-    draw of K/V to a subset of KV heads (other heads are left zero; the rng stream is unchanged)."""
-    B, Hkv, G = w.batch, w.n_kv_heads, w.group
+    draw of K/V to a subset of KV heads (other heads are left zero; the rng stream is unchanged).
+    ``workers`` > 1 draws the requests of a per-request-seeded workload in forked processes (same values);
+    call it before the process touches a GPU."""
+    global _FORK_STATE
+    B = w.batch
     ctx = np.asarray(w.ctx, dtype=np.int64)
     cu = np.zeros(B + 1, dtype=np.int64)
     cu[1:] = np.cumsum(ctx)
     total = int(cu[-1])
     sdt = np.uint16 if w.dtype == "bf16" else np.float32
-    K = np.zeros((total, Hkv, HEAD_DIM), dtype=sdt)
-    V = np.zeros((total, Hkv, HEAD_DIM), dtype=sdt)
-    q = np.zeros((B, w.n_q_heads, HEAD_DIM), dtype=sdt)
-    sig = np.zeros((B, Hkv, HEAD_DIM), dtype=np.float64)
-    bas = None if basis == "none" else np.zeros((B, Hkv, 2, HEAD_DIM, HEAD_DIM), dtype=np.float32)
-    brng = np.random.default_rng([w.seed, 7])
-
-    rng = np.random.default_rng(w.seed)
-    if w.seeding == "ragged":
-        rng.uniform(0.0, 1.0, B)   # the context draw comes first on this stream (see _ragged_contexts)
-    for r in range(B):
-        if w.seeding == "per_request":
-            rng = np.random.default_rng(w.seed + r)
-        n = int(ctx[r])
-        t0 = int(cu[r])
-        for h in range(Hkv):
-            perm = rng.permutation(HEAD_DIM)
-            sigma = (perm + 1.0) ** -0.5
-            out = rng.choice(HEAD_DIM, _N_OUTLIERS, replace=False)
-            sigma[out] *= _OUTLIER_GAIN
-            sig[r, h] = sigma
-            for slot, dst in ((0, K), (1, V)):
-                x = rng.standard_normal((n, HEAD_DIM)) * sigma
-                xs = _store(x, w.dtype)
-                if heads is None or h in heads:
-                    dst[t0:t0 + n, h, :] = xs
-                if bas is not None:
-                    if basis == "svd":
-                        bas[r, h, slot] = _svd_basis(to_f64(xs, w.dtype)) if (heads is None or h in heads) \
-                            else np.eye(HEAD_DIM, dtype=np.float32)
-                    elif basis == "sperm":
-                        bas[r, h, slot] = _sperm_basis(brng)
-                    else:
-                        raise ValueError(basis)
-            qq = rng.standard_normal((G, HEAD_DIM)) * sigma
-            q[r, h * G:(h + 1) * G, :] = _store(qq, w.dtype)
+    par = workers > 1 and w.seeding == "per_request" and B > 1
+    alloc = _shared_array if par else (lambda shape, dt: np.zeros(shape, dtype=dt))
+    K = alloc((total, w.n_kv_heads, HEAD_DIM), sdt)
+    V = alloc((total, w.n_kv_heads, HEAD_DIM), sdt)
+    q = alloc((B, w.n_q_heads, HEAD_DIM), sdt)
+    sig = alloc((B, w.n_kv_heads, HEAD_DIM), np.float64)
+    bas = None if basis == "none" else alloc((B, w.n_kv_heads, 2, HEAD_DIM, HEAD_DIM), np.float32)
+    if par:
+        import multiprocessing as mp
+        _FORK_STATE = (w, cu, K, V, q, sig, bas, basis, heads)
+        try:
+            with mp.get_context("fork").Pool(min(workers, B)) as pool:
+                list(pool.imap_unordered(_fork_worker, range(B)))
+        finally:
+            _FORK_STATE = None
+    else:
+        rng = np.random.default_rng(w.seed)
+        if w.seeding == "ragged":
+            rng.uniform(0.0, 1.0, B)   # the context draw comes first on this stream (see _ragged_contexts)
+        for r in range(B):
+            if w.seeding == "per_request":
+                rng = np.random.default_rng(w.seed + r)
+                brng = np.random.default_rng([w.seed, 7, r])
+            else:
+                brng = np.random.default_rng([w.seed, 7, r])
+            _draw_request(w, rng, r, int(cu[r]), int(ctx[r]), K, V, q, sig, bas, basis, brng, heads)
     T = np.asarray(w.T, dtype=np.int32)
     return Inputs(w, K, V, q, bas, cu, T, sig)
 
