@@ -67,12 +67,6 @@ __device__ __forceinline__ void wave_lds_sync() {
 __device__ __forceinline__ uint32_t atomic_add_dev(uint32_t* p, uint32_t v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ uint32_t atomic_add_acqrel_dev(uint32_t* p, uint32_t v) {
-    return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t load_dev(const uint32_t* p) {
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 // Index r with base[r] <= b < base[r+1] for a non-decreasing base[0..n] with base[0] == 0 <= b < base[n].
 __device__ __forceinline__ int find_slot(const int32_t* base, int n, int b) {

@@ -5,11 +5,12 @@
 //
 // Kernels, in stream order, for every (request r, KV head g):
 //   prep     q'_h = q_h @ B_K (fp32), Qbar = sum of the group's q'_h; clears the selection state.
-//   score    s_j = sum over token j's stored channels of Qbar_i * k_j,i for every stored key (8 lanes per token,
-//            coalesced 16-byte loads, Qbar gathered from LDS); writes an order-preserving 32-bit key per token and
-//            a 4096-bin histogram of the key's top 12 bits.  The last workgroup of a stream finds the bin that
-//            holds the T-th largest key.
-//   count    per 4096-key block: keys in that bin or above.
+//   score    s_j = sum over token j's stored channels of Qbar_i * k_j,i for every stored key (c/8 lanes per
+//            token, one coalesced 16-byte value load per lane and pass, eight passes in flight per wave, Qbar
+//            gathered from LDS); writes an order-preserving 32-bit key per token and a 4096-bin histogram of the
+//            key's top 12 bits.
+//   count    finds the histogram bin that holds the T-th largest key, then counts per 4096-key block the keys in
+//            that bin or above.
 //   write    the same keys, compacted in ascending token order (block offsets from the counts).
 //   final    one workgroup per stream resolves the exact T-th key inside the boundary bin (two more 10-bit radix
 //            levels) and emits the selected tokens in ascending order; ties go to the lower token index.
@@ -50,99 +51,181 @@ __device__ __forceinline__ int idx_at(const uint32_t* iw, int k) { return (iw[k 
 // =====================================================================================================
 // prep
 // =====================================================================================================
-__global__ __launch_bounds__(128) void k_dec_prep(DecArgs a, Upload tab) {
-    if (blockIdx.x == 0)
-        for (int i = threadIdx.x; i < tab.n; i += 128) tab.dst[i] = tab.w[i];
+__global__ __launch_bounds__(256) void k_dec_prep(DecArgs a, Upload tab) {
+    __shared__ __attribute__((aligned(16))) float bs[MKV_D * MKV_D];
     __shared__ float qs[MKV_MAX_GROUP_DEV][MKV_D];
+    __shared__ float qo[MKV_MAX_GROUP_DEV][MKV_D];
+    const int tid = threadIdx.x;
+    if (blockIdx.x == 0)
+        for (int i = tid; i < tab.n; i += 256) tab.dst[i] = tab.w[i];
     const int stream = blockIdx.x, r = stream / a.Hkv, g = stream - r * a.Hkv;
-    const int i = threadIdx.x, G = a.G, Hq = a.G * a.Hkv;
-    for (int h = 0; h < G; ++h) {
-        const size_t qi = ((size_t)r * Hq + g * G + h) * MKV_D + i;
-        qs[h][i] = a.dtype == 1 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qi])
+    const int G = a.G, Hq = a.G * a.Hkv;
+    u32x4* hz = reinterpret_cast<u32x4*>(a.hist + (size_t)stream * kHistBins);
+    for (int i = tid; i < kHistBins / 4; i += 256) hz[i] = u32x4{0u, 0u, 0u, 0u};
+    if (tid < kStateWords) a.state[stream * kStateWords + tid] = 0u;
+    const float* Bk = a.basis ? a.basis + ((((size_t)r * a.Hkv + g) * 2) << 14) : nullptr;
+    if (Bk) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(Bk);
+        f32x4* dst = reinterpret_cast<f32x4*>(bs);
+        f32x4 v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = src[tid + 256 * j];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dst[tid + 256 * j] = v[j];
+    }
+    for (int i = tid; i < G * MKV_D; i += 256) {
+        const int h = i >> 7, c = i & 127;
+        const size_t qi = ((size_t)r * Hq + g * G + h) * MKV_D + c;
+        qs[h][c] = a.dtype == 1 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qi])
                                 : reinterpret_cast<const float*>(a.q)[qi];
     }
     __syncthreads();
-    float acc[MKV_MAX_GROUP_DEV];
-    const float* Bk = a.basis ? a.basis + ((((size_t)r * a.Hkv + g) * 2) << 14) : nullptr;
-    for (int h = 0; h < MKV_MAX_GROUP_DEV; ++h) acc[h] = 0.f;
-    if (Bk) {
-        for (int k = 0; k < MKV_D; ++k) {
-            const float b = Bk[k * MKV_D + i];
-#pragma unroll
-            for (int h = 0; h < MKV_MAX_GROUP_DEV; ++h)
-                if (h < G) acc[h] = fmaf(qs[h][k], b, acc[h]);
+    const int i = tid & 127;
+    for (int h = tid >> 7; h < G; h += 2) {
+        float acc;
+        if (Bk) {
+            acc = 0.f;
+#pragma unroll 8
+            for (int k = 0; k < MKV_D; ++k) acc = fmaf(qs[h][k], bs[k * MKV_D + i], acc);
+        } else {
+            acc = qs[h][i];
         }
-    } else {
-        for (int h = 0; h < G; ++h) acc[h] = qs[h][i];
+        qo[h][i] = acc;
+        a.qp[((size_t)r * Hq + g * G + h) * MKV_D + i] = acc;
     }
-    float qb = 0.f;
-    for (int h = 0; h < MKV_MAX_GROUP_DEV; ++h) {
-        if (h < G) {
-            a.qp[((size_t)r * Hq + g * G + h) * MKV_D + i] = acc[h];
-            qb += acc[h];
-        }
+    __syncthreads();
+    if (tid < MKV_D) {
+        float qb = 0.f;
+        for (int h = 0; h < G; ++h) qb += qo[h][tid];
+        a.qbar[(size_t)stream * MKV_D + tid] = qb;
     }
-    a.qbar[(size_t)stream * MKV_D + i] = qb;
-    for (int j = i; j < kHistBins; j += 128) a.hist[(size_t)stream * kHistBins + j] = 0u;
-    if (i < kStateWords) a.state[stream * kStateWords + i] = 0u;
 }
 
 hipError_t launch_dec_prep(const DecArgs& a, const Upload& tab, hipStream_t s) {
-    hipLaunchKernelGGL(k_dec_prep, dim3(a.B * a.Hkv), dim3(128), 0, s, a, tab);
+    hipLaunchKernelGGL(k_dec_prep, dim3(a.B * a.Hkv), dim3(256), 0, s, a, tab);
     return hipGetLastError();
 }
 
 // =====================================================================================================
 // score
 // =====================================================================================================
-// One 64-token segment of stream keys with C kept channels: 8 lanes per token, 8 tokens per pass.  Lane
-// (t8, sl) returns the score of token 8*sl + t8.
-template <int BV, int C>
-__device__ __forceinline__ float score_segment(const uint8_t* seg, int ns, const float* sq, int t8, int sl) {
-    constexpr int VPL = C / 8;                 // values per lane
-    constexpr int VB = VPL * BV;               // value bytes per lane
-    constexpr int VW = (VB + 3) / 4;
-    constexpr int IW = C < MKV_D ? (VPL + 3) / 4 : 1;
-    const uint8_t* vbase = seg + sl * VB;
-    const uint8_t* ibase = seg + (size_t)ns * C * BV + sl * VPL;
-    float mine = 0.f;
+// The segments of one workgroup are read as a flat sequence of passes.  In every pass each lane loads one
+// 16-byte chunk of stored values (8 bf16 or 4 fp32: VPL slots) and the matching VPL one-byte channel
+// indices, so a token with c kept channels spans LPT = c / VPL consecutive lanes and a pass covers
+// TPP = 64 / LPT tokens; the load shape is the same for every kept count.  A wave keeps kRing passes in
+// flight (their loads issued before the oldest one is consumed).
+constexpr int kRing = 8;
+constexpr int kMaxSpw = 64;
+constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past every workgroup's range: loads return 0
+
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+struct PassMeta {
+    int lc;      // log2 of the kept channels of the pass's segment
+    int tbase;   // stream-local index of the pass's first token
+    int tlim;    // stream-local end of the segment's tokens (-1: no pass)
+};
+
+// Walks a wave's segments (every fourth of the workgroup's) pass by pass.  All fields are wave-uniform and
+// every count is a power of two, so lanes-per-token and tokens-per-pass are shifts.
+template <int BV>
+struct PassIter {
+    static constexpr int LVPL = BV == 2 ? 3 : 2;    // log2 of values per lane per pass (16 bytes)
+    const uint32_t* s_rel;   // LDS: byte offset of each local segment from the workgroup's first one
+    const int* s_m;          // LDS: log2(kept channels) | tokens << 8
+    int k, kend, p, P, lc, ns, rel;
+
+    __device__ __forceinline__ void load_seg() {
+        const int kk = min(k, kend - 1);
+        const int w = uni(s_m[kk]);
+        rel = uni((int)s_rel[kk]);
+        lc = w & 0xFF;
+        ns = w >> 8;
+        const int ltpp = 6 + LVPL - lc;              // log2 tokens per pass
+        P = uni((ns + (1 << ltpp) - 1) >> ltpp);
+    }
+    __device__ __forceinline__ void next() {
+        p = uni(p + 1);
+        if (p == P) { p = 0; k = uni(k + 4); if (k < kend) load_seg(); }
+    }
+};
+
+// Issues the buffer loads of the iterator's current pass (or, past the wave's last pass, loads that the range
+// check turns into zeros without a memory access).  Lanes past the segment's last token get zeros the same way.
+template <int BV>
+__device__ __forceinline__ void issue_pass(PassIter<BV>& it, int lane, int seg_first, __amdgpu_buffer_rsrc_t rs,
+                                           u32x4& v, u32x2& ix, PassMeta& m) {
+    constexpr int LVPL = PassIter<BV>::LVPL, VPL = 1 << LVPL;
+    const bool live = it.k < it.kend;
+    const int llpt = it.lc - LVPL, ltpp = 6 - llpt;
+    const int s = seg_first + it.k;
+    m.lc = it.lc;
+    m.tbase = s * MKV_SEG + (it.p << ltpp);
+    m.tlim = live ? s * MKV_SEG + it.ns : -1;
+    const bool ok = live && (it.p << ltpp) + (lane >> llpt) < it.ns;
+    const uint32_t voff = ok ? (uint32_t)(it.rel + (it.p << 10) + lane * 16) : kOutOfRange;
+    const uint32_t ioff = (ok && it.lc < 7)
+        ? (uint32_t)(it.rel + ((it.ns << it.lc) * BV) + (it.p << (6 + LVPL)) + lane * VPL) : kOutOfRange;
+    v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0);
+    if constexpr (VPL == 8) ix = __builtin_amdgcn_raw_buffer_load_b64(rs, ioff, 0, 0);
+    else ix.x = __builtin_amdgcn_raw_buffer_load_b32(rs, ioff, 0, 0);
+    if (live) it.next();
+}
+
+template <int BV>
+__device__ __forceinline__ float bf_or_f(const uint32_t* w, int k) {
+    if constexpr (BV == 2) return (k & 1) ? __uint_as_float(w[k >> 1] & 0xFFFF0000u) : __uint_as_float(w[k >> 1] << 16);
+    else return __uint_as_float(w[k]);
+}
+
+template <int BV>
+__device__ __forceinline__ void consume_pass(const u32x4& v, const u32x2& ix, const PassMeta& m, int lane,
+                                             const float* sq, uint32_t* keys, uint32_t* sh) {
+    constexpr int LVPL = PassIter<BV>::LVPL, VPL = 1 << LVPL;
+    const int llpt = m.lc - LVPL;
+    const int sub = lane & ((1 << llpt) - 1);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float acc = 0.f;
+    if (m.lc == 7) {
+        // every channel stored: this lane holds channels [sub*VPL, sub*VPL + VPL)
+        const f32x4* q4 = reinterpret_cast<const f32x4*>(sq + sub * VPL);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        uint32_t vw[4][VW], iw[4][IW];
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-            const int tk = (half * 4 + pp) * 8 + t8;
-            if (tk < ns) {
-                ldb<VB>(vw[pp], vbase + (size_t)tk * C * BV);
-                if constexpr (C < MKV_D) ldb<VPL>(iw[pp], ibase + (size_t)tk * C);
-            } else {
-#pragma unroll
-                for (int x = 0; x < VW; ++x) vw[pp][x] = 0u;
-#pragma unroll
-                for (int x = 0; x < IW; ++x) iw[pp][x] = 0u;
-            }
+        for (int j = 0; j < VPL / 4; ++j) {
+            const f32x4 qq = q4[j];
+            acc = fmaf(qq.x, bf_or_f<BV>(w, 4 * j), acc);
+            acc = fmaf(qq.y, bf_or_f<BV>(w, 4 * j + 1), acc);
+            acc = fmaf(qq.z, bf_or_f<BV>(w, 4 * j + 2), acc);
+            acc = fmaf(qq.w, bf_or_f<BV>(w, 4 * j + 3), acc);
         }
+    } else {
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-            float acc = 0.f;
-#pragma unroll
-            for (int k = 0; k < VPL; ++k) {
-                const int ch = (C == MKV_D) ? sl * VPL + k : idx_at(iw[pp], k);
-                acc = fmaf(sq[ch], val_at<BV>(vw[pp], k), acc);
-            }
-            acc = sum8(acc);
-            if (sl == half * 4 + pp) mine = acc;
+        for (int k = 0; k < VPL; ++k) {
+            const uint32_t iw = k < 4 ? ix.x : ix.y;
+            const uint32_t ch = (iw >> (8 * (k & 3))) & 0xFFu;   // < 128 for stored data
+            acc = fmaf(sq[ch], bf_or_f<BV>(w, k), acc);
         }
     }
-    return mine;
+    acc += dpp_f<0xB1>(acc);                    // pairs
+    if (llpt >= 2) acc += dpp_f<0x4E>(acc);     // quads
+    if (llpt >= 3) acc += dpp_f<0x141>(acc);    // groups of 8 (half-row mirror)
+    if (llpt >= 4) acc += dpp_f<0x140>(acc);    // rows of 16 (row mirror)
+    if (llpt >= 5) acc += __shfl_xor(acc, 16, MKV_WAVE);
+    const int t = m.tbase + (lane >> llpt);
+    if (sub == 0 && t < m.tlim) {
+        const uint32_t key = score_key(acc);
+        keys[t] = key;
+        atomicAdd(&sh[key >> 20], 1u);
+    }
 }
 
 template <int BV>
 __global__ __launch_bounds__(256) void k_score(DecArgs a) {
-    __shared__ float sq[MKV_D];
+    __shared__ float sq[2 * MKV_D];             // Qbar, then a zero pad that index bytes >= 128 can never reach
     __shared__ uint32_t sh[kHistBins];
-    __shared__ uint32_t tmp[8];
-    __shared__ int s_last;
+    __shared__ uint32_t s_rel[kMaxSpw];
+    __shared__ int s_m[kMaxSpw];
+    __shared__ uint64_t s_base;
+    __shared__ uint32_t s_span;
     const int b = blockIdx.x;
     const int r = find_slot(a.t_sblk, a.B, b);
     const int n = a.t_n[r], Sr = (n + MKV_SEG - 1) / MKV_SEG, nch = (Sr + a.spw - 1) / a.spw;
@@ -152,69 +235,64 @@ __global__ __launch_bounds__(256) void k_score(DecArgs a) {
     const int64_t seg0 = (int64_t)a.Hkv * a.t_segbase[r] + (int64_t)g * Sr;
     const int64_t keybase = (int64_t)a.t_tokbase[r] * a.Hkv + (int64_t)g * n;
     const int tid = threadIdx.x;
+    const int s0 = chunk * a.spw, s1 = min(Sr, s0 + a.spw), nloc = s1 - s0;
     for (int i = tid; i < kHistBins; i += 256) sh[i] = 0u;
-    if (tid < MKV_D) sq[tid] = a.qbar[(size_t)stream * MKV_D + tid];
+    if (tid < MKV_D) {
+        sq[tid] = a.qbar[(size_t)stream * MKV_D + tid];
+        sq[MKV_D + tid] = 0.f;
+    }
+    if (tid < nloc) {
+        const uint64_t off = a.seg_off[seg0 + s0 + tid], base = a.seg_off[seg0 + s0];
+        const int c = a.keep[a.codes[seg0 + s0 + tid]];
+        const int ns = min(MKV_SEG, n - (s0 + tid) * MKV_SEG);
+        s_rel[tid] = (uint32_t)(off - base);
+        s_m[tid] = (31 - __clz(c)) | (ns << 8);
+        if (tid == nloc - 1) {
+            s_base = base;
+            s_span = (uint32_t)(off - base) + (uint32_t)(ns * c * (BV + (c < MKV_D ? 1 : 0)));
+        }
+    }
     __syncthreads();
 
-    const int wid = tid >> 6, lane = tid & 63, t8 = lane >> 3, sl = lane & 7;
-    const int s0 = chunk * a.spw, s1 = min(Sr, s0 + a.spw);
-    for (int s = s0 + wid; s < s1; s += 4) {
-        const int64_t gs = seg0 + s;
-        const int c = a.keep[a.codes[gs]];
-        const uint8_t* seg = a.payload + a.seg_off[gs];
-        const int ns = min(MKV_SEG, n - s * MKV_SEG);
-        float sc;
-        switch (c) {
-            case 128: sc = score_segment<BV, 128>(seg, ns, sq, t8, sl); break;
-            case 64: sc = score_segment<BV, 64>(seg, ns, sq, t8, sl); break;
-            case 32: sc = score_segment<BV, 32>(seg, ns, sq, t8, sl); break;
-            default: sc = score_segment<BV, 16>(seg, ns, sq, t8, sl); break;
+    const int wid = uni(tid >> 6), lane = tid & 63;   // the wave index is uniform across the wave
+    if (wid < nloc) {
+        const uint64_t base = s_base;
+        const uint32_t blo = (uint32_t)uni((int)(uint32_t)base), bhi = (uint32_t)uni((int)(uint32_t)(base >> 32));
+        const uint8_t* bp = a.payload + (((uint64_t)bhi << 32) | blo);
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)bp, (short)0, uni((int)s_span), 0x00020000);
+        PassIter<BV> it;
+        it.s_rel = s_rel;
+        it.s_m = s_m;
+        it.k = wid;
+        it.kend = nloc;
+        it.p = 0;
+        it.load_seg();
+        int np = 0;   // passes of this wave
+        for (int k = wid; k < nloc; k += 4) {
+            const int w = s_m[k], ltpp = 6 + PassIter<BV>::LVPL - (w & 0xFF), ns = w >> 8;
+            np += (ns + (1 << ltpp) - 1) >> ltpp;
         }
-        const int tok = sl * 8 + t8;
-        if (tok < ns) {
-            const uint32_t key = score_key(sc);
-            a.keys[keybase + (int64_t)s * MKV_SEG + tok] = key;
-            atomicAdd(&sh[key >> 20], 1u);
+        np = uni(np);
+        uint32_t* keys = a.keys + keybase;
+        u32x4 v[kRing];
+        u32x2 ix[kRing];
+        PassMeta m[kRing];
+#pragma unroll
+        for (int k = 0; k < kRing; ++k) issue_pass<BV>(it, lane, s0, rs, v[k], ix[k], m[k]);
+        for (int base = 0; base < np; base += kRing) {
+#pragma unroll
+            for (int k = 0; k < kRing; ++k) {
+                consume_pass<BV>(v[k], ix[k], m[k], lane, sq, keys, sh);
+                issue_pass<BV>(it, lane, s0, rs, v[k], ix[k], m[k]);
+            }
         }
     }
     __syncthreads();
     uint32_t* gh = a.hist + (size_t)stream * kHistBins;
     for (int i = tid; i < kHistBins; i += 256) {
-        const uint32_t v = sh[i];
-        if (v) atomic_add_dev(&gh[i], v);
-    }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t old = atomic_add_acqrel_dev(&a.state[stream * kStateWords + ST_DONE], 1u);
-        s_last = (old == (uint32_t)(nch - 1));
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
-
-    // Last workgroup of the stream: the bin of the T-th largest key.  Thread t owns bins
-    // [4095 - 16t - 15, 4095 - 16t], scanned from the top.
-    const uint32_t T = (uint32_t)a.t_T[r];
-    uint32_t cnt[16], loc = 0;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) { cnt[k] = load_dev(&gh[kHistBins - 1 - (16 * tid + k)]); loc += cnt[k]; }
-    uint32_t total;
-    const uint32_t above = block_exscan(loc, tmp, &total);
-    if (above < T && above + loc >= T) {
-        uint32_t run = above;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            if (run + cnt[k] >= T) {
-                uint32_t* st = a.state + stream * kStateWords;
-                st[ST_P1] = (uint32_t)(kHistBins - 1 - (16 * tid + k));
-                st[ST_NGT] = run;
-                st[ST_NCAND] = cnt[k];
-                st[ST_NEED] = T - run;
-                break;
-            }
-            run += cnt[k];
-        }
+        const uint32_t c = sh[i];
+        if (c) atomic_add_dev(&gh[i], c);
     }
 }
 
@@ -245,10 +323,46 @@ __device__ __forceinline__ KBlock kblock(const DecArgs& a) {
     return k;
 }
 
+// The bin of the T-th largest key in the stream's first-level histogram (complete once the score kernel has
+// finished): bins are scanned from the top, thread t owning bins [4095 - 16t - 15, 4095 - 16t].  Every block of
+// the stream computes it; block 0 records it in the stream's selection state for the later kernels.
+__device__ __forceinline__ uint32_t threshold_bin(const DecArgs& a, int stream, uint32_t T, bool record,
+                                                  uint32_t* tmp, uint32_t* s_p1) {
+    const int tid = threadIdx.x;
+    const uint32_t* gh = a.hist + (size_t)stream * kHistBins;
+    uint32_t cnt[16], loc = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) { cnt[k] = gh[kHistBins - 1 - (16 * tid + k)]; loc += cnt[k]; }
+    uint32_t total;
+    const uint32_t above = block_exscan(loc, tmp, &total);
+    if (above < T && above + loc >= T) {
+        uint32_t run = above;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            if (run + cnt[k] >= T) {
+                const uint32_t p1 = (uint32_t)(kHistBins - 1 - (16 * tid + k));
+                *s_p1 = p1;
+                if (record) {
+                    uint32_t* st = a.state + stream * kStateWords;
+                    st[ST_P1] = p1;
+                    st[ST_NGT] = run;
+                    st[ST_NCAND] = cnt[k];
+                    st[ST_NEED] = T - run;
+                }
+                break;
+            }
+            run += cnt[k];
+        }
+    }
+    __syncthreads();
+    return *s_p1;
+}
+
 __global__ __launch_bounds__(256) void k_sel_count(DecArgs a) {
     __shared__ uint32_t tmp[8];
+    __shared__ uint32_t s_p1;
     const KBlock k = kblock(a);
-    const uint32_t p1 = a.state[k.stream * kStateWords + ST_P1];
+    const uint32_t p1 = threshold_bin(a, k.stream, (uint32_t)a.t_T[k.r], k.kb == 0, tmp, &s_p1);
     const int lo = k.kb * kKeysPerBlock, cnt = min(kKeysPerBlock, k.n - lo);
     const uint32_t* keys = a.keys + k.keybase + lo;
     uint32_t c = 0;
@@ -574,8 +688,18 @@ __global__ __launch_bounds__(256) void k_combine(DecArgs a) {
         o[h][ch] = (Ls > 0.f) ? O / Ls : 0.f;
     }
     const float* Bv = a.basis ? a.basis + ((((size_t)r * a.Hkv + g) * 2 + 1) << 14) : nullptr;
-    if (Bv)
-        for (int i = tid; i < MKV_D * MKV_D; i += 256) bsh[(i >> 7) * (MKV_D + 1) + (i & 127)] = Bv[i];
+    if (Bv) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(Bv);
+        f32x4 v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = src[tid + 256 * j];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int e = 4 * (tid + 256 * j), row = e >> 7, col = e & 127;
+            float* d = &bsh[row * (MKV_D + 1) + col];
+            d[0] = v[j].x; d[1] = v[j].y; d[2] = v[j].z; d[3] = v[j].w;
+        }
+    }
     __syncthreads();
     for (int i = tid; i < G * MKV_D; i += 256) {
         const int h = i >> 7, row = i & 127;

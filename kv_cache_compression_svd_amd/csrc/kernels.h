@@ -12,7 +12,7 @@ constexpr int kKeysPerBlock = 4096;     // keys per workgroup in the selection p
 constexpr int kAttnChunk = 256;         // selected tokens per attention workgroup
 
 // selection state words
-enum { ST_DONE = 0, ST_P1 = 1, ST_NGT = 2, ST_NCAND = 3, ST_NEED = 4 };
+enum { ST_P1 = 1, ST_NGT = 2, ST_NCAND = 3, ST_NEED = 4 };
 
 struct Upload {
     int32_t* dst;
