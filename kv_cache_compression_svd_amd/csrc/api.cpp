@@ -167,7 +167,7 @@ StoreLayout store_layout(const Shape& sh) {
     L.basis = align_up(L.seg_off + 16 * (uint64_t)sh.S);
     L.payload = align_up(L.basis + (uint64_t)sh.B * sh.Hkv * 2 * MKV_HEAD_DIM * MKV_HEAD_DIM * sizeof(float));
     L.capacity = 2ull * sh.Hkv * (uint64_t)sh.total * MKV_HEAD_DIM * dtype_bytes(sh.dtype);
-    L.bytes = L.payload + L.capacity;
+    L.bytes = L.payload + L.capacity + kAlign;   // slack: fixed-shape row loads may read past the last row
     return L;
 }
 
@@ -370,7 +370,8 @@ mkv_status plan_decode(const mkv_store* s, int32_t n_q_heads, const int32_t* T, 
     if (P->G != 1 && P->G != 2 && P->G != 4 && P->G != 8) return fail(MKV_E_UNSUPPORTED, "query heads per KV head must be 1, 2, 4 or 8 (got %d)", P->G);
     P->Hq = n_q_heads;
     const int B = sh.B;
-    P->spw = (int32_t)std::max<int64_t>(4, std::min<int64_t>(64, sh.S / 2048));
+    // segments per score workgroup: about 16K workgroups for long contexts (short tail round), 4..16
+    P->spw = (int32_t)std::max<int64_t>(4, std::min<int64_t>(16, sh.S / 16384));
     P->tab.assign(7 * B + 3, 0);
     int32_t* tn = P->tab.data();
     int32_t* tseg = tn + B;

@@ -115,7 +115,7 @@ hipError_t launch_dec_prep(const DecArgs& a, const Upload& tab, hipStream_t s) {
 // TPP = 64 / LPT tokens; the load shape is the same for every kept count.  A wave keeps kRing passes in
 // flight (their loads issued before the oldest one is consumed).
 constexpr int kRing = 8;
-constexpr int kMaxSpw = 64;
+constexpr int kMaxSpw = 16;
 constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past every workgroup's range: loads return 0
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -158,7 +158,7 @@ __device__ __forceinline__ void issue_pass(PassIter<BV>& it, int lane, int seg_f
     constexpr int LVPL = PassIter<BV>::LVPL, VPL = 1 << LVPL;
     const bool live = it.k < it.kend;
     const int llpt = it.lc - LVPL, ltpp = 6 - llpt;
-    const int s = seg_first + it.k;
+    const int s = seg_first + it.k;   // segment index relative to the first segment of the workgroup
     m.lc = it.lc;
     m.tbase = s * MKV_SEG + (it.p << ltpp);
     m.tlim = live ? s * MKV_SEG + it.ns : -1;
@@ -180,7 +180,7 @@ __device__ __forceinline__ float bf_or_f(const uint32_t* w, int k) {
 
 template <int BV>
 __device__ __forceinline__ void consume_pass(const u32x4& v, const u32x2& ix, const PassMeta& m, int lane,
-                                             const float* sq, uint32_t* keys, uint32_t* sh) {
+                                             const float* sq, uint32_t* skeys) {
     constexpr int LVPL = PassIter<BV>::LVPL, VPL = 1 << LVPL;
     const int llpt = m.lc - LVPL;
     const int sub = lane & ((1 << llpt) - 1);
@@ -211,17 +211,14 @@ __device__ __forceinline__ void consume_pass(const u32x4& v, const u32x2& ix, co
     if (llpt >= 4) acc += dpp_f<0x140>(acc);    // rows of 16 (row mirror)
     if (llpt >= 5) acc += __shfl_xor(acc, 16, MKV_WAVE);
     const int t = m.tbase + (lane >> llpt);
-    if (sub == 0 && t < m.tlim) {
-        const uint32_t key = score_key(acc);
-        keys[t] = key;
-        atomicAdd(&sh[key >> 20], 1u);
-    }
+    if (sub == 0 && t < m.tlim) skeys[t] = score_key(acc);
 }
 
 template <int BV>
 __global__ __launch_bounds__(256) void k_score(DecArgs a) {
     __shared__ float sq[2 * MKV_D];             // Qbar, then a zero pad that index bytes >= 128 can never reach
     __shared__ uint32_t sh[kHistBins];
+    __shared__ uint32_t skeys[kMaxSpw * MKV_SEG];   // this workgroup's keys, written out coalesced at the end
     __shared__ uint32_t s_rel[kMaxSpw];
     __shared__ int s_m[kMaxSpw];
     __shared__ uint64_t s_base;
@@ -274,18 +271,27 @@ __global__ __launch_bounds__(256) void k_score(DecArgs a) {
             np += (ns + (1 << ltpp) - 1) >> ltpp;
         }
         np = uni(np);
-        uint32_t* keys = a.keys + keybase;
         u32x4 v[kRing];
         u32x2 ix[kRing];
         PassMeta m[kRing];
 #pragma unroll
-        for (int k = 0; k < kRing; ++k) issue_pass<BV>(it, lane, s0, rs, v[k], ix[k], m[k]);
+        for (int k = 0; k < kRing; ++k) issue_pass<BV>(it, lane, 0, rs, v[k], ix[k], m[k]);
         for (int base = 0; base < np; base += kRing) {
 #pragma unroll
             for (int k = 0; k < kRing; ++k) {
-                consume_pass<BV>(v[k], ix[k], m[k], lane, sq, keys, sh);
-                issue_pass<BV>(it, lane, s0, rs, v[k], ix[k], m[k]);
+                consume_pass<BV>(v[k], ix[k], m[k], lane, sq, skeys);
+                issue_pass<BV>(it, lane, 0, rs, v[k], ix[k], m[k]);
             }
+        }
+    }
+    __syncthreads();
+    {   // keys out (coalesced) and the workgroup histogram
+        const int ntok = min(n - s0 * MKV_SEG, nloc * MKV_SEG);
+        uint32_t* keys = a.keys + keybase + (int64_t)s0 * MKV_SEG;
+        for (int i = tid; i < ntok; i += 256) {
+            const uint32_t key = skeys[i];
+            keys[i] = key;
+            atomicAdd(&sh[key >> 20], 1u);
         }
     }
     __syncthreads();
@@ -498,34 +504,50 @@ hipError_t launch_sel_final(const DecArgs& a, hipStream_t s) {
 // =====================================================================================================
 // sparse exact attention over the selected tokens
 // =====================================================================================================
-// Partial logits of the G query heads against this lane's slots of a key row with C kept channels.
-template <int BV, int C, int G>
-__device__ __forceinline__ void key_row(const uint8_t* seg, int ns, int tt, int sl, const float* qt, float* lg) {
-    constexpr int VPL = C / 8, VB = VPL * BV, VW = (VB + 3) / 4, IW = C < MKV_D ? (VPL + 3) / 4 : 1;
-    uint32_t vw[VW], iw[IW];
-    ldb<VB>(vw, seg + (size_t)tt * C * BV + sl * VB);
-    if constexpr (C < MKV_D) ldb<VPL>(iw, seg + (size_t)ns * C * BV + (size_t)tt * C + sl * VPL);
+// One selected token's row, as seen by the 8 lanes of its group: each lane owns c/8 consecutive slots.  The
+// lane loads a fixed shape whatever c is (16 slots of values, 8 index bytes from a 4-byte aligned address);
+// bytes past its slots are ignored, and the store keeps slack after the payload for these over-reads.
+template <int BV>
+struct RowBuf {
+    static constexpr int VW = 16 * BV / 4;   // value words per lane (16 slots)
+    uint32_t v[VW];
+    uint32_t ix[2];
+};
+
+struct RowMeta {
+    uint64_t vaddr;   // first value byte of the token's row in the segment
+    uint64_t iaddr;   // first index byte of the token's row (unused when c == 128)
+};
+
+template <int BV>
+__device__ __forceinline__ void load_row(RowBuf<BV>& rb, const uint8_t* payload, uint64_t vrow, uint64_t irow, int lc,
+                                         int sl, bool ok) {
+    const int nsl_shift = lc - 3;                       // log2 of slots per lane
+    const uint8_t* va = ok ? payload + vrow + (size_t)(sl << nsl_shift) * BV : payload;
+    const uint64_t ib = irow + (uint64_t)(sl << nsl_shift);
+    const uint8_t* ia = ok ? payload + (ib & ~3ull) : payload;
 #pragma unroll
-    for (int k = 0; k < VPL; ++k) {
-        const int ch = (C == MKV_D) ? sl * VPL + k : idx_at(iw, k);
-        const float v = val_at<BV>(vw, k);
-#pragma unroll
-        for (int h = 0; h < G; ++h) lg[h] = fmaf(qt[ch * G + h], v, lg[h]);
+    for (int j = 0; j < RowBuf<BV>::VW / 4; ++j) {
+        const u32x4 x = reinterpret_cast<const u32x4*>(va)[j];
+        rb.v[4 * j] = x.x; rb.v[4 * j + 1] = x.y; rb.v[4 * j + 2] = x.z; rb.v[4 * j + 3] = x.w;
     }
+    const u32x2 y = *reinterpret_cast<const u32x2*>(ia);
+    const int sh = ok ? (int)(ib & 3) * 8 : 0;
+    // drop the misaligned leading bytes (only c = 16 has them)
+    rb.ix[0] = sh ? ((y.x >> sh) | (y.y << (32 - sh))) : y.x;
+    rb.ix[1] = sh ? (y.y >> sh) : y.y;
 }
 
-// Scatter this lane's slots of a value row into a dense 128-float row.
-template <int BV, int C>
-__device__ __forceinline__ void value_row(const uint8_t* seg, int ns, int tt, int sl, float* dense) {
-    constexpr int VPL = C / 8, VB = VPL * BV, VW = (VB + 3) / 4, IW = C < MKV_D ? (VPL + 3) / 4 : 1;
-    uint32_t vw[VW], iw[IW];
-    ldb<VB>(vw, seg + (size_t)tt * C * BV + sl * VB);
-    if constexpr (C < MKV_D) ldb<VPL>(iw, seg + (size_t)ns * C * BV + (size_t)tt * C + sl * VPL);
-#pragma unroll
-    for (int k = 0; k < VPL; ++k) {
-        const int ch = (C == MKV_D) ? sl * VPL + k : idx_at(iw, k);
-        dense[ch] = val_at<BV>(vw, k);
-    }
+template <int BV>
+__device__ __forceinline__ float row_val(const RowBuf<BV>& rb, int k) {
+    if constexpr (BV == 2) return (k & 1) ? __uint_as_float(rb.v[k >> 1] & 0xFFFF0000u) : __uint_as_float(rb.v[k >> 1] << 16);
+    else return __uint_as_float(rb.v[k]);
+}
+
+// channel of slot k of this lane (k < 8 for stored indices; c == 128 uses the slot position)
+__device__ __forceinline__ int row_ch(const uint32_t* ix, int lc, int sl, int k) {
+    if (lc == 7) return sl * 16 + k;
+    return (ix[k >> 2] >> (8 * (k & 3))) & 0xFF;
 }
 
 template <int BV, int G>
@@ -535,6 +557,8 @@ __global__ __launch_bounds__(256) void k_attend(DecArgs a) {
     __shared__ float pt[4][8][G];
     __shared__ float wm[4][G], wl[4][G];
     __shared__ float wacc[4][G][MKV_D];
+    __shared__ RowMeta mk[4][64], mv[4][64];
+    __shared__ int mc[4][64];     // log2 c of K | log2 c of V << 8 | valid << 16
     const int b = blockIdx.x;
     const int r = find_slot(a.t_ablk, a.B, b);
     const int n = a.t_n[r], T = a.t_T[r], Sr = (n + MKV_SEG - 1) / MKV_SEG;
@@ -542,44 +566,87 @@ __global__ __launch_bounds__(256) void k_attend(DecArgs a) {
     const int local = b - a.t_ablk[r];
     const int g = local / nach, chunk = local - g * nach;
     const int stream = r * a.Hkv + g, Hq = a.G * a.Hkv;
-    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63, t8 = lane >> 3, sl = lane & 7;
+    const int tid = threadIdx.x, wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int t8 = lane >> 3, sl = lane & 7;
     for (int i = tid; i < MKV_D * G; i += 256) {
         const int h = i >> 7, ch = i & 127;
         qt[ch * G + h] = a.qp[((size_t)r * Hq + g * G + h) * MKV_D + ch];
     }
+    {   // this lane's token: list entry, segments, row addresses
+        const int32_t* list = a.sel_int + (size_t)stream * a.sel_int_stride;
+        const int li = chunk * kAttnChunk + wid * 64 + lane;
+        const int j = (li < T) ? list[li] : -1;
+        int word = 0;
+        RowMeta k_{0, 0}, v_{0, 0};
+        if (j >= 0) {
+            const int s = j >> 6, tt = j & 63, ns = min(MKV_SEG, n - s * MKV_SEG);
+            const int64_t gk = (int64_t)a.Hkv * a.t_segbase[r] + (int64_t)g * Sr + s, gv = a.S + gk;
+            const int ck = a.keep[a.codes[gk]], cv = a.keep[a.codes[gv]];
+            const uint64_t ok_ = a.seg_off[gk], ov = a.seg_off[gv];
+            const int lck = 31 - __clz(ck), lcv = 31 - __clz(cv);
+            k_.vaddr = ok_ + ((uint64_t)tt << lck) * BV;
+            k_.iaddr = ok_ + ((uint64_t)ns << lck) * BV + ((uint64_t)tt << lck);
+            v_.vaddr = ov + ((uint64_t)tt << lcv) * BV;
+            v_.iaddr = ov + ((uint64_t)ns << lcv) * BV + ((uint64_t)tt << lcv);
+            word = lck | (lcv << 8) | (1 << 16);
+        } else {
+            word = 7 | (7 << 8);
+        }
+        mk[wid][lane] = k_;
+        mv[wid][lane] = v_;
+        mc[wid][lane] = word;
+    }
     __syncthreads();
-    const int32_t* list = a.sel_int + (size_t)stream * a.sel_int_stride;
-    const int64_t segK = (int64_t)a.Hkv * a.t_segbase[r] + (int64_t)g * Sr;
-    const int64_t segV = a.S + segK;
     const float scale = 1.4426950408889634f * 0.08838834764831845f;   // log2(e) / sqrt(128)
     float m[G], l[G], acc[G][2];
 #pragma unroll
     for (int h = 0; h < G; ++h) { m[h] = -INFINITY; l[h] = 0.f; acc[h][0] = 0.f; acc[h][1] = 0.f; }
 
-    for (int pass = 0; pass < 8; ++pass) {
-        const int li = chunk * kAttnChunk + wid * 64 + pass * 8 + t8;
-        const int j = (li < T) ? list[li] : -1;
+    RowBuf<BV> kb[2], vbuf[2];
+    int wd[2];
+    {
+        const int w0 = mc[wid][t8];
+        const RowMeta k0 = mk[wid][t8], v0 = mv[wid][t8];
+        load_row<BV>(kb[0], a.payload, k0.vaddr, k0.iaddr, w0 & 0xFF, sl, (w0 >> 16) & 1);
+        load_row<BV>(vbuf[0], a.payload, v0.vaddr, v0.iaddr, (w0 >> 8) & 0xFF, sl, (w0 >> 16) & 1);
+        wd[0] = w0;
+    }
+#pragma unroll 1
+    for (int pp = 0; pp < 8; pp += 2) {
+#pragma unroll
+    for (int cur = 0; cur < 2; ++cur) {
+        const int pass = pp + cur, nxt = cur ^ 1;
+        if (pass + 1 < 8) {
+            const int tk = (pass + 1) * 8 + t8;
+            const int w1 = mc[wid][tk];
+            const RowMeta k1 = mk[wid][tk], v1 = mv[wid][tk];
+            load_row<BV>(kb[nxt], a.payload, k1.vaddr, k1.iaddr, w1 & 0xFF, sl, (w1 >> 16) & 1);
+            load_row<BV>(vbuf[nxt], a.payload, v1.vaddr, v1.iaddr, (w1 >> 8) & 0xFF, sl, (w1 >> 16) & 1);
+            wd[nxt] = w1;
+        }
+        const int w = wd[cur];
+        const bool valid = (w >> 16) & 1;
+        const int lck = w & 0xFF, lcv = (w >> 8) & 0xFF;
+        const int nk = 1 << (lck - 3), nv = 1 << (lcv - 3);
         float lg[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) lg[h] = 0.f;
-        int s = 0, tt = 0, ns = 0;
-        if (j >= 0) {
-            s = j >> 6; tt = j & 63; ns = min(MKV_SEG, n - s * MKV_SEG);
-            const int64_t gs = segK + s;
-            const int c = a.keep[a.codes[gs]];
-            const uint8_t* seg = a.payload + a.seg_off[gs];
-            switch (c) {
-                case 128: key_row<BV, 128, G>(seg, ns, tt, sl, qt, lg); break;
-                case 64: key_row<BV, 64, G>(seg, ns, tt, sl, qt, lg); break;
-                case 32: key_row<BV, 32, G>(seg, ns, tt, sl, qt, lg); break;
-                default: key_row<BV, 16, G>(seg, ns, tt, sl, qt, lg); break;
+        const bool wide = __builtin_amdgcn_readfirstlane(__ballot(lck == 7 || lcv == 7) != 0);
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+            if (k < 8 || wide) {
+                const bool on = k < nk;
+                const int ch = on ? row_ch(kb[cur].ix, lck, sl, k) : 0;
+                const float x = on ? row_val<BV>(kb[cur], k) : 0.f;
+#pragma unroll
+                for (int h = 0; h < G; ++h) lg[h] = fmaf(qt[ch * G + h], x, lg[h]);
             }
         }
         float sc[G], p[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) {
             lg[h] = sum8(lg[h]);
-            lg[h] = (j >= 0) ? lg[h] * scale : -INFINITY;
+            lg[h] = valid ? lg[h] * scale : -INFINITY;
             float pm = lg[h];
             pm = fmaxf(pm, __shfl_xor(pm, 8, MKV_WAVE));
             pm = fmaxf(pm, __shfl_xor(pm, 16, MKV_WAVE));
@@ -595,15 +662,10 @@ __global__ __launch_bounds__(256) void k_attend(DecArgs a) {
         *reinterpret_cast<f32x4*>(&dense[sl * 16 + 8]) = f32x4{0.f, 0.f, 0.f, 0.f};
         *reinterpret_cast<f32x4*>(&dense[sl * 16 + 12]) = f32x4{0.f, 0.f, 0.f, 0.f};
         wave_lds_sync();
-        if (j >= 0) {
-            const int64_t gs = segV + s;
-            const int c = a.keep[a.codes[gs]];
-            const uint8_t* seg = a.payload + a.seg_off[gs];
-            switch (c) {
-                case 128: value_row<BV, 128>(seg, ns, tt, sl, dense); break;
-                case 64: value_row<BV, 64>(seg, ns, tt, sl, dense); break;
-                case 32: value_row<BV, 32>(seg, ns, tt, sl, dense); break;
-                default: value_row<BV, 16>(seg, ns, tt, sl, dense); break;
+        if (valid) {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                if ((k < 8 || wide) && k < nv) dense[row_ch(vbuf[cur].ix, lcv, sl, k)] = row_val<BV>(vbuf[cur], k);
             }
         }
         if (sl == 0) {
@@ -632,6 +694,7 @@ __global__ __launch_bounds__(256) void k_attend(DecArgs a) {
         }
         wave_lds_sync();
     }
+    }
     if (lane == 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h) { wm[wid][h] = m[h]; wl[wid][h] = l[h]; }
@@ -643,15 +706,15 @@ __global__ __launch_bounds__(256) void k_attend(DecArgs a) {
         const int h = i >> 7, ch = i & 127;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) M = fmaxf(M, wm[w][h]);
+        for (int w2 = 0; w2 < 4; ++w2) M = fmaxf(M, wm[w2][h]);
         float O = 0.f, Ls = 0.f;
         if (M != -INFINITY) {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                if (wm[w][h] != -INFINITY) {
-                    const float f = exp2f(wm[w][h] - M);
-                    O = fmaf(wacc[w][h][ch], f, O);
-                    Ls = fmaf(wl[w][h], f, Ls);
+            for (int w2 = 0; w2 < 4; ++w2) {
+                if (wm[w2][h] != -INFINITY) {
+                    const float f = exp2f(wm[w2][h] - M);
+                    O = fmaf(wacc[w2][h][ch], f, O);
+                    Ls = fmaf(wl[w2][h], f, Ls);
                 }
             }
         }
@@ -673,9 +736,11 @@ __global__ __launch_bounds__(256) void k_combine(DecArgs a) {
     for (int i = tid; i < G * MKV_D; i += 256) {
         const int h = i >> 7, ch = i & 127;
         float M = -INFINITY;
+#pragma unroll 8
         for (int c = 0; c < nach; ++c) M = fmaxf(M, a.part[((size_t)(first + c) * G + h) * (MKV_D + 2)]);
         float O = 0.f, Ls = 0.f;
         if (M != -INFINITY) {
+#pragma unroll 8
             for (int c = 0; c < nach; ++c) {
                 const float* pp = a.part + ((size_t)(first + c) * G + h) * (MKV_D + 2);
                 if (pp[0] != -INFINITY) {
