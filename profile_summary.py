@@ -30,9 +30,42 @@ def pmc(db, pat=None):
             print(f"{name[:64]:64s} {cn:>12s} {v:18.1f} {n:10d}")
 
 
+def _avg(db, counter, pat):
+    c = sqlite3.connect(db)
+    rows = list(c.execute("select name, avg(counter_value), count(*) from pmc_events where counter_name = ? "
+                          "group by name", (counter,)))
+    rows = [r for r in rows if pat in r[0]]
+    if len(rows) != 1:
+        raise SystemExit(f"{db}: expected one kernel matching {pat!r} with {counter}, got {rows}")
+    return rows[0][1], rows[0][2]
+
+
+def traffic(kernel_pat, fetch_db, write_db, copy_fetch_db, copy_write_db, copy_bytes, source_hash):
+    """HBM bytes per dispatch of one kernel from FETCH_SIZE and WRITE_SIZE passes (KiB per dispatch), each
+    scaled by what the same counter reads for a device copy of copy_bytes bytes."""
+    f, nf = _avg(fetch_db, "FETCH_SIZE", kernel_pat)
+    w, nw = _avg(write_db, "WRITE_SIZE", kernel_pat)
+    cf, _ = _avg(copy_fetch_db, "FETCH_SIZE", "copyBuffer")
+    cw, _ = _avg(copy_write_db, "WRITE_SIZE", "copyBuffer")
+    kf = copy_bytes / (cf * 1024.0)
+    kw = copy_bytes / (cw * 1024.0)
+    print(f"kernel_pattern: {kernel_pat}")
+    print(f"fetch_kib_per_dispatch: {f:.1f}  (dispatches {nf})")
+    print(f"write_kib_per_dispatch: {w:.1f}  (dispatches {nw})")
+    print(f"copy_fetch_kib_per_dispatch: {cf:.1f}")
+    print(f"copy_write_kib_per_dispatch: {cw:.1f}")
+    print(f"copy_bytes: {copy_bytes}")
+    print(f"fetch_factor: {kf:.4f}")
+    print(f"write_factor: {kw:.4f}")
+    print(f"traffic_bytes_per_dispatch: {f * 1024.0 * kf + w * 1024.0 * kw:.0f}")
+    print(f"source_sha256_16: {source_hash}")
+
+
 if __name__ == "__main__":
-    mode, db = sys.argv[1], sys.argv[2]
+    mode = sys.argv[1]
     if mode == "trace":
-        trace(db)
-    else:
-        pmc(db, sys.argv[3] if len(sys.argv) > 3 else None)
+        trace(sys.argv[2])
+    elif mode == "pmc":
+        pmc(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else None)
+    elif mode == "traffic":
+        traffic(sys.argv[2], *sys.argv[3:7], int(sys.argv[7]), sys.argv[8])
