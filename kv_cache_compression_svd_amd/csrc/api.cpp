@@ -36,11 +36,11 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ---- kernel timing --------------------------------------------------------------------------------------
 enum KernelId {
-    K_UPLOAD = 0, K_CMP_DECIDE, K_CMP_SCAN, K_CMP_PACK, K_DEC_PREP, K_SCORE, K_SEL_COUNT, K_SEL_WRITE,
-    K_SEL_FINAL, K_ATTEND, K_COMBINE, K_COUNT
+    K_UPLOAD = 0, K_CMP_DECIDE, K_CMP_SCAN, K_CMP_PACK, K_DEC_PREP, K_SCORE, K_SEL_COLLECT, K_SEL_EMIT,
+    K_ATTEND, K_COMBINE, K_COUNT
 };
 const char* kKernelNames[K_COUNT] = {"upload", "compress_decide", "compress_scan", "compress_pack", "decode_prep",
-                                     "score", "select_count", "select_write", "select_final", "attend", "combine"};
+                                     "score", "select_collect", "select_emit", "attend", "combine"};
 
 struct Profiler {
     std::mutex mu;
@@ -358,7 +358,7 @@ struct DecPlan {
     int32_t G = 0, Hq = 0, spw = 0, max_T = 0;
     std::vector<int32_t> tab;    // n | segbase | tokbase | T | sblk | kblk | ablk
     int64_t n_sblk = 0, n_kblk = 0, n_ablk = 0;
-    uint64_t o_tab, o_state, o_hist, o_qp, o_qbar, o_keys, o_bcnt, o_L, o_sel, o_part, bytes;
+    uint64_t o_tab, o_state, o_hist, o_qp, o_qbar, o_keys, o_L, o_sel, o_part, bytes;
 };
 
 mkv_status plan_decode(const mkv_store* s, int32_t n_q_heads, const int32_t* T, DecPlan* P) {
@@ -380,14 +380,15 @@ mkv_status plan_decode(const mkv_store* s, int32_t n_q_heads, const int32_t* T, 
     int32_t* tsb = tT + B;
     int32_t* tkb = tsb + B + 1;
     int32_t* tab_ = tkb + B + 1;
-    int64_t sb = 0, kb = 0, ab = 0;
+    int64_t sb = 0, kb = 0, ab = 0, kpad = 0;
     for (int r = 0; r < B; ++r) {
         if (T[r] < 1) return fail(MKV_E_ARG, "T[%d] = %d must be >= 1", r, T[r]);
         const int64_t n = sh.cu[r + 1] - sh.cu[r];
         const int64_t te = std::min<int64_t>(T[r], n);
         tn[r] = (int32_t)n;
         tseg[r] = sh.segbase[r];
-        ttok[r] = (int32_t)sh.cu[r];
+        ttok[r] = (int32_t)kpad;          // keys of request r start at Hkv * (earlier contexts padded to 64)
+        kpad += cdiv(n, 64) * 64;
         tT[r] = (int32_t)te;
         tsb[r] = (int32_t)sb;
         tkb[r] = (int32_t)kb;
@@ -405,7 +406,7 @@ mkv_status plan_decode(const mkv_store* s, int32_t n_q_heads, const int32_t* T, 
     P->n_ablk = ab;
     if (sb > INT32_MAX || kb > INT32_MAX || ab > INT32_MAX) return fail(MKV_E_UNSUPPORTED, "too many workgroups");
     const uint64_t streams = (uint64_t)B * sh.Hkv;
-    const uint64_t th = (uint64_t)sh.total * sh.Hkv;
+    const uint64_t th = (uint64_t)kpad * sh.Hkv;
     uint64_t o = 0;
     P->o_tab = o; o = align_up(o + 4 * P->tab.size());
     P->o_state = o; o = align_up(o + 4 * streams * kStateWords);
@@ -413,7 +414,6 @@ mkv_status plan_decode(const mkv_store* s, int32_t n_q_heads, const int32_t* T, 
     P->o_qp = o; o = align_up(o + 4ull * B * n_q_heads * MKV_HEAD_DIM);
     P->o_qbar = o; o = align_up(o + 4 * streams * MKV_HEAD_DIM);
     P->o_keys = o; o = align_up(o + 4 * th);
-    P->o_bcnt = o; o = align_up(o + 4 * (uint64_t)std::max<int64_t>(kb, 1));
     P->o_L = o; o = align_up(o + 8 * th);
     P->o_sel = o; o = align_up(o + 4 * streams * (uint64_t)std::max<int32_t>(P->max_T, 1));
     P->o_part = o; o = align_up(o + 4ull * std::max<int64_t>(ab, 1) * P->G * (MKV_HEAD_DIM + 2));
@@ -477,7 +477,6 @@ mkv_status mkv_decode_attn(const mkv_store* s, const void* q, int32_t n_q_heads,
     a.keys = reinterpret_cast<uint32_t*>(w + P.o_keys);
     a.hist = reinterpret_cast<uint32_t*>(w + P.o_hist);
     a.state = reinterpret_cast<uint32_t*>(w + P.o_state);
-    a.bcnt = reinterpret_cast<uint32_t*>(w + P.o_bcnt);
     a.L = reinterpret_cast<uint2*>(w + P.o_L);
     a.part = reinterpret_cast<float*>(w + P.o_part);
 
@@ -490,9 +489,8 @@ mkv_status mkv_decode_attn(const mkv_store* s, const void* q, int32_t n_q_heads,
     std::memcpy(first.w, P.tab.data(), sizeof(int32_t) * first.n);
     if ((st = run(K_DEC_PREP, stream, [&] { return launch_dec_prep(a, first, stream); }))) return st;
     if ((st = run(K_SCORE, stream, [&] { return launch_score(a, (int)P.n_sblk, stream); }))) return st;
-    if ((st = run(K_SEL_COUNT, stream, [&] { return launch_sel_count(a, (int)P.n_kblk, stream); }))) return st;
-    if ((st = run(K_SEL_WRITE, stream, [&] { return launch_sel_write(a, (int)P.n_kblk, stream); }))) return st;
-    if ((st = run(K_SEL_FINAL, stream, [&] { return launch_sel_final(a, stream); }))) return st;
+    if ((st = run(K_SEL_COLLECT, stream, [&] { return launch_sel_collect(a, (int)P.n_kblk, stream); }))) return st;
+    if ((st = run(K_SEL_EMIT, stream, [&] { return launch_sel_emit(a, stream); }))) return st;
     if ((st = run(K_ATTEND, stream, [&] { return launch_attend(a, (int)P.n_ablk, stream); }))) return st;
     if ((st = run(K_COMBINE, stream, [&] { return launch_combine(a, stream); }))) return st;
     return MKV_OK;

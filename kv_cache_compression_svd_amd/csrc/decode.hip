@@ -9,13 +9,14 @@
 //            token, one coalesced 16-byte value load per lane and pass, eight passes in flight per wave, Qbar
 //            gathered from LDS); writes an order-preserving 32-bit key per token and a 4096-bin histogram of the
 //            key's top 12 bits.
-//   count    finds the histogram bin that holds the T-th largest key, then counts per 4096-key block the keys in
-//            that bin or above.
-//   write    the same keys, compacted in ascending token order (block offsets from the counts).
-//   final    one workgroup per stream resolves the exact T-th key inside the boundary bin (two more 10-bit radix
-//            levels) and emits the selected tokens in ascending order; ties go to the lower token index.
-//   attend   256 selected tokens per workgroup: exact logits of the group's query heads against the sparse keys,
-//            online softmax, weighted sum of the sparse values; emits (max, sum, partial output) per head.
+//   collect  finds the histogram bin that holds the T-th largest key (coarse then fine histogram), and appends the
+//            tokens above it and the candidates inside it to two per-stream lists.
+//   emit     one workgroup per stream resolves the exact T-th key among the candidates (two more 10-bit radix
+//            levels) and writes the selected tokens in ascending order through an LDS bitmap; ties go to the
+//            lower token index.
+//   attend   256 selected tokens per workgroup (64 per wave): exact logits of the group's query heads against the
+//            sparse keys, a softmax per wave and head, weighted sum of the sparse values; emits (max, sum, partial
+//            output) per head.
 //   combine  log-sum-exp merge of the partials, then out_h = o'_h @ B_V^T.
 #include "common.cuh"
 #include "kernels.h"
@@ -47,6 +48,12 @@ __device__ __forceinline__ float val_at(const uint32_t* vw, int k) {
     else return __uint_as_float(vw[k]);
 }
 __device__ __forceinline__ int idx_at(const uint32_t* iw, int k) { return (iw[k >> 2] >> (8 * (k & 3))) & 0xFF; }
+
+// Keys and selection lists of stream (r, g) start at a 64-token aligned offset: requests are padded to a
+// multiple of 64 tokens, so 16-byte vector loads of keys stay aligned.
+__device__ __forceinline__ int64_t key_base(const DecArgs& a, int r, int g, int n) {
+    return (int64_t)a.t_tokbase[r] * a.Hkv + (int64_t)g * ((n + 63) & ~63);
+}
 
 // =====================================================================================================
 // prep
@@ -230,7 +237,7 @@ __global__ __launch_bounds__(256) void k_score(DecArgs a) {
     const int g = local / nch, chunk = local - g * nch;
     const int stream = r * a.Hkv + g;
     const int64_t seg0 = (int64_t)a.Hkv * a.t_segbase[r] + (int64_t)g * Sr;
-    const int64_t keybase = (int64_t)a.t_tokbase[r] * a.Hkv + (int64_t)g * n;
+    const int64_t keybase = key_base(a, r, g, n);
     const int tid = threadIdx.x;
     const int s0 = chunk * a.spw, s1 = min(Sr, s0 + a.spw), nloc = s1 - s0;
     for (int i = tid; i < kHistBins; i += 256) sh[i] = 0u;
@@ -295,10 +302,17 @@ __global__ __launch_bounds__(256) void k_score(DecArgs a) {
         }
     }
     __syncthreads();
+    // flush: fine bins, and per coarse bin (64 fine bins = one wave's slice in each iteration) its total
     uint32_t* gh = a.hist + (size_t)stream * kHistBins;
-    for (int i = tid; i < kHistBins; i += 256) {
+    uint32_t* gc = a.state + stream * kStateWords + kCoarseOff;
+#pragma unroll 4
+    for (int it = 0; it < kHistBins / 256; ++it) {
+        const int i = it * 256 + tid;
         const uint32_t c = sh[i];
         if (c) atomic_add_dev(&gh[i], c);
+        uint32_t cs = c;
+        for (int m2 = 32; m2 >= 1; m2 >>= 1) cs += __shfl_xor(cs, m2, MKV_WAVE);
+        if (lane == 0 && cs) atomic_add_dev(&gc[i >> 6], cs);
     }
 }
 
@@ -310,9 +324,9 @@ hipError_t launch_score(const DecArgs& a, int n_blocks, hipStream_t s) {
 }
 
 // =====================================================================================================
-// selection passes
+// selection: collect (grid-wide) and emit (one workgroup per stream)
 // =====================================================================================================
-struct KBlock { int r, g, kb, n, stream, first_blk; int64_t keybase; };
+struct KBlock { int r, g, kb, n, stream; int64_t keybase; };
 
 __device__ __forceinline__ KBlock kblock(const DecArgs& a) {
     KBlock k;
@@ -324,101 +338,87 @@ __device__ __forceinline__ KBlock kblock(const DecArgs& a) {
     k.g = local / nkb;
     k.kb = local - k.g * nkb;
     k.stream = k.r * a.Hkv + k.g;
-    k.first_blk = b - k.kb;
-    k.keybase = (int64_t)a.t_tokbase[k.r] * a.Hkv + (int64_t)k.g * k.n;
+    k.keybase = key_base(a, k.r, k.g, k.n);
     return k;
 }
 
-// The bin of the T-th largest key in the stream's first-level histogram (complete once the score kernel has
-// finished): bins are scanned from the top, thread t owning bins [4095 - 16t - 15, 4095 - 16t].  Every block of
-// the stream computes it; block 0 records it in the stream's selection state for the later kernels.
-__device__ __forceinline__ uint32_t threshold_bin(const DecArgs& a, int stream, uint32_t T, bool record,
-                                                  uint32_t* tmp, uint32_t* s_p1) {
-    const int tid = threadIdx.x;
-    const uint32_t* gh = a.hist + (size_t)stream * kHistBins;
-    uint32_t cnt[16], loc = 0;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) { cnt[k] = gh[kHistBins - 1 - (16 * tid + k)]; loc += cnt[k]; }
-    uint32_t total;
-    const uint32_t above = block_exscan(loc, tmp, &total);
-    if (above < T && above + loc >= T) {
-        uint32_t run = above;
-#pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            if (run + cnt[k] >= T) {
-                const uint32_t p1 = (uint32_t)(kHistBins - 1 - (16 * tid + k));
-                *s_p1 = p1;
-                if (record) {
-                    uint32_t* st = a.state + stream * kStateWords;
-                    st[ST_P1] = p1;
-                    st[ST_NGT] = run;
-                    st[ST_NCAND] = cnt[k];
-                    st[ST_NEED] = T - run;
-                }
-                break;
-            }
-            run += cnt[k];
-        }
+// Inclusive prefix over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl(uint32_t v) {
+    const int lane = threadIdx.x & 63;
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_up(v, d, MKV_WAVE);
+        if (lane >= d) v += y;
     }
-    __syncthreads();
-    return *s_p1;
+    return v;
 }
 
-__global__ __launch_bounds__(256) void k_sel_count(DecArgs a) {
-    __shared__ uint32_t tmp[8];
-    __shared__ uint32_t s_p1;
-    const KBlock k = kblock(a);
-    const uint32_t p1 = threshold_bin(a, k.stream, (uint32_t)a.t_T[k.r], k.kb == 0, tmp, &s_p1);
-    const int lo = k.kb * kKeysPerBlock, cnt = min(kKeysPerBlock, k.n - lo);
-    const uint32_t* keys = a.keys + k.keybase + lo;
-    uint32_t c = 0;
-    for (int i = threadIdx.x; i < cnt; i += 256) c += ((keys[i] >> 20) >= p1) ? 1u : 0u;
-    uint32_t total;
-    block_exscan(c, tmp, &total);
-    if (threadIdx.x == 0) a.bcnt[blockIdx.x] = total;
+// Bin of the T-th largest key (first wave of the block): the 64-bin coarse histogram (top 6 key bits) gives the
+// coarse bin, its 64 fine bins (top 12 bits) the bin p1.  res <- p1, keys above p1, keys in p1, keys to take in p1.
+__device__ __forceinline__ void find_threshold(const DecArgs& a, int stream, uint32_t T, uint32_t* res) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t* st = a.state + stream * kStateWords;
+    const uint32_t cv = st[kCoarseOff + 63 - lane];
+    const uint32_t ci = wave_incl(cv), ce = ci - cv;
+    const uint64_t cb_bal = __ballot(ce < T && ci >= T);
+    const int cl = max(__ffsll((unsigned long long)cb_bal) - 1, 0);
+    const int cb = 63 - cl;
+    const uint32_t above = __shfl(ce, cl, MKV_WAVE);
+    const uint32_t fv = a.hist[(size_t)stream * kHistBins + cb * 64 + 63 - lane];
+    const uint32_t fi = wave_incl(fv) + above, fe = fi - fv;
+    if (fe < T && fi >= T) {
+        res[0] = (uint32_t)(cb * 64 + 63 - lane);
+        res[1] = fe;
+        res[2] = fv;
+        res[3] = T - fe;
+    }
 }
 
-__global__ __launch_bounds__(256) void k_sel_write(DecArgs a) {
+// For every block of 4096 keys of a stream: keys above the threshold bin go to the stream's list of taken tokens,
+// keys inside it to the candidate list (both unordered; space reserved with one device atomic per list).
+__global__ __launch_bounds__(256) void k_sel_collect(DecArgs a) {
+    __shared__ uint32_t res[4];
     __shared__ uint32_t tmp[8];
-    __shared__ uint32_t sk[kKeysPerBlock];
+    __shared__ uint32_t s_base[2];
     const KBlock k = kblock(a);
-    const uint32_t p1 = a.state[k.stream * kStateWords + ST_P1];
-    const int lo = k.kb * kKeysPerBlock, cnt = min(kKeysPerBlock, k.n - lo);
     const int tid = threadIdx.x;
-    // offset of this block: entries of the earlier blocks of the stream
-    uint32_t pre = 0;
-    for (int i = tid; i < k.kb; i += 256) pre += a.bcnt[k.first_blk + i];
-    uint32_t base;
-    block_exscan(pre, tmp, &base);
-    const uint32_t* keys = a.keys + k.keybase + lo;
-    for (int i = tid; i < cnt; i += 256) sk[i] = keys[i];
+    const uint32_t T = (uint32_t)a.t_T[k.r];
+    if (tid < 4) res[tid] = 0u;
     __syncthreads();
-    uint32_t f = 0;
+    if (tid < 64) find_threshold(a, k.stream, T, res);
+    __syncthreads();
+    const uint32_t p1 = res[0], ngt = res[1];
+    uint32_t* st = a.state + k.stream * kStateWords;
+    if (k.kb == 0 && tid < 4) st[ST_P1 + tid] = res[tid];
+    const int lo = k.kb * kKeysPerBlock + 16 * tid;
+    const u32x4* keys4 = reinterpret_cast<const u32x4*>(a.keys + k.keybase);
+    const int last4 = (((k.n + 63) & ~63) >> 2) - 1;
+    uint32_t kk[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const u32x4 v = keys4[min((lo >> 2) + q, last4)];
+        kk[4 * q] = v.x; kk[4 * q + 1] = v.y; kk[4 * q + 2] = v.z; kk[4 * q + 3] = v.w;
+    }
+    uint32_t gm = 0, cm = 0;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
-        const int i = tid * 16 + j;
-        if (i < cnt && (sk[i] >> 20) >= p1) f |= 1u << j;
+        const bool in = lo + j < k.n;
+        gm |= ((in && (kk[j] >> 20) > p1) ? 1u : 0u) << j;
+        cm |= ((in && (kk[j] >> 20) == p1) ? 1u : 0u) << j;
     }
-    uint32_t total;
-    uint32_t pos = base + block_exscan(__popc(f), tmp, &total);
+    uint32_t tot;
+    const uint32_t off = block_exscan((uint32_t)__popc(gm) | ((uint32_t)__popc(cm) << 16), tmp, &tot);
+    if (tid == 0) {
+        s_base[0] = (tot & 0xFFFFu) ? atomic_add_dev(&st[ST_GTFILL], tot & 0xFFFFu) : 0u;
+        s_base[1] = (tot >> 16) ? atomic_add_dev(&st[ST_CFILL], tot >> 16) : 0u;
+    }
+    __syncthreads();
     uint2* L = a.L + k.keybase;
+    uint32_t pg = s_base[0] + (off & 0xFFFFu), pc = ngt + s_base[1] + (off >> 16);
+#pragma unroll
     for (int j = 0; j < 16; ++j) {
-        if ((f >> j) & 1u) {
-            const int i = tid * 16 + j;
-            L[pos++] = make_uint2((uint32_t)(lo + i), sk[i]);
-        }
+        if ((gm >> j) & 1u) L[pg++] = make_uint2((uint32_t)(lo + j), kk[j]);
+        if ((cm >> j) & 1u) L[pc++] = make_uint2((uint32_t)(lo + j), kk[j]);
     }
-}
-
-hipError_t launch_sel_count(const DecArgs& a, int n_blocks, hipStream_t s) {
-    if (n_blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_sel_count, dim3(n_blocks), dim3(256), 0, s, a);
-    return hipGetLastError();
-}
-hipError_t launch_sel_write(const DecArgs& a, int n_blocks, hipStream_t s) {
-    if (n_blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_sel_write, dim3(n_blocks), dim3(256), 0, s, a);
-    return hipGetLastError();
 }
 
 // Largest bin b (of h[0..1023], one per thread) with (sum of bins >= b) >= need; returns b and the count
@@ -432,10 +432,41 @@ __device__ __forceinline__ void find_bin1024(const uint32_t* h, uint32_t need, u
     __syncthreads();
 }
 
-__global__ __launch_bounds__(1024) void k_sel_final(DecArgs a) {
+constexpr int kTileBits = 1 << 17;          // tokens per bitmap tile of the emit kernel (16 KB of LDS)
+constexpr int kTileWords = kTileBits / 32;
+
+// Tokens of one bitmap tile in ascending order: thread t owns words [4t, 4t+4); returns the tile's count.
+__device__ __forceinline__ uint32_t emit_tile(const uint32_t* bm, int tile0, uint32_t carry, int32_t* srow,
+                                              int32_t* urow, uint32_t* tmp) {
+    const int tid = threadIdx.x;
+    uint32_t w[4], c = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { w[j] = bm[4 * tid + j]; c += __popc(w[j]); }
+    uint32_t tot;
+    uint32_t pos = carry + block_exscan(c, tmp, &tot);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint32_t x = w[j];
+        while (x) {
+            const int bit = __ffs(x) - 1;
+            x &= x - 1;
+            const int32_t idx = tile0 + (4 * tid + j) * 32 + bit;
+            srow[pos] = idx;
+            if (urow) urow[pos] = idx;
+            ++pos;
+        }
+    }
+    return tot;
+}
+
+// One workgroup per stream: the exact T-th key among the candidates (two 10-bit radix levels), the cut among
+// keys equal to it (lowest token indices first), then the selected tokens in ascending order through a bitmap.
+__global__ __launch_bounds__(1024) void k_sel_emit(DecArgs a) {
+    __shared__ uint32_t bm[kTileWords];
     __shared__ uint32_t h[1024];
     __shared__ uint32_t tmp[20];
-    __shared__ uint32_t res[2];
+    __shared__ uint32_t res[4];
+    __shared__ uint32_t s_eq;
     const int stream = blockIdx.x, r = stream / a.Hkv, g = stream - r * a.Hkv;
     const int n = a.t_n[r], T = a.t_T[r];
     const int tid = threadIdx.x;
@@ -443,51 +474,86 @@ __global__ __launch_bounds__(1024) void k_sel_final(DecArgs a) {
     if (n > 0 && T > 0) {
         const uint32_t* st = a.state + stream * kStateWords;
         const uint32_t p1 = st[ST_P1], ngt = st[ST_NGT], ncand = st[ST_NCAND], need = st[ST_NEED];
-        const uint32_t m = ngt + ncand;
-        const int64_t keybase = (int64_t)a.t_tokbase[r] * a.Hkv + (int64_t)g * n;
-        const uint2* L = a.L + keybase;
+        const uint2* L = a.L + key_base(a, r, g, n);
+        const uint2* cand = L + ngt;
         const bool all = (need == ncand);
         uint32_t kstar = 0, need_eq = 0;
+        int cut = n;   // ties equal to K* are taken up to this token index
         if (!all) {
             h[tid] = 0u;
+            if (tid == 0) s_eq = 0u;
             __syncthreads();
-            for (uint32_t i = tid; i < m; i += 1024) {
-                const uint32_t key = L[i].y;
-                if ((key >> 20) == p1) atomicAdd(&h[(key >> 10) & 1023u], 1u);
-            }
+            for (uint32_t i = tid; i < ncand; i += 1024) atomicAdd(&h[(cand[i].y >> 10) & 1023u], 1u);
             __syncthreads();
             find_bin1024(h, need, tmp, res);
             const uint32_t b2 = res[0], need2 = res[1];
             const uint32_t pre22 = (p1 << 10) | b2;
             h[tid] = 0u;
             __syncthreads();
-            for (uint32_t i = tid; i < m; i += 1024) {
-                const uint32_t key = L[i].y;
+            for (uint32_t i = tid; i < ncand; i += 1024) {
+                const uint32_t key = cand[i].y;
                 if ((key >> 10) == pre22) atomicAdd(&h[key & 1023u], 1u);
             }
             __syncthreads();
             find_bin1024(h, need2, tmp, res);
             kstar = (pre22 << 10) | res[0];
             need_eq = res[1];
+            const uint32_t eq_total = h[res[0]];
+            if (need_eq < eq_total) {
+                // the need_eq-th smallest token index among the keys equal to K*: scan tie bitmaps tile by tile
+                uint32_t seen = 0;
+                cut = -1;
+                for (int t0 = 0; t0 < n && cut < 0; t0 += kTileBits) {
+                    for (int i = tid; i < kTileWords; i += 1024) bm[i] = 0u;
+                    __syncthreads();
+                    for (uint32_t i = tid; i < ncand; i += 1024) {
+                        const uint2 e = cand[i];
+                        if (e.y == kstar && (int)e.x >= t0 && (int)e.x < t0 + kTileBits)
+                            atomicOr(&bm[(e.x - t0) >> 5], 1u << ((e.x - t0) & 31));
+                    }
+                    __syncthreads();
+                    uint32_t w[4], c = 0;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) { w[j] = bm[4 * tid + j]; c += __popc(w[j]); }
+                    uint32_t tot;
+                    const uint32_t before = seen + block_exscan(c, tmp, &tot);
+                    if (before < need_eq && before + c >= need_eq) {
+                        uint32_t run = before;
+                        for (int j = 0; j < 4 && cut < 0; ++j) {
+                            uint32_t x = w[j];
+                            while (x) {
+                                const int bit = __ffs(x) - 1;
+                                x &= x - 1;
+                                if (++run == need_eq) { res[0] = (uint32_t)(t0 + (4 * tid + j) * 32 + bit); break; }
+                            }
+                            if (run == need_eq) break;
+                        }
+                    }
+                    seen += tot;
+                    __syncthreads();
+                    if (seen >= need_eq) cut = (int)res[0];
+                    __syncthreads();
+                }
+            }
         }
         int32_t* srow = a.sel_int + (size_t)stream * a.sel_int_stride;
-        uint32_t run_keep = 0, run_eq = 0;
-        for (uint32_t b0 = 0; b0 < m; b0 += 1024) {
-            const uint32_t i = b0 + tid;
-            const bool valid = i < m;
-            const uint2 e = valid ? L[i] : make_uint2(0u, 0u);
-            const bool is_gt = valid && (all || e.y > kstar);
-            const bool is_eq = valid && !all && e.y == kstar;
-            uint32_t eqt, kt;
-            const uint32_t eqx = block_exscan(is_eq ? 1u : 0u, tmp, &eqt);
-            const bool keep = is_gt || (is_eq && run_eq + eqx < need_eq);
-            const uint32_t kx = block_exscan(keep ? 1u : 0u, tmp, &kt);
-            if (keep) {
-                srow[run_keep + kx] = (int32_t)e.x;
-                if (urow) urow[run_keep + kx] = (int32_t)e.x;
+        uint32_t carry = 0;
+        for (int t0 = 0; t0 < n; t0 += kTileBits) {
+            for (int i = tid; i < kTileWords; i += 1024) bm[i] = 0u;
+            __syncthreads();
+            for (uint32_t i = tid; i < ngt; i += 1024) {
+                const uint32_t x = L[i].x;
+                if ((int)x >= t0 && (int)x < t0 + kTileBits) atomicOr(&bm[(x - t0) >> 5], 1u << ((x - t0) & 31));
             }
-            run_eq += eqt;
-            run_keep += kt;
+            for (uint32_t i = tid; i < ncand; i += 1024) {
+                const uint2 e = cand[i];
+                const bool take = all || e.y > kstar || (e.y == kstar && (int)e.x <= cut);
+                if (take && (int)e.x >= t0 && (int)e.x < t0 + kTileBits)
+                    atomicOr(&bm[(e.x - t0) >> 5], 1u << ((e.x - t0) & 31));
+            }
+            __syncthreads();
+            carry += emit_tile(bm, t0, carry, srow, urow, tmp);
+            __syncthreads();
         }
     }
     if (urow) {
@@ -496,8 +562,13 @@ __global__ __launch_bounds__(1024) void k_sel_final(DecArgs a) {
     }
 }
 
-hipError_t launch_sel_final(const DecArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(k_sel_final, dim3(a.B * a.Hkv), dim3(1024), 0, s, a);
+hipError_t launch_sel_collect(const DecArgs& a, int n_blocks, hipStream_t s) {
+    if (n_blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_sel_collect, dim3(n_blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+hipError_t launch_sel_emit(const DecArgs& a, hipStream_t s) {
+    hipLaunchKernelGGL(k_sel_emit, dim3(a.B * a.Hkv), dim3(1024), 0, s, a);
     return hipGetLastError();
 }
 
@@ -554,11 +625,11 @@ template <int BV, int G>
 __global__ __launch_bounds__(256) void k_attend(DecArgs a) {
     __shared__ __attribute__((aligned(16))) float qt[MKV_D * G];
     __shared__ __attribute__((aligned(16))) float vb[4][8][MKV_D];
-    __shared__ float pt[4][8][G];
+    __shared__ float ps[4][64][G];            // logits, then softmax numerators, of each wave's 64 tokens
     __shared__ float wm[4][G], wl[4][G];
     __shared__ float wacc[4][G][MKV_D];
     __shared__ RowMeta mk[4][64], mv[4][64];
-    __shared__ int mc[4][64];     // log2 c of K | log2 c of V << 8 | valid << 16
+    __shared__ int mc[4][64];                 // log2 c of K | log2 c of V << 8 | valid << 16
     const int b = blockIdx.x;
     const int r = find_slot(a.t_ablk, a.B, b);
     const int n = a.t_n[r], T = a.t_T[r], Sr = (n + MKV_SEG - 1) / MKV_SEG;
@@ -576,7 +647,7 @@ __global__ __launch_bounds__(256) void k_attend(DecArgs a) {
         const int32_t* list = a.sel_int + (size_t)stream * a.sel_int_stride;
         const int li = chunk * kAttnChunk + wid * 64 + lane;
         const int j = (li < T) ? list[li] : -1;
-        int word = 0;
+        int word;
         RowMeta k_{0, 0}, v_{0, 0};
         if (j >= 0) {
             const int s = j >> 6, tt = j & 63, ns = min(MKV_SEG, n - s * MKV_SEG);
@@ -598,106 +669,107 @@ __global__ __launch_bounds__(256) void k_attend(DecArgs a) {
     }
     __syncthreads();
     const float scale = 1.4426950408889634f * 0.08838834764831845f;   // log2(e) / sqrt(128)
-    float m[G], l[G], acc[G][2];
-#pragma unroll
-    for (int h = 0; h < G; ++h) { m[h] = -INFINITY; l[h] = 0.f; acc[h][0] = 0.f; acc[h][1] = 0.f; }
+    const bool wide = __builtin_amdgcn_readfirstlane(__ballot((mc[wid][lane] & 0xFF) == 7 ||
+                                                              ((mc[wid][lane] >> 8) & 0xFF) == 7) != 0);
 
-    RowBuf<BV> kb[2], vbuf[2];
-    int wd[2];
-    {
-        const int w0 = mc[wid][t8];
-        const RowMeta k0 = mk[wid][t8], v0 = mv[wid][t8];
-        load_row<BV>(kb[0], a.payload, k0.vaddr, k0.iaddr, w0 & 0xFF, sl, (w0 >> 16) & 1);
-        load_row<BV>(vbuf[0], a.payload, v0.vaddr, v0.iaddr, (w0 >> 8) & 0xFF, sl, (w0 >> 16) & 1);
-        wd[0] = w0;
-    }
-#pragma unroll 1
-    for (int pp = 0; pp < 8; pp += 2) {
+    // ---- logits of the wave's 64 tokens: 8 lanes per token, four passes of rows in flight ----
 #pragma unroll
-    for (int cur = 0; cur < 2; ++cur) {
-        const int pass = pp + cur, nxt = cur ^ 1;
-        if (pass + 1 < 8) {
-            const int tk = (pass + 1) * 8 + t8;
-            const int w1 = mc[wid][tk];
-            const RowMeta k1 = mk[wid][tk], v1 = mv[wid][tk];
-            load_row<BV>(kb[nxt], a.payload, k1.vaddr, k1.iaddr, w1 & 0xFF, sl, (w1 >> 16) & 1);
-            load_row<BV>(vbuf[nxt], a.payload, v1.vaddr, v1.iaddr, (w1 >> 8) & 0xFF, sl, (w1 >> 16) & 1);
-            wd[nxt] = w1;
+    for (int half = 0; half < 2; ++half) {
+        RowBuf<BV> kr[4];
+        int wd[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int tk = (half * 4 + q) * 8 + t8;
+            wd[q] = mc[wid][tk];
+            const RowMeta km = mk[wid][tk];
+            load_row<BV>(kr[q], a.payload, km.vaddr, km.iaddr, wd[q] & 0xFF, sl, (wd[q] >> 16) & 1);
         }
-        const int w = wd[cur];
-        const bool valid = (w >> 16) & 1;
-        const int lck = w & 0xFF, lcv = (w >> 8) & 0xFF;
-        const int nk = 1 << (lck - 3), nv = 1 << (lcv - 3);
-        float lg[G];
 #pragma unroll
-        for (int h = 0; h < G; ++h) lg[h] = 0.f;
-        const bool wide = __builtin_amdgcn_readfirstlane(__ballot(lck == 7 || lcv == 7) != 0);
+        for (int q = 0; q < 4; ++q) {
+            const int lck = wd[q] & 0xFF, nk = 1 << (lck - 3);
+            float lg[G];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            if (k < 8 || wide) {
-                const bool on = k < nk;
-                const int ch = on ? row_ch(kb[cur].ix, lck, sl, k) : 0;
-                const float x = on ? row_val<BV>(kb[cur], k) : 0.f;
-#pragma unroll
-                for (int h = 0; h < G; ++h) lg[h] = fmaf(qt[ch * G + h], x, lg[h]);
-            }
-        }
-        float sc[G], p[G];
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            lg[h] = sum8(lg[h]);
-            lg[h] = valid ? lg[h] * scale : -INFINITY;
-            float pm = lg[h];
-            pm = fmaxf(pm, __shfl_xor(pm, 8, MKV_WAVE));
-            pm = fmaxf(pm, __shfl_xor(pm, 16, MKV_WAVE));
-            pm = fmaxf(pm, __shfl_xor(pm, 32, MKV_WAVE));
-            const float nm = fmaxf(m[h], pm);
-            if (nm == -INFINITY) { sc[h] = 1.f; p[h] = 0.f; }
-            else { sc[h] = exp2f(m[h] - nm); p[h] = exp2f(lg[h] - nm); }
-            m[h] = nm;
-        }
-        float* dense = vb[wid][t8];
-        *reinterpret_cast<f32x4*>(&dense[sl * 16 + 0]) = f32x4{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<f32x4*>(&dense[sl * 16 + 4]) = f32x4{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<f32x4*>(&dense[sl * 16 + 8]) = f32x4{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<f32x4*>(&dense[sl * 16 + 12]) = f32x4{0.f, 0.f, 0.f, 0.f};
-        wave_lds_sync();
-        if (valid) {
+            for (int h = 0; h < G; ++h) lg[h] = 0.f;
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
-                if ((k < 8 || wide) && k < nv) dense[row_ch(vbuf[cur].ix, lcv, sl, k)] = row_val<BV>(vbuf[cur], k);
+                if (k < 8 || wide) {
+                    const bool on = k < nk;
+                    const int ch = on ? row_ch(kr[q].ix, lck, sl, k) : 0;
+                    const float x = on ? row_val<BV>(kr[q], k) : 0.f;
+#pragma unroll
+                    for (int h = 0; h < G; ++h) lg[h] = fmaf(qt[ch * G + h], x, lg[h]);
+                }
             }
-        }
-        if (sl == 0) {
-#pragma unroll
-            for (int h = 0; h < G; ++h) pt[wid][t8][h] = p[h];
-        }
-        wave_lds_sync();
-#pragma unroll
-        for (int h = 0; h < G; ++h) {
-            float ps = 0.f;
-#pragma unroll
-            for (int t = 0; t < 8; ++t) ps += pt[wid][t][h];
-            l[h] = l[h] * sc[h] + ps;
-            acc[h][0] *= sc[h];
-            acc[h][1] *= sc[h];
-        }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const float2 v = *reinterpret_cast<const float2*>(&vb[wid][t][2 * lane]);
+            const bool valid = (wd[q] >> 16) & 1;
 #pragma unroll
             for (int h = 0; h < G; ++h) {
-                const float pp = pt[wid][t][h];
-                acc[h][0] = fmaf(pp, v.x, acc[h][0]);
-                acc[h][1] = fmaf(pp, v.y, acc[h][1]);
+                const float v = sum8(lg[h]);
+                if (sl == 0) ps[wid][(half * 4 + q) * 8 + t8][h] = valid ? v * scale : -INFINITY;
             }
         }
-        wave_lds_sync();
     }
+    wave_lds_sync();
+
+    // ---- softmax over the wave's tokens, one lane per token ----
+    float mW[G], lW[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const float x = ps[wid][lane][h];
+        const float M = wave_max(x);
+        const float e = (M == -INFINITY) ? 0.f : exp2f(x - M);
+        mW[h] = M;
+        lW[h] = wave_sum(e);
+        ps[wid][lane][h] = e;
+    }
+    wave_lds_sync();
+
+    // ---- weighted sum of the sparse value rows; lane owns channels 2*lane, 2*lane+1 ----
+    float acc[G][2];
+#pragma unroll
+    for (int h = 0; h < G; ++h) { acc[h][0] = 0.f; acc[h][1] = 0.f; }
+    float* dense = vb[wid][t8];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        RowBuf<BV> vr[4];
+        int wd[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int tk = (half * 4 + q) * 8 + t8;
+            wd[q] = mc[wid][tk];
+            const RowMeta vm = mv[wid][tk];
+            load_row<BV>(vr[q], a.payload, vm.vaddr, vm.iaddr, (wd[q] >> 8) & 0xFF, sl, (wd[q] >> 16) & 1);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int pass = half * 4 + q;
+            *reinterpret_cast<f32x4*>(&dense[sl * 16 + 0]) = f32x4{0.f, 0.f, 0.f, 0.f};
+            *reinterpret_cast<f32x4*>(&dense[sl * 16 + 4]) = f32x4{0.f, 0.f, 0.f, 0.f};
+            *reinterpret_cast<f32x4*>(&dense[sl * 16 + 8]) = f32x4{0.f, 0.f, 0.f, 0.f};
+            *reinterpret_cast<f32x4*>(&dense[sl * 16 + 12]) = f32x4{0.f, 0.f, 0.f, 0.f};
+            wave_lds_sync();
+            if ((wd[q] >> 16) & 1) {
+                const int lcv = (wd[q] >> 8) & 0xFF, nv = 1 << (lcv - 3);
+#pragma unroll
+                for (int k = 0; k < 16; ++k)
+                    if ((k < 8 || wide) && k < nv) dense[row_ch(vr[q].ix, lcv, sl, k)] = row_val<BV>(vr[q], k);
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const float2 v = *reinterpret_cast<const float2*>(&vb[wid][t][2 * lane]);
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const float pp = ps[wid][pass * 8 + t][h];
+                    acc[h][0] = fmaf(pp, v.x, acc[h][0]);
+                    acc[h][1] = fmaf(pp, v.y, acc[h][1]);
+                }
+            }
+            wave_lds_sync();
+        }
     }
     if (lane == 0) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) { wm[wid][h] = m[h]; wl[wid][h] = l[h]; }
+        for (int h = 0; h < G; ++h) { wm[wid][h] = mW[h]; wl[wid][h] = lW[h]; }
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) { wacc[wid][h][2 * lane] = acc[h][0]; wacc[wid][h][2 * lane + 1] = acc[h][1]; }

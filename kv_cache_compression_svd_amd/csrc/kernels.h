@@ -7,12 +7,13 @@ namespace mkv {
 
 constexpr int kUploadWords = 448;       // int32 words a table upload carries in its kernel arguments
 constexpr int kHistBins = 4096;         // first radix level of the top-T select: key bits [31:20]
-constexpr int kStateWords = 16;         // per (request, KV head) selection state
+constexpr int kStateWords = 128;        // per (request, KV head) selection state and coarse histogram
+constexpr int kCoarseOff = 64;          // coarse histogram (top 6 key bits) inside the state words
 constexpr int kKeysPerBlock = 4096;     // keys per workgroup in the selection passes
 constexpr int kAttnChunk = 256;         // selected tokens per attention workgroup
 
 // selection state words
-enum { ST_P1 = 1, ST_NGT = 2, ST_NCAND = 3, ST_NEED = 4 };
+enum { ST_P1 = 1, ST_NGT = 2, ST_NCAND = 3, ST_NEED = 4, ST_GTFILL = 5, ST_CFILL = 6 };
 
 struct Upload {
     int32_t* dst;
@@ -58,7 +59,8 @@ struct DecArgs {
     int32_t sel_stride;
     int32_t* sel_int;           // internal selection lists [B*Hkv][sel_int_stride]
     int32_t sel_int_stride;
-    // per-request tables (device): n | seg_base | tok_base | T_eff | sblk_base | kblk_base | ablk_base
+    // per-request tables (device): n | seg_base | key base (sum of earlier contexts padded to 64 tokens) |
+    // T_eff | sblk_base | kblk_base | ablk_base
     const int32_t* t_n;
     const int32_t* t_segbase;
     const int32_t* t_tokbase;
@@ -69,19 +71,17 @@ struct DecArgs {
     int32_t spw;                // segments per score workgroup
     float* qp;                  // [B][Hq][128]
     float* qbar;                // [B][Hkv][128]
-    uint32_t* keys;             // [total_tokens*Hkv]
+    uint32_t* keys;             // [Hkv * sum of contexts padded to 64 tokens]
     uint32_t* hist;             // [B*Hkv][4096]
     uint32_t* state;            // [B*Hkv][16]
-    uint32_t* bcnt;             // [n_kblk]
-    uint2* L;                   // [total_tokens*Hkv] (token index, key)
+    uint2* L;                   // same indexing as keys: taken tokens, then candidates, as (token index, key)
     float* part;                // [n_ablk][G][130]
 };
 
 hipError_t launch_dec_prep(const DecArgs& a, const Upload& tab, hipStream_t s);
 hipError_t launch_score(const DecArgs& a, int n_blocks, hipStream_t s);
-hipError_t launch_sel_count(const DecArgs& a, int n_blocks, hipStream_t s);
-hipError_t launch_sel_write(const DecArgs& a, int n_blocks, hipStream_t s);
-hipError_t launch_sel_final(const DecArgs& a, hipStream_t s);
+hipError_t launch_sel_collect(const DecArgs& a, int n_blocks, hipStream_t s);
+hipError_t launch_sel_emit(const DecArgs& a, hipStream_t s);
 hipError_t launch_attend(const DecArgs& a, int n_blocks, hipStream_t s);
 hipError_t launch_combine(const DecArgs& a, hipStream_t s);
 

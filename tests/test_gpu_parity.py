@@ -243,3 +243,12 @@ def test_repeat_runs_are_bit_identical(mkv):
     o2, q2 = mkv.mkv_decode_attn(s1, q, inp.T)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(q1, q2)
+
+
+def test_long_stream_spans_several_bitmap_tiles(mkv):
+    """A 300K-token stream spans three 131072-token bitmap tiles of the selection's emit step."""
+    wl = _custom([300_000, 5_000], [5_000, 150], Hq=4, Hkv=1, seed=9)
+    inp = W.generate(wl, basis="sperm")
+    ref = oracle.compress_all(inp)
+    store, q = _compress_gpu(mkv, inp)
+    _decode_compare(mkv, inp, store, q, ref)
