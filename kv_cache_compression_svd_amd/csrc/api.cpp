@@ -171,14 +171,28 @@ StoreLayout store_layout(const Shape& sh) {
     return L;
 }
 
+// Compression work split: segments per workgroup (about 4096 workgroups over both tensors) and workgroups per
+// tensor.
+struct CmpPlan {
+    int64_t spw = 1, nblk = 0;
+};
+CmpPlan cmp_plan(const Shape& sh) {
+    CmpPlan P;
+    P.spw = std::max<int64_t>(1, std::min<int64_t>(64, (2 * sh.S) / 4096));
+    for (int r = 0; r < sh.B; ++r)
+        P.nblk += (int64_t)sh.Hkv * cdiv(cdiv(sh.cu[r + 1] - sh.cu[r], MKV_SEG_LEN), P.spw);
+    return P;
+}
+
 struct ScratchLayout {
-    uint64_t tab, thr, bytes;
+    uint64_t tab, thr, wg, bytes;
 };
 ScratchLayout scratch_layout(const Shape& sh) {
     ScratchLayout L;
     L.tab = 0;
     L.thr = align_up(sizeof(int32_t) * (4ull * sh.B + 1));
-    L.bytes = L.thr + 2ull * sh.total * sh.Hkv * 4 * sizeof(uint16_t);
+    L.wg = align_up(L.thr + 2ull * sh.total * sh.Hkv * 4 * sizeof(uint16_t));
+    L.bytes = L.wg + 2ull * std::max<int64_t>(cmp_plan(sh).nblk, 1) * sizeof(uint64_t);
     return L;
 }
 
@@ -253,8 +267,7 @@ mkv_status mkv_compress(const mkv_kv_desc* kv, const float* basis, const mkv_seg
 
     uint8_t* base = static_cast<uint8_t*>(store_buf);
     uint8_t* scr = static_cast<uint8_t*>(scratch);
-    // workgroup chunking: about 4096 workgroups over both tensors
-    const int64_t spw = std::max<int64_t>(1, std::min<int64_t>(64, (2 * sh.S) / 4096));
+    const int64_t spw = cmp_plan(sh).spw;
     std::vector<int32_t> tab(4 * sh.B + 1);
     int64_t nblk = 0;
     for (int r = 0; r < sh.B; ++r) {
@@ -292,13 +305,14 @@ mkv_status mkv_compress(const mkv_kv_desc* kv, const float* basis, const mkv_seg
     a.seg_off = reinterpret_cast<uint64_t*>(base + L.seg_off);
     a.payload = base + L.payload;
     a.thr = reinterpret_cast<uint16_t*>(scr + SL.thr);
+    a.wg_total = reinterpret_cast<uint64_t*>(scr + SL.wg);
     for (int k = 0; k < 4; ++k) a.keep[k] = k < policy->n_keep ? policy->keep[k] : 0;
     a.n_keep = policy->n_keep;
     a.frac = policy->energy_frac;
     const int dt = sh.dtype == MKV_BF16 ? 1 : 0;
     uint64_t* total = reinterpret_cast<uint64_t*>(base);
     if ((st = run(K_CMP_DECIDE, stream, [&] { return launch_cmp_decide(a, dt, stream); }))) return st;
-    if ((st = run(K_CMP_SCAN, stream, [&] { return launch_cmp_scan(a.seg_off, 2 * sh.S, total, stream); }))) return st;
+    if ((st = run(K_CMP_SCAN, stream, [&] { return launch_cmp_scan(a.wg_total, 2 * nblk, total, stream); }))) return st;
     if ((st = run(K_CMP_PACK, stream, [&] { return launch_cmp_pack(a, dt, stream); }))) return st;
     return make_handle(sh, policy, basis ? 1 : 0, store_buf, out);
 }

@@ -4,10 +4,10 @@
 //
 // Two passes over each 64-token segment tile of one (request, KV head, tensor) stream:
 //   decide: rotate (MFMA), find per-vector magnitude thresholds of the c largest channels, test the energy
-//           rule in float64, pick the segment's kept-channel count, record its payload size;
-//   scan:   exclusive scan of the segment sizes -> payload offsets;
-//   pack:   rotate again, keep the channels above each vector's threshold (ties: lower channel first), and
-//           write the segment as one contiguous block (values, then uint8 channel indices).
+//           rule in float64, pick the segment's kept-channel count; each workgroup records its payload bytes;
+//   scan:   exclusive scan of the workgroup totals -> each workgroup's payload offset;
+//   pack:   rotate again, keep the channels above each vector's threshold (ties: lower channel first), write
+//           each segment as one contiguous block (values, then uint8 channel indices) and its offset.
 // The rotation of bf16 data multiplies the bf16 tile by the fp32 basis split into three bf16 parts
 // (hi + mid + lo carries 24 significant bits), accumulating in fp32; fp32 data is rotated in float64 on the
 // vector ALUs.
@@ -217,101 +217,252 @@ __device__ __forceinline__ int segment_code(int best, bool valid, int* s_code) {
 }
 
 // =====================================================================================================
-// bf16 kernel: 256 threads; wave w rotates output channels [32w, 32w+32) of a 64x128 tile with MFMA.
+// bf16 path: 8 lanes per vector, each owning 16 channels (8 words of packed 16-bit magnitudes)
+// =====================================================================================================
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int v) { return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false); }
+__device__ __forceinline__ int sum8i(int v) {
+    v += dpp_i<0xB1>(v);
+    v += dpp_i<0x4E>(v);
+    v += dpp_i<0x141>(v);
+    return v;
+}
+__device__ __forceinline__ uint32_t max8u(uint32_t v) {
+    v = max(v, (uint32_t)dpp_i<0xB1>((int)v));
+    v = max(v, (uint32_t)dpp_i<0x4E>((int)v));
+    v = max(v, (uint32_t)dpp_i<0x141>((int)v));
+    return v;
+}
+__device__ __forceinline__ uint32_t min8u(uint32_t v) {
+    v = min(v, (uint32_t)dpp_i<0xB1>((int)v));
+    v = min(v, (uint32_t)dpp_i<0x4E>((int)v));
+    v = min(v, (uint32_t)dpp_i<0x141>((int)v));
+    return v;
+}
+__device__ __forceinline__ double sum8d(double v) {
+    v += __shfl_xor(v, 1, MKV_WAVE);
+    v += __shfl_xor(v, 2, MKV_WAVE);
+    v += __shfl_xor(v, 4, MKV_WAVE);
+    return v;
+}
+// exclusive prefix over the 8 lanes of a vector (lane order = channel order)
+__device__ __forceinline__ int excl8(int v, int p) {
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < 8; d <<= 1) {
+        const int y = __shfl_up(x, d, MKV_WAVE);
+        if (p >= d) x += y;
+    }
+    return x - v;
+}
+// count of this lane's 16 magnitudes >= cand (0 <= cand <= 0x8000)
+__device__ __forceinline__ int count_ge16(const uint32_t* w, uint32_t cand) {
+    const u16x2 cc = {(unsigned short)cand, (unsigned short)cand};
+    u16x2 acc = {0, 0};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const u16x2 m = __builtin_bit_cast(u16x2, w[j] & 0x7FFF7FFFu);
+        acc += (m - cc) >> (unsigned short)15;   // 1 where m < cand
+    }
+    return 16 - (int)(acc.x + acc.y);
+}
+
+// Largest code k the vector admits (keep[k] channels hold >= frac of its energy); thr[k] <- the magnitude of its
+// keep[k]-th largest value.  Thresholds are searched bit by bit, only over the bits where the lower end of the
+// range and the vector's largest magnitude differ; smaller counts are searched above the previous threshold.
+__device__ __forceinline__ int vector_decide8(const uint32_t* w, const CmpArgs& a, uint32_t* thr) {
+    double e = 0.0;
+    u16x2 mx2 = {0, 0}, mn2 = {0x7FFF, 0x7FFF};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const double lo = bf16_to_f32(w[j] & 0xFFFFu), hi = bf16_to_f32(w[j] >> 16);
+        e += lo * lo;
+        e += hi * hi;
+        const u16x2 m = __builtin_bit_cast(u16x2, w[j] & 0x7FFF7FFFu);
+        mx2 = __builtin_elementwise_max(mx2, m);
+        mn2 = __builtin_elementwise_min(mn2, m);
+    }
+    const double e_all = sum8d(e);
+    const double bound = __dmul_rn(a.frac, e_all);
+    const uint32_t mx = max8u(max((uint32_t)mx2.x, (uint32_t)mx2.y));
+    uint32_t lo_end = min8u(min((uint32_t)mn2.x, (uint32_t)mn2.y));
+    int best = 0;
+    for (int k = 1; k < a.n_keep; ++k) {
+        const int c = a.keep[k];
+        const uint32_t diff = lo_end ^ mx;
+        uint32_t t = mx;
+        if (diff) {
+            const int hb = 31 - __clz(diff);
+            t = mx & ~((2u << hb) - 1u);
+            for (int bit = hb; bit >= 0; --bit) {
+                const uint32_t cand = t | (1u << bit);
+                if (sum8i(count_ge16(w, cand)) >= c) t = cand;
+            }
+        }
+        double part = 0.0;
+        int gt = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const uint32_t lo = w[j] & 0xFFFFu, hi = w[j] >> 16;
+            if ((lo & 0x7FFFu) > t) { const double x = bf16_to_f32(lo); part += x * x; ++gt; }
+            if ((hi & 0x7FFFu) > t) { const double x = bf16_to_f32(hi); part += x * x; ++gt; }
+        }
+        const double tv = bf16_to_f32(t);
+        const double ec = sum8d(part) + (double)(c - sum8i(gt)) * (tv * tv);
+        thr[k] = t;
+        if (ec >= bound) best = k;
+        lo_end = t;
+    }
+    return best;
+}
+
+// This lane's kept channels of one vector into the staging block (values [ns][c] then indices [ns][c]).
+__device__ __forceinline__ void vector_pack8(const uint32_t* w, uint32_t t, int c, int v, int p, int ns, uint8_t* stg) {
+    uint32_t gtm = 0, eqm = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t lo = w[j] & 0x7FFFu, hi = (w[j] >> 16) & 0x7FFFu;
+        gtm |= (lo > t ? 1u : 0u) << (2 * j);
+        gtm |= (hi > t ? 1u : 0u) << (2 * j + 1);
+        eqm |= (lo == t ? 1u : 0u) << (2 * j);
+        eqm |= (hi == t ? 1u : 0u) << (2 * j + 1);
+    }
+    const int need = c - sum8i(__popc(gtm));
+    const int eqc = __popc(eqm);
+    const int take = min(max(need - excl8(eqc, p), 0), eqc);
+    const uint32_t keepm = gtm | lowest_bits(eqm, take);
+    int pos = excl8(__popc(keepm), p);
+    uint16_t* vals = reinterpret_cast<uint16_t*>(stg) + (size_t)v * c;
+    uint8_t* idx = stg + (size_t)ns * c * 2 + (size_t)v * c;
+    for (int j = 0; j < 16; ++j) {
+        if (!((keepm >> j) & 1u)) continue;
+        vals[pos] = (uint16_t)((j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu));
+        idx[pos] = (uint8_t)(16 * p + j);
+        ++pos;
+    }
+}
+
+// Segment code: minimum over the valid vectors of the tile (8 waves x 8 vectors).
+__device__ __forceinline__ int segment_code8(int best, bool valid, int* s_code) {
+    int v = valid ? best : 255;
+    for (int m = 32; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m, MKV_WAVE));
+    if ((threadIdx.x & 63) == 0) s_code[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int code = s_code[0];
+#pragma unroll
+    for (int w = 1; w < 8; ++w) code = min(code, s_code[w]);
+    return code;
+}
+
+// =====================================================================================================
+// bf16 kernel: 512 threads; wave w rotates output channels [16w, 16w+16) of each 64x128 tile with MFMA
+// (16x16x32 bf16, the fp32 basis split into three bf16 parts held in registers); tiles are double-buffered
+// in LDS, the next one loaded while the current one is rotated and selected.
 // =====================================================================================================
 constexpr int XS = 136;   // LDS row stride in u16 (272 B: 16-B aligned, skews banks between rows)
 
 template <bool PACK>
-__global__ __launch_bounds__(256) void k_cmp_bf16(CmpArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t xs[64 * XS];
+__global__ __launch_bounds__(512) void k_cmp_bf16(CmpArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][64 * XS];
     __shared__ __attribute__((aligned(16))) uint16_t xh[64 * XS];
     __shared__ __attribute__((aligned(16))) uint8_t stg[64 * 64 * 3];
-    __shared__ int s_code[4];
+    __shared__ int s_code[8];
 
     const Tile t = cmp_tile(a);
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wid = uni(tid >> 6);
     const uint16_t* src = reinterpret_cast<const uint16_t*>(t.X ? a.V : a.K);
     const float* Bm = a.basis ? a.basis + ((((size_t)t.r * a.Hkv + t.h) * 2 + t.X) << 14) : nullptr;
 
-    // basis fragments of this wave's 32 output channels, split into three bf16 parts
-    bf16x8 bh[2][4], bmid[2][4], blo[2][4];
+    bf16x8 bh[4], bmid[4], blo[4];
     if (Bm) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int k = 32 * ks + (lane >> 4) * 8 + i;
-                    const int col = 32 * wid + 16 * nt + (lane & 15);
-                    const float v = Bm[k * MKV_D + col];
-                    const uint32_t hb = f32_to_bf16_rne(v);
-                    const float r1 = v - bf16_to_f32(hb);
-                    const uint32_t mb = f32_to_bf16_rne(r1);
-                    const float r2 = r1 - bf16_to_f32(mb);
-                    const uint32_t lb = f32_to_bf16_rne(r2);
-                    bh[nt][ks][i] = __builtin_bit_cast(__bf16, (unsigned short)hb);
-                    bmid[nt][ks][i] = __builtin_bit_cast(__bf16, (unsigned short)mb);
-                    blo[nt][ks][i] = __builtin_bit_cast(__bf16, (unsigned short)lb);
-                }
+            for (int i = 0; i < 8; ++i) {
+                const int k = 32 * ks + (lane >> 4) * 8 + i;
+                const int col = 16 * wid + (lane & 15);
+                const float v = Bm[k * MKV_D + col];
+                const uint32_t hb = f32_to_bf16_rne(v);
+                const float r1 = v - bf16_to_f32(hb);
+                const uint32_t mb = f32_to_bf16_rne(r1);
+                const float r2 = r1 - bf16_to_f32(mb);
+                const uint32_t lb = f32_to_bf16_rne(r2);
+                bh[ks][i] = __builtin_bit_cast(__bf16, (unsigned short)hb);
+                bmid[ks][i] = __builtin_bit_cast(__bf16, (unsigned short)mb);
+                blo[ks][i] = __builtin_bit_cast(__bf16, (unsigned short)lb);
+            }
     }
-    const uint16_t* rot = Bm ? xh : xs;
+    // tile rows: thread -> row tid/8, 16 channels (32 bytes) starting at 16 * (tid % 8)
+    const int lrow = tid >> 3, lq = tid & 7;
+    u32x4 r0 = {0, 0, 0, 0}, r1 = {0, 0, 0, 0};
+    auto load_tile = [&](int s) {
+        const int ns = min(MKV_SEG, t.n - s * MKV_SEG);
+        if (lrow < ns) {
+            const int64_t tok = t.tok0 + (int64_t)s * MKV_SEG + lrow;
+            const u32x4* p = reinterpret_cast<const u32x4*>(src + ((tok * a.Hkv + t.h) << 7) + lq * 16);
+            r0 = p[0];
+            r1 = p[1];
+        } else {
+            r0 = u32x4{0, 0, 0, 0};
+            r1 = u32x4{0, 0, 0, 0};
+        }
+    };
+    auto store_tile = [&](uint16_t* X) {
+        u32x4* d = reinterpret_cast<u32x4*>(&X[lrow * XS + lq * 16]);
+        d[0] = r0;
+        d[1] = r1;
+    };
+    if (t.s0 < t.s1) {
+        load_tile(t.s0);
+        store_tile(xs[0]);
+    }
+    uint64_t wg_bytes = 0;                                  // decide: payload bytes of this workgroup
+    uint64_t wg_off = PACK ? a.wg_total[blockIdx.x] : 0;    // pack: offset of this workgroup's first segment
 
     for (int s = t.s0; s < t.s1; ++s) {
+        const int cur = (s - t.s0) & 1;
         const int ns = min(MKV_SEG, t.n - s * MKV_SEG);
         const int64_t tokS = t.tok0 + (int64_t)s * MKV_SEG;
         const int64_t gs = t.seg0 + s;
-        {   // x tile -> LDS (rows past the segment end are zero)
-            const int row = tid >> 2, q = tid & 3;
-            u32x4* dst = reinterpret_cast<u32x4*>(&xs[row * XS + q * 32]);
-            if (row < ns) {
-                const u32x4* p = reinterpret_cast<const u32x4*>(src + ((((tokS + row) * a.Hkv + t.h)) << 7) + q * 32);
-                const u32x4 v0 = p[0], v1 = p[1], v2 = p[2], v3 = p[3];
-                dst[0] = v0; dst[1] = v1; dst[2] = v2; dst[3] = v3;
-            } else {
-                const u32x4 z = {0, 0, 0, 0};
-                dst[0] = z; dst[1] = z; dst[2] = z; dst[3] = z;
-            }
-        }
         __syncthreads();
+        const bool more = s + 1 < t.s1;
+        if (more) load_tile(s + 1);
+        const uint16_t* X = xs[cur];
         if (Bm) {
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
-                f32x4 am[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, ac[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+                f32x4 am = {0, 0, 0, 0}, ac = {0, 0, 0, 0};
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
-                    const bf16x8 A = *reinterpret_cast<const bf16x8*>(&xs[(16 * mt + (lane & 15)) * XS + 32 * ks + (lane >> 4) * 8]);
-#pragma unroll
-                    for (int nt = 0; nt < 2; ++nt) {
-                        am[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bh[nt][ks], am[nt], 0, 0, 0);
-                        ac[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, blo[nt][ks], ac[nt], 0, 0, 0);
-                        ac[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bmid[nt][ks], ac[nt], 0, 0, 0);
-                    }
+                    const bf16x8 A = *reinterpret_cast<const bf16x8*>(&X[(16 * mt + (lane & 15)) * XS + 32 * ks + (lane >> 4) * 8]);
+                    am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bh[ks], am, 0, 0, 0);
+                    ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, blo[ks], ac, 0, 0, 0);
+                    ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bmid[ks], ac, 0, 0, 0);
                 }
 #pragma unroll
-                for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int row = 16 * mt + (lane >> 4) * 4 + i;
-                        const int col = 32 * wid + 16 * nt + (lane & 15);
-                        xh[row * XS + col] = (uint16_t)f32_to_bf16_rne(am[nt][i] + ac[nt][i]);
-                    }
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * mt + (lane >> 4) * 4 + i;
+                    xh[row * XS + 16 * wid + (lane & 15)] = (uint16_t)f32_to_bf16_rne(am[i] + ac[i]);
+                }
             }
             __syncthreads();
         }
-
-        const int v = tid >> 2, p = tid & 3;
+        const uint16_t* R = Bm ? xh : X;
+        const int v = tid >> 3, p = tid & 7;
         const bool valid = v < ns;
-        uint32_t w[16];
+        uint32_t w[8];
         {
-            const u32x4* rp = reinterpret_cast<const u32x4*>(&rot[v * XS + p * 32]);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) { const u32x4 x = rp[j]; w[4*j] = x.x; w[4*j+1] = x.y; w[4*j+2] = x.z; w[4*j+3] = x.w; }
+            const u32x4* rp = reinterpret_cast<const u32x4*>(&R[v * XS + p * 16]);
+            const u32x4 x0 = rp[0], x1 = rp[1];
+            w[0] = x0.x; w[1] = x0.y; w[2] = x0.z; w[3] = x0.w;
+            w[4] = x1.x; w[5] = x1.y; w[6] = x1.z; w[7] = x1.w;
         }
         if (!PACK) {
             uint32_t thr[4] = {0, 0, 0, 0};
-            const int best = vector_decide<true>(w, a, thr);
-            const int code = segment_code(best, valid, s_code);
+            const int best = vector_decide8(w, a, thr);
+            const int code = segment_code8(best, valid, s_code);
             if (valid && p == 0) {
                 uint16_t* tp = a.thr + thr_index(a, t, tokS + v);
                 for (int k = 1; k < a.n_keep; ++k) tp[k] = (uint16_t)thr[k];
@@ -319,31 +470,34 @@ __global__ __launch_bounds__(256) void k_cmp_bf16(CmpArgs a) {
             if (tid == 0) {
                 const int c = a.keep[code];
                 a.codes[gs] = (uint8_t)code;
-                a.seg_off[gs] = (uint64_t)ns * c * (2 + (c < MKV_D ? 1 : 0));
+                wg_bytes += (uint64_t)ns * c * (2 + (c < MKV_D ? 1 : 0));
             }
         } else {
             const int code = a.codes[gs];
             const int c = a.keep[code];
-            uint8_t* dst = a.payload + a.seg_off[gs];
+            uint8_t* dst = a.payload + wg_off;
+            if (tid == 0) a.seg_off[gs] = wg_off;
+            wg_off += (uint64_t)ns * c * (2 + (c < MKV_D ? 1 : 0));
             if (c == MKV_D) {
                 const int nq = ns * 16;   // 16-byte pieces of ns rows of 256 bytes
-                for (int qd = tid; qd < nq; qd += 256) {
+                for (int qd = tid; qd < nq; qd += 512) {
                     const int row = qd >> 4, col = (qd & 15) * 8;
-                    *reinterpret_cast<u32x4*>(dst + (size_t)qd * 16) = *reinterpret_cast<const u32x4*>(&rot[row * XS + col]);
+                    *reinterpret_cast<u32x4*>(dst + (size_t)qd * 16) = *reinterpret_cast<const u32x4*>(&R[row * XS + col]);
                 }
             } else {
                 if (valid) {
                     const uint32_t tt = a.thr[thr_index(a, t, tokS + v) + code];
-                    vector_pack<true>(w, tt, c, v, p, ns, stg);
+                    vector_pack8(w, tt, c, v, p, ns, stg);
                 }
                 __syncthreads();
                 const int nq = ns * c * 3 / 16;
-                for (int qd = tid; qd < nq; qd += 256)
+                for (int qd = tid; qd < nq; qd += 512)
                     *reinterpret_cast<u32x4*>(dst + (size_t)qd * 16) = *reinterpret_cast<const u32x4*>(stg + (size_t)qd * 16);
             }
         }
-        __syncthreads();
+        if (more) store_tile(xs[cur ^ 1]);
     }
+    if (!PACK && tid == 0) a.wg_total[blockIdx.x] = wg_bytes;
 }
 
 // =====================================================================================================
@@ -367,6 +521,8 @@ __global__ __launch_bounds__(256) void k_cmp_f32(CmpArgs a) {
         for (int i = tid; i < MKV_D * MKV_D; i += 256) bs[i] = Bm[i];
     const float* rot = Bm ? xh : xs;
     uint8_t* stg = reinterpret_cast<uint8_t*>(xs);   // reused after the rotation (20 KB <= 33 KB)
+    uint64_t wg_bytes = 0;                                  // decide: payload bytes of this workgroup
+    uint64_t wg_off = PACK ? a.wg_total[blockIdx.x] : 0;    // pack: offset of this workgroup's first segment
 
     for (int s = t.s0; s < t.s1; ++s) {
         const int ns = min(MKV_SEG, t.n - s * MKV_SEG);
@@ -425,12 +581,14 @@ __global__ __launch_bounds__(256) void k_cmp_f32(CmpArgs a) {
             if (tid == 0) {
                 const int c = a.keep[code];
                 a.codes[gs] = (uint8_t)code;
-                a.seg_off[gs] = (uint64_t)ns * c * (4 + (c < MKV_D ? 1 : 0));
+                wg_bytes += (uint64_t)ns * c * (4 + (c < MKV_D ? 1 : 0));
             }
         } else {
             const int code = a.codes[gs];
             const int c = a.keep[code];
-            uint8_t* dst = a.payload + a.seg_off[gs];
+            uint8_t* dst = a.payload + wg_off;
+            if (tid == 0) a.seg_off[gs] = wg_off;
+            wg_off += (uint64_t)ns * c * (4 + (c < MKV_D ? 1 : 0));
             if (c == MKV_D) {
                 const int nq = ns * 32;   // 16-byte pieces of ns rows of 512 bytes
                 for (int qd = tid; qd < nq; qd += 256) {
@@ -451,6 +609,7 @@ __global__ __launch_bounds__(256) void k_cmp_f32(CmpArgs a) {
         }
         __syncthreads();
     }
+    if (!PACK && tid == 0) a.wg_total[blockIdx.x] = wg_bytes;
 }
 
 constexpr size_t kF32Lds = (size_t)(2 * 64 * XF + MKV_D * MKV_D) * sizeof(float);
@@ -460,7 +619,7 @@ static hipError_t launch_cmp(const CmpArgs& a, int dtype, hipStream_t s) {
     const dim3 grid(2 * a.nblk), block(256);
     if (a.nblk == 0) return hipSuccess;
     if (dtype == 1) {
-        hipLaunchKernelGGL(k_cmp_bf16<PACK>, grid, block, 0, s, a);
+        hipLaunchKernelGGL(k_cmp_bf16<PACK>, grid, dim3(512), 0, s, a);
     } else {
         static bool attr_set = false;
         if (!attr_set) {
@@ -476,35 +635,37 @@ hipError_t launch_cmp_decide(const CmpArgs& a, int dtype, hipStream_t s) { retur
 hipError_t launch_cmp_pack(const CmpArgs& a, int dtype, hipStream_t s) { return launch_cmp<true>(a, dtype, s); }
 
 // =====================================================================================================
-// exclusive scan of the segment sizes (one workgroup; each thread owns a contiguous run)
+// exclusive scan of the workgroup payload totals (one workgroup, tiles of 1024)
 // =====================================================================================================
 __global__ __launch_bounds__(1024) void k_cmp_scan(uint64_t* a, int64_t n, uint64_t* total) {
     __shared__ uint64_t tmp[17];
-    const int64_t per = (n + 1023) / 1024;
-    const int64_t lo = min((int64_t)threadIdx.x * per, n), hi = min(lo + per, n);
-    uint64_t sum = 0;
-    for (int64_t i = lo; i < hi; ++i) sum += a[i];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    uint64_t x = sum;
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint64_t y = __shfl_up(x, d, MKV_WAVE);
-        if (lane >= d) x += y;
+    uint64_t carry = 0;
+    for (int64_t b0 = 0; b0 < n; b0 += 1024) {
+        const int64_t i = b0 + threadIdx.x;
+        const uint64_t v = i < n ? a[i] : 0;
+        uint64_t x = v;
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint64_t y = __shfl_up(x, d, MKV_WAVE);
+            if (lane >= d) x += y;
+        }
+        if (lane == 63) tmp[wid] = x;
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint64_t run = 0;
+            for (int w = 0; w < 16; ++w) { const uint64_t q = tmp[w]; tmp[w] = run; run += q; }
+            tmp[16] = run;
+        }
+        __syncthreads();
+        if (i < n) a[i] = carry + tmp[wid] + x - v;
+        carry += tmp[16];
+        __syncthreads();
     }
-    if (lane == 63) tmp[wid] = x;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint64_t run = 0;
-        for (int w = 0; w < 16; ++w) { const uint64_t q = tmp[w]; tmp[w] = run; run += q; }
-        tmp[16] = run;
-    }
-    __syncthreads();
-    uint64_t run = tmp[wid] + x - sum;
-    for (int64_t i = lo; i < hi; ++i) { const uint64_t v = a[i]; a[i] = run; run += v; }
-    if (threadIdx.x == 0) *total = tmp[16];
+    if (threadIdx.x == 0) *total = carry;
 }
 
-hipError_t launch_cmp_scan(uint64_t* seg_off, int64_t count, uint64_t* total, hipStream_t s) {
-    hipLaunchKernelGGL(k_cmp_scan, dim3(1), dim3(1024), 0, s, seg_off, count, total);
+hipError_t launch_cmp_scan(uint64_t* wg_total, int64_t count, uint64_t* total, hipStream_t s) {
+    hipLaunchKernelGGL(k_cmp_scan, dim3(1), dim3(1024), 0, s, wg_total, count, total);
     return hipGetLastError();
 }
 

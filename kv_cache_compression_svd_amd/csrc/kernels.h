@@ -31,9 +31,10 @@ struct CmpArgs {
     int64_t S;                  // segments per tensor
     int64_t total_tokens;
     uint8_t* codes;             // [2][S]
-    uint64_t* seg_off;          // [2][S]: segment sizes after the decide pass, byte offsets after the scan
+    uint64_t* seg_off;          // [2][S]: byte offsets of the segments in the payload (written by the pack pass)
     uint8_t* payload;
     uint16_t* thr;              // [2][total_tokens][Hkv][4] per-vector magnitude thresholds (scratch)
+    uint64_t* wg_total;         // [2*nblk] payload bytes of each workgroup's segments, then their offsets
     int32_t keep[4];
     int32_t n_keep;
     double frac;
@@ -41,7 +42,7 @@ struct CmpArgs {
 
 hipError_t launch_upload(const Upload& u, hipStream_t s);
 hipError_t launch_cmp_decide(const CmpArgs& a, int dtype, hipStream_t s);
-hipError_t launch_cmp_scan(uint64_t* seg_off, int64_t count, uint64_t* total, hipStream_t s);
+hipError_t launch_cmp_scan(uint64_t* wg_total, int64_t count, uint64_t* total, hipStream_t s);
 hipError_t launch_cmp_pack(const CmpArgs& a, int dtype, hipStream_t s);
 
 // ---- decode -------------------------------------------------------------------------------------------

@@ -59,7 +59,9 @@ def test_sizes_match_layout():
     b = align(seg_off + 16 * S)
     p = align(b + basis)
     assert sb.value == p + payload + 256    # slack after the payload
-    assert tb.value == align(4 * (4 * 2 + 1)) + 2 * 300 * 8 * 4 * 2
+    # scratch: request tables | per-vector thresholds | one payload total per compression workgroup
+    nblk = 8 * (2 + 4)                  # one segment per workgroup at this size
+    assert tb.value == align(align(4 * (4 * 2 + 1)) + 2 * 300 * 8 * 4 * 2) + 2 * nblk * 8
 
 
 @pytest.mark.parametrize("field,value,code", [
