@@ -369,8 +369,8 @@ mkv_status mkv_store_destroy(mkv_store* s) {
 namespace {
 
 struct DecPlan {
-    int32_t G = 0, Hq = 0, spw = 0, max_T = 0;
-    std::vector<int32_t> tab;    // n | segbase | tokbase | T | sblk | kblk | ablk
+    int32_t G = 0, Hq = 0, spw = 0, sgx = 0, max_T = 0;
+    std::vector<int32_t> tab;    // n | segbase | tokbase | T | kblk | ablk
     int64_t n_sblk = 0, n_kblk = 0, n_ablk = 0;
     uint64_t o_tab, o_state, o_hist, o_qp, o_qbar, o_keys, o_L, o_sel, o_part, bytes;
 };
@@ -384,17 +384,17 @@ mkv_status plan_decode(const mkv_store* s, int32_t n_q_heads, const int32_t* T, 
     if (P->G != 1 && P->G != 2 && P->G != 4 && P->G != 8) return fail(MKV_E_UNSUPPORTED, "query heads per KV head must be 1, 2, 4 or 8 (got %d)", P->G);
     P->Hq = n_q_heads;
     const int B = sh.B;
-    // segments per score workgroup: about 16K workgroups for long contexts (short tail round), 4..16
-    P->spw = (int32_t)std::max<int64_t>(4, std::min<int64_t>(16, sh.S / 16384));
-    P->tab.assign(7 * B + 3, 0);
+    // segments per score workgroup, a multiple of 4 (one segment per wave at a time): about 16K workgroups for
+    // long contexts
+    P->spw = (int32_t)(std::max<int64_t>(4, std::min<int64_t>(16, sh.S / 16384)) & ~3ll);
+    P->tab.assign(6 * B + 2, 0);
     int32_t* tn = P->tab.data();
     int32_t* tseg = tn + B;
     int32_t* ttok = tseg + B;
     int32_t* tT = ttok + B;
-    int32_t* tsb = tT + B;
-    int32_t* tkb = tsb + B + 1;
+    int32_t* tkb = tT + B;
     int32_t* tab_ = tkb + B + 1;
-    int64_t sb = 0, kb = 0, ab = 0, kpad = 0;
+    int64_t sgx = 0, kb = 0, ab = 0, kpad = 0;
     for (int r = 0; r < B; ++r) {
         if (T[r] < 1) return fail(MKV_E_ARG, "T[%d] = %d must be >= 1", r, T[r]);
         const int64_t n = sh.cu[r + 1] - sh.cu[r];
@@ -404,21 +404,20 @@ mkv_status plan_decode(const mkv_store* s, int32_t n_q_heads, const int32_t* T, 
         ttok[r] = (int32_t)kpad;          // keys of request r start at Hkv * (earlier contexts padded to 64)
         kpad += cdiv(n, 64) * 64;
         tT[r] = (int32_t)te;
-        tsb[r] = (int32_t)sb;
         tkb[r] = (int32_t)kb;
         tab_[r] = (int32_t)ab;
-        sb += (int64_t)sh.Hkv * cdiv(cdiv(n, MKV_SEG_LEN), P->spw);
+        sgx = std::max<int64_t>(sgx, cdiv(cdiv(n, MKV_SEG_LEN), P->spw));
         kb += (int64_t)sh.Hkv * cdiv(n, kKeysPerBlock);
         ab += (int64_t)sh.Hkv * cdiv(te, kAttnChunk);
         P->max_T = std::max<int32_t>(P->max_T, (int32_t)te);
     }
-    tsb[B] = (int32_t)sb;
     tkb[B] = (int32_t)kb;
     tab_[B] = (int32_t)ab;
-    P->n_sblk = sb;
+    P->sgx = (int32_t)std::max<int64_t>(sgx, 1);
+    P->n_sblk = (int64_t)P->sgx * B * sh.Hkv;
     P->n_kblk = kb;
     P->n_ablk = ab;
-    if (sb > INT32_MAX || kb > INT32_MAX || ab > INT32_MAX) return fail(MKV_E_UNSUPPORTED, "too many workgroups");
+    if (P->n_sblk > INT32_MAX || kb > INT32_MAX || ab > INT32_MAX) return fail(MKV_E_UNSUPPORTED, "too many workgroups");
     const uint64_t streams = (uint64_t)B * sh.Hkv;
     const uint64_t th = (uint64_t)kpad * sh.Hkv;
     uint64_t o = 0;
@@ -482,10 +481,10 @@ mkv_status mkv_decode_attn(const mkv_store* s, const void* q, int32_t n_q_heads,
     a.t_segbase = tb + sh.B;
     a.t_tokbase = tb + 2 * sh.B;
     a.t_T = tb + 3 * sh.B;
-    a.t_sblk = tb + 4 * sh.B;
-    a.t_kblk = tb + 5 * sh.B + 1;
-    a.t_ablk = tb + 6 * sh.B + 2;
+    a.t_kblk = tb + 4 * sh.B;
+    a.t_ablk = tb + 5 * sh.B + 1;
     a.spw = P.spw;
+    a.sgx = P.sgx;
     a.qp = reinterpret_cast<float*>(w + P.o_qp);
     a.qbar = reinterpret_cast<float*>(w + P.o_qbar);
     a.keys = reinterpret_cast<uint32_t*>(w + P.o_keys);
@@ -502,11 +501,13 @@ mkv_status mkv_decode_attn(const mkv_store* s, const void* q, int32_t n_q_heads,
     first.n = (int32_t)std::min<size_t>(kUploadWords, P.tab.size());
     std::memcpy(first.w, P.tab.data(), sizeof(int32_t) * first.n);
     if ((st = run(K_DEC_PREP, stream, [&] { return launch_dec_prep(a, first, stream); }))) return st;
+
+    const int streams = sh.B * sh.Hkv;
     if ((st = run(K_SCORE, stream, [&] { return launch_score(a, (int)P.n_sblk, stream); }))) return st;
     if ((st = run(K_SEL_COLLECT, stream, [&] { return launch_sel_collect(a, (int)P.n_kblk, stream); }))) return st;
-    if ((st = run(K_SEL_EMIT, stream, [&] { return launch_sel_emit(a, stream); }))) return st;
+    if ((st = run(K_SEL_EMIT, stream, [&] { return launch_sel_emit(a, streams, stream); }))) return st;
     if ((st = run(K_ATTEND, stream, [&] { return launch_attend(a, (int)P.n_ablk, stream); }))) return st;
-    if ((st = run(K_COMBINE, stream, [&] { return launch_combine(a, stream); }))) return st;
+    if ((st = run(K_COMBINE, stream, [&] { return launch_combine(a, streams, stream); }))) return st;
     return MKV_OK;
 }
 

@@ -116,38 +116,53 @@ hipError_t launch_dec_prep(const DecArgs& a, const Upload& tab, hipStream_t s) {
 // =====================================================================================================
 // score
 // =====================================================================================================
-// The segments of one workgroup are read as a flat sequence of passes.  In every pass each lane loads one
-// 16-byte chunk of stored values (8 bf16 or 4 fp32: VPL slots) and the matching VPL one-byte channel
-// indices, so a token with c kept channels spans LPT = c / VPL consecutive lanes and a pass covers
-// TPP = 64 / LPT tokens; the load shape is the same for every kept count.  A wave keeps kRing passes in
-// flight (their loads issued before the oldest one is consumed).
+// Work split: the segments of one stream are dealt out to its workgroups in an interleaved order, so that the
+// workgroups of a stream (which are dispatched together) sweep its payload front to back side by side rather
+// than each streaming a distant chunk of its own.  With g workgroups for a stream of S segments, local slot k
+// (k = 4*kk + w; wave w takes slots w, w+4, ...) of workgroup i holds segment 4*i + w + 4*g*kk.
+//
+// A wave reads its segments as a flat sequence of passes.  In every pass each lane loads one 16-byte chunk of
+// stored values (8 bf16 or 4 fp32: VPL slots) and the matching VPL one-byte channel indices, so a token with c
+// kept channels spans LPT = c / VPL consecutive lanes and a pass covers TPP = 64 / LPT tokens; the load shape is
+// the same for every kept count.  A wave keeps kRing passes in flight (their loads issued before the oldest one
+// is consumed).
 constexpr int kRing = 8;
 constexpr int kMaxSpw = 16;
-constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past every workgroup's range: loads return 0
+constexpr uint32_t kOutOfRange = 0x80000000u;   // buffer offset past every segment: loads return 0
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// stream segment held by local slot k of workgroup i (stride = 4 * workgroups of the stream)
+__device__ __forceinline__ int slot_segment(int i, int k, int stride) { return 4 * i + (k & 3) + stride * (k >> 2); }
+
 struct PassMeta {
     int lc;      // log2 of the kept channels of the pass's segment
-    int tbase;   // stream-local index of the pass's first token
-    int tlim;    // stream-local end of the segment's tokens (-1: no pass)
+    int tbase;   // workgroup-local index (slot * 64 + token) of the pass's first token
+    int tlim;    // workgroup-local end of the segment's tokens (-1: no pass)
 };
 
-// Walks a wave's segments (every fourth of the workgroup's) pass by pass.  All fields are wave-uniform and
-// every count is a power of two, so lanes-per-token and tokens-per-pass are shifts.
+// Walks a wave's segments (every fourth local slot) pass by pass.  All fields are wave-uniform and every count
+// is a power of two, so lanes-per-token and tokens-per-pass are shifts.  Each segment gets a buffer resource of
+// its own, sized to the segment, so that lanes past its last token read zeros.
 template <int BV>
 struct PassIter {
     static constexpr int LVPL = BV == 2 ? 3 : 2;    // log2 of values per lane per pass (16 bytes)
-    const uint32_t* s_rel;   // LDS: byte offset of each local segment from the workgroup's first one
+    const uint8_t* payload;
+    const uint64_t* s_off;   // LDS: payload offset of each local slot's segment
     const int* s_m;          // LDS: log2(kept channels) | tokens << 8
-    int k, kend, p, P, lc, ns, rel;
+    int k, kend, p, P, lc, ns;
+    __amdgpu_buffer_rsrc_t rs;
 
     __device__ __forceinline__ void load_seg() {
         const int kk = min(k, kend - 1);
         const int w = uni(s_m[kk]);
-        rel = uni((int)s_rel[kk]);
+        const uint64_t off = s_off[kk];
+        const uint32_t lo = (uint32_t)uni((int)(uint32_t)off), hi = (uint32_t)uni((int)(uint32_t)(off >> 32));
         lc = w & 0xFF;
         ns = w >> 8;
+        const int bytes = (ns << lc) * (BV + (lc < 7 ? 1 : 0));
+        rs = __builtin_amdgcn_make_buffer_rsrc((void*)(payload + (((uint64_t)hi << 32) | lo)), (short)0, bytes,
+                                               0x00020000);
         const int ltpp = 6 + LVPL - lc;              // log2 tokens per pass
         P = uni((ns + (1 << ltpp) - 1) >> ltpp);
     }
@@ -160,22 +175,20 @@ struct PassIter {
 // Issues the buffer loads of the iterator's current pass (or, past the wave's last pass, loads that the range
 // check turns into zeros without a memory access).  Lanes past the segment's last token get zeros the same way.
 template <int BV>
-__device__ __forceinline__ void issue_pass(PassIter<BV>& it, int lane, int seg_first, __amdgpu_buffer_rsrc_t rs,
-                                           u32x4& v, u32x2& ix, PassMeta& m) {
+__device__ __forceinline__ void issue_pass(PassIter<BV>& it, int lane, u32x4& v, u32x2& ix, PassMeta& m) {
     constexpr int LVPL = PassIter<BV>::LVPL, VPL = 1 << LVPL;
     const bool live = it.k < it.kend;
     const int llpt = it.lc - LVPL, ltpp = 6 - llpt;
-    const int s = seg_first + it.k;   // segment index relative to the first segment of the workgroup
     m.lc = it.lc;
-    m.tbase = s * MKV_SEG + (it.p << ltpp);
-    m.tlim = live ? s * MKV_SEG + it.ns : -1;
+    m.tbase = it.k * MKV_SEG + (it.p << ltpp);
+    m.tlim = live ? it.k * MKV_SEG + it.ns : -1;
     const bool ok = live && (it.p << ltpp) + (lane >> llpt) < it.ns;
-    const uint32_t voff = ok ? (uint32_t)(it.rel + (it.p << 10) + lane * 16) : kOutOfRange;
+    const uint32_t voff = ok ? (uint32_t)((it.p << 10) + lane * 16) : kOutOfRange;
     const uint32_t ioff = (ok && it.lc < 7)
-        ? (uint32_t)(it.rel + ((it.ns << it.lc) * BV) + (it.p << (6 + LVPL)) + lane * VPL) : kOutOfRange;
-    v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0);
-    if constexpr (VPL == 8) ix = __builtin_amdgcn_raw_buffer_load_b64(rs, ioff, 0, 0);
-    else ix.x = __builtin_amdgcn_raw_buffer_load_b32(rs, ioff, 0, 0);
+        ? (uint32_t)(((it.ns << it.lc) * BV) + (it.p << (6 + LVPL)) + lane * VPL) : kOutOfRange;
+    v = __builtin_amdgcn_raw_buffer_load_b128(it.rs, voff, 0, 0);
+    if constexpr (VPL == 8) ix = __builtin_amdgcn_raw_buffer_load_b64(it.rs, ioff, 0, 0);
+    else ix.x = __builtin_amdgcn_raw_buffer_load_b32(it.rs, ioff, 0, 0);
     if (live) it.next();
 }
 
@@ -221,52 +234,44 @@ __device__ __forceinline__ void consume_pass(const u32x4& v, const u32x2& ix, co
     if (sub == 0 && t < m.tlim) skeys[t] = score_key(acc);
 }
 
+// Grid: a.sgx workgroups per stream (the most any request needs), streams in order; workgroups past their
+// stream's count exit at once.
 template <int BV>
 __global__ __launch_bounds__(256) void k_score(DecArgs a) {
     __shared__ float sq[2 * MKV_D];             // Qbar, then a zero pad that index bytes >= 128 can never reach
     __shared__ uint32_t sh[kHistBins];
-    __shared__ uint32_t skeys[kMaxSpw * MKV_SEG];   // this workgroup's keys, written out coalesced at the end
-    __shared__ uint32_t s_rel[kMaxSpw];
+    __shared__ uint32_t skeys[kMaxSpw * MKV_SEG];   // this workgroup's keys, written out per segment at the end
+    __shared__ uint64_t s_off[kMaxSpw];
     __shared__ int s_m[kMaxSpw];
-    __shared__ uint64_t s_base;
-    __shared__ uint32_t s_span;
-    const int b = blockIdx.x;
-    const int r = find_slot(a.t_sblk, a.B, b);
-    const int n = a.t_n[r], Sr = (n + MKV_SEG - 1) / MKV_SEG, nch = (Sr + a.spw - 1) / a.spw;
-    const int local = b - a.t_sblk[r];
-    const int g = local / nch, chunk = local - g * nch;
-    const int stream = r * a.Hkv + g;
+    const int stream = uni((int)(blockIdx.x / (uint32_t)a.sgx)), i = uni((int)blockIdx.x - stream * a.sgx);
+    const int r = uni(stream / a.Hkv), g = stream - r * a.Hkv;
+    const int n = a.t_n[r], Sr = (n + MKV_SEG - 1) / MKV_SEG, gs = (Sr + a.spw - 1) / a.spw;
+    if (i >= gs) return;                        // whole workgroup, before any barrier
+    const int stride = 4 * gs;
     const int64_t seg0 = (int64_t)a.Hkv * a.t_segbase[r] + (int64_t)g * Sr;
     const int64_t keybase = key_base(a, r, g, n);
     const int tid = threadIdx.x;
-    const int s0 = chunk * a.spw, s1 = min(Sr, s0 + a.spw), nloc = s1 - s0;
-    for (int i = tid; i < kHistBins; i += 256) sh[i] = 0u;
+    int nloc = 0;                               // valid slots form a prefix of [0, spw)
+    for (int kk = 0; kk < a.spw / 4; ++kk) nloc += max(0, min(4, Sr - (4 * i + stride * kk)));
+    nloc = uni(nloc);
+    if (tid < nloc) {
+        const int sg = slot_segment(i, tid, stride);
+        const int c = a.keep[a.codes[seg0 + sg]];
+        s_off[tid] = a.seg_off[seg0 + sg];
+        s_m[tid] = (31 - __clz(c)) | (min(MKV_SEG, n - sg * MKV_SEG) << 8);
+    }
+    for (int j = tid; j < kHistBins; j += 256) sh[j] = 0u;
     if (tid < MKV_D) {
         sq[tid] = a.qbar[(size_t)stream * MKV_D + tid];
         sq[MKV_D + tid] = 0.f;
-    }
-    if (tid < nloc) {
-        const uint64_t off = a.seg_off[seg0 + s0 + tid], base = a.seg_off[seg0 + s0];
-        const int c = a.keep[a.codes[seg0 + s0 + tid]];
-        const int ns = min(MKV_SEG, n - (s0 + tid) * MKV_SEG);
-        s_rel[tid] = (uint32_t)(off - base);
-        s_m[tid] = (31 - __clz(c)) | (ns << 8);
-        if (tid == nloc - 1) {
-            s_base = base;
-            s_span = (uint32_t)(off - base) + (uint32_t)(ns * c * (BV + (c < MKV_D ? 1 : 0)));
-        }
     }
     __syncthreads();
 
     const int wid = uni(tid >> 6), lane = tid & 63;   // the wave index is uniform across the wave
     if (wid < nloc) {
-        const uint64_t base = s_base;
-        const uint32_t blo = (uint32_t)uni((int)(uint32_t)base), bhi = (uint32_t)uni((int)(uint32_t)(base >> 32));
-        const uint8_t* bp = a.payload + (((uint64_t)bhi << 32) | blo);
-        const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc((void*)bp, (short)0, uni((int)s_span), 0x00020000);
         PassIter<BV> it;
-        it.s_rel = s_rel;
+        it.payload = a.payload;
+        it.s_off = s_off;
         it.s_m = s_m;
         it.k = wid;
         it.kend = nloc;
@@ -282,22 +287,22 @@ __global__ __launch_bounds__(256) void k_score(DecArgs a) {
         u32x2 ix[kRing];
         PassMeta m[kRing];
 #pragma unroll
-        for (int k = 0; k < kRing; ++k) issue_pass<BV>(it, lane, 0, rs, v[k], ix[k], m[k]);
+        for (int k = 0; k < kRing; ++k) issue_pass<BV>(it, lane, v[k], ix[k], m[k]);
         for (int base = 0; base < np; base += kRing) {
 #pragma unroll
             for (int k = 0; k < kRing; ++k) {
                 consume_pass<BV>(v[k], ix[k], m[k], lane, sq, skeys);
-                issue_pass<BV>(it, lane, 0, rs, v[k], ix[k], m[k]);
+                issue_pass<BV>(it, lane, v[k], ix[k], m[k]);
             }
         }
     }
     __syncthreads();
-    {   // keys out (coalesced) and the workgroup histogram
-        const int ntok = min(n - s0 * MKV_SEG, nloc * MKV_SEG);
-        uint32_t* keys = a.keys + keybase + (int64_t)s0 * MKV_SEG;
-        for (int i = tid; i < ntok; i += 256) {
-            const uint32_t key = skeys[i];
-            keys[i] = key;
+    // keys out (256 contiguous bytes per segment) and the workgroup histogram
+    for (int j = tid; j < nloc * MKV_SEG; j += 256) {
+        const int tok = slot_segment(i, j >> 6, stride) * MKV_SEG + (j & 63);
+        if (tok < n) {
+            const uint32_t key = skeys[j];
+            a.keys[keybase + tok] = key;
             atomicAdd(&sh[key >> 20], 1u);
         }
     }
@@ -307,12 +312,12 @@ __global__ __launch_bounds__(256) void k_score(DecArgs a) {
     uint32_t* gc = a.state + stream * kStateWords + kCoarseOff;
 #pragma unroll 4
     for (int it = 0; it < kHistBins / 256; ++it) {
-        const int i = it * 256 + tid;
-        const uint32_t c = sh[i];
-        if (c) atomic_add_dev(&gh[i], c);
+        const int j = it * 256 + tid;
+        const uint32_t c = sh[j];
+        if (c) atomic_add_dev(&gh[j], c);
         uint32_t cs = c;
         for (int m2 = 32; m2 >= 1; m2 >>= 1) cs += __shfl_xor(cs, m2, MKV_WAVE);
-        if (lane == 0 && cs) atomic_add_dev(&gc[i >> 6], cs);
+        if (lane == 0 && cs) atomic_add_dev(&gc[j >> 6], cs);
     }
 }
 
@@ -567,8 +572,9 @@ hipError_t launch_sel_collect(const DecArgs& a, int n_blocks, hipStream_t s) {
     hipLaunchKernelGGL(k_sel_collect, dim3(n_blocks), dim3(256), 0, s, a);
     return hipGetLastError();
 }
-hipError_t launch_sel_emit(const DecArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(k_sel_emit, dim3(a.B * a.Hkv), dim3(1024), 0, s, a);
+hipError_t launch_sel_emit(const DecArgs& a, int n_streams, hipStream_t s) {
+    if (n_streams == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_sel_emit, dim3(n_streams), dim3(1024), 0, s, a);
     return hipGetLastError();
 }
 
@@ -796,6 +802,9 @@ __global__ __launch_bounds__(256) void k_attend(DecArgs a) {
     }
 }
 
+// One workgroup per stream: log-sum-exp merge of the attention chunks' partials, then out = o'·B_Vᵀ.  Wave w
+// merges query heads w, w+4, ...; lane l owns channels 2l, 2l+1 and chunk weights are broadcast from the lane
+// that computed them, so every chunk's loads are independent and issue together.
 template <int G>
 __global__ __launch_bounds__(256) void k_combine(DecArgs a) {
     __shared__ float o[G][MKV_D];
@@ -804,37 +813,64 @@ __global__ __launch_bounds__(256) void k_combine(DecArgs a) {
     const int n = a.t_n[r], T = (n > 0) ? a.t_T[r] : 0;
     const int nach = (T + kAttnChunk - 1) / kAttnChunk;
     const int first = a.t_ablk[r] + g * nach;
-    const int tid = threadIdx.x, Hq = a.G * a.Hkv;
-    for (int i = tid; i < G * MKV_D; i += 256) {
-        const int h = i >> 7, ch = i & 127;
+    const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int Hq = a.G * a.Hkv;
+    const float* Bv = a.basis ? a.basis + ((((size_t)r * a.Hkv + g) * 2 + 1) << 14) : nullptr;
+    f32x4 bvr[16];
+    if (Bv) {   // issue the basis loads first: their latency overlaps the merge
+        const f32x4* src = reinterpret_cast<const f32x4*>(Bv);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) bvr[j] = src[tid + 256 * j];
+    }
+    constexpr int PW = MKV_D + 2;
+    for (int h = wid; h < G; h += 4) {
         float M = -INFINITY;
-#pragma unroll 8
-        for (int c = 0; c < nach; ++c) M = fmaxf(M, a.part[((size_t)(first + c) * G + h) * (MKV_D + 2)]);
-        float O = 0.f, Ls = 0.f;
+        for (int c = lane; c < nach; c += 64) M = fmaxf(M, a.part[((size_t)(first + c) * G + h) * PW]);
+        M = wave_max(M);
+        float O0 = 0.f, O1 = 0.f, Ls = 0.f;
         if (M != -INFINITY) {
-#pragma unroll 8
-            for (int c = 0; c < nach; ++c) {
-                const float* pp = a.part + ((size_t)(first + c) * G + h) * (MKV_D + 2);
-                if (pp[0] != -INFINITY) {
-                    const float f = exp2f(pp[0] - M);
-                    O = fmaf(pp[2 + ch], f, O);
-                    Ls = fmaf(pp[1], f, Ls);
+            for (int c0 = 0; c0 < nach; c0 += 64) {
+                const int c = c0 + lane;
+                float f = 0.f, l = 0.f;
+                if (c < nach) {
+                    const float* pp = a.part + ((size_t)(first + c) * G + h) * PW;
+                    const float m = pp[0];
+                    f = (m == -INFINITY) ? 0.f : exp2f(m - M);
+                    l = pp[1];
+                }
+                Ls += f * l;
+                const int cnt = min(64, nach - c0);
+                int k = 0;
+                for (; k + 8 <= cnt; k += 8) {
+                    float2 v[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        v[u] = *reinterpret_cast<const float2*>(a.part + ((size_t)(first + c0 + k + u) * G + h) * PW + 2 + 2 * lane);
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const float fk = __shfl(f, k + u, MKV_WAVE);
+                        O0 = fmaf(fk, v[u].x, O0);
+                        O1 = fmaf(fk, v[u].y, O1);
+                    }
+                }
+                for (; k < cnt; ++k) {
+                    const float2 v = *reinterpret_cast<const float2*>(a.part + ((size_t)(first + c0 + k) * G + h) * PW + 2 + 2 * lane);
+                    const float fk = __shfl(f, k, MKV_WAVE);
+                    O0 = fmaf(fk, v.x, O0);
+                    O1 = fmaf(fk, v.y, O1);
                 }
             }
+            Ls = wave_sum(Ls);
         }
-        o[h][ch] = (Ls > 0.f) ? O / Ls : 0.f;
+        o[h][2 * lane] = (Ls > 0.f) ? O0 / Ls : 0.f;
+        o[h][2 * lane + 1] = (Ls > 0.f) ? O1 / Ls : 0.f;
     }
-    const float* Bv = a.basis ? a.basis + ((((size_t)r * a.Hkv + g) * 2 + 1) << 14) : nullptr;
     if (Bv) {
-        const f32x4* src = reinterpret_cast<const f32x4*>(Bv);
-        f32x4 v[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = src[tid + 256 * j];
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const int e = 4 * (tid + 256 * j), row = e >> 7, col = e & 127;
             float* d = &bsh[row * (MKV_D + 1) + col];
-            d[0] = v[j].x; d[1] = v[j].y; d[2] = v[j].z; d[3] = v[j].w;
+            d[0] = bvr[j].x; d[1] = bvr[j].y; d[2] = bvr[j].z; d[3] = bvr[j].w;
         }
     }
     __syncthreads();
@@ -843,6 +879,7 @@ __global__ __launch_bounds__(256) void k_combine(DecArgs a) {
         float v;
         if (Bv) {
             v = 0.f;
+#pragma unroll 8
             for (int k = 0; k < MKV_D; ++k) v = fmaf(o[h][k], bsh[row * (MKV_D + 1) + k], v);
         } else {
             v = o[h][row];
@@ -868,8 +905,9 @@ hipError_t launch_attend(const DecArgs& a, int n_blocks, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_combine(const DecArgs& a, hipStream_t s) {
-    const dim3 grid(a.B * a.Hkv), block(256);
+hipError_t launch_combine(const DecArgs& a, int n_streams, hipStream_t s) {
+    if (n_streams == 0) return hipSuccess;
+    const dim3 grid(n_streams), block(256);
     switch (a.G) {
         case 1: hipLaunchKernelGGL(k_combine<1>, grid, block, 0, s, a); break;
         case 2: hipLaunchKernelGGL(k_combine<2>, grid, block, 0, s, a); break;

@@ -61,15 +61,15 @@ struct DecArgs {
     int32_t* sel_int;           // internal selection lists [B*Hkv][sel_int_stride]
     int32_t sel_int_stride;
     // per-request tables (device): n | seg_base | key base (sum of earlier contexts padded to 64 tokens) |
-    // T_eff | sblk_base | kblk_base | ablk_base
+    // T_eff | kblk_base | ablk_base
     const int32_t* t_n;
     const int32_t* t_segbase;
     const int32_t* t_tokbase;
     const int32_t* t_T;
-    const int32_t* t_sblk;
     const int32_t* t_kblk;
     const int32_t* t_ablk;
-    int32_t spw;                // segments per score workgroup
+    int32_t spw;                // segments per score workgroup (a multiple of 4)
+    int32_t sgx;                // score workgroups per stream in the grid (the most any request needs)
     float* qp;                  // [B][Hq][128]
     float* qbar;                // [B][Hkv][128]
     uint32_t* keys;             // [Hkv * sum of contexts padded to 64 tokens]
@@ -82,8 +82,8 @@ struct DecArgs {
 hipError_t launch_dec_prep(const DecArgs& a, const Upload& tab, hipStream_t s);
 hipError_t launch_score(const DecArgs& a, int n_blocks, hipStream_t s);
 hipError_t launch_sel_collect(const DecArgs& a, int n_blocks, hipStream_t s);
-hipError_t launch_sel_emit(const DecArgs& a, hipStream_t s);
+hipError_t launch_sel_emit(const DecArgs& a, int n_streams, hipStream_t s);
 hipError_t launch_attend(const DecArgs& a, int n_blocks, hipStream_t s);
-hipError_t launch_combine(const DecArgs& a, hipStream_t s);
+hipError_t launch_combine(const DecArgs& a, int n_streams, hipStream_t s);
 
 }  // namespace mkv
