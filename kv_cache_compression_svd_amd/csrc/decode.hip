@@ -239,7 +239,8 @@ __device__ __forceinline__ void consume_pass(const u32x4& v, const u32x2& ix, co
 template <int BV>
 __global__ __launch_bounds__(256) void k_score(DecArgs a) {
     __shared__ float sq[2 * MKV_D];             // Qbar, then a zero pad that index bytes >= 128 can never reach
-    __shared__ uint32_t sh[kHistBins];
+    __shared__ __attribute__((aligned(16))) uint32_t sh[kHistBins];
+    __shared__ uint32_t shc[64];                    // coarse bins (top 6 key bits)
     __shared__ uint32_t skeys[kMaxSpw * MKV_SEG];   // this workgroup's keys, written out per segment at the end
     __shared__ uint64_t s_off[kMaxSpw];
     __shared__ int s_m[kMaxSpw];
@@ -260,7 +261,8 @@ __global__ __launch_bounds__(256) void k_score(DecArgs a) {
         s_off[tid] = a.seg_off[seg0 + sg];
         s_m[tid] = (31 - __clz(c)) | (min(MKV_SEG, n - sg * MKV_SEG) << 8);
     }
-    for (int j = tid; j < kHistBins; j += 256) sh[j] = 0u;
+    for (int j = tid; j < kHistBins / 4; j += 256) reinterpret_cast<u32x4*>(sh)[j] = u32x4{0u, 0u, 0u, 0u};
+    if (tid < 64) shc[tid] = 0u;
     if (tid < MKV_D) {
         sq[tid] = a.qbar[(size_t)stream * MKV_D + tid];
         sq[MKV_D + tid] = 0.f;
@@ -304,20 +306,20 @@ __global__ __launch_bounds__(256) void k_score(DecArgs a) {
             const uint32_t key = skeys[j];
             a.keys[keybase + tok] = key;
             atomicAdd(&sh[key >> 20], 1u);
+            atomicAdd(&shc[key >> 26], 1u);
         }
     }
     __syncthreads();
-    // flush: fine bins, and per coarse bin (64 fine bins = one wave's slice in each iteration) its total
+    // flush the non-empty fine and coarse bins
     uint32_t* gh = a.hist + (size_t)stream * kHistBins;
-    uint32_t* gc = a.state + stream * kStateWords + kCoarseOff;
 #pragma unroll 4
-    for (int it = 0; it < kHistBins / 256; ++it) {
-        const int j = it * 256 + tid;
+    for (int j = tid; j < kHistBins; j += 256) {
         const uint32_t c = sh[j];
         if (c) atomic_add_dev(&gh[j], c);
-        uint32_t cs = c;
-        for (int m2 = 32; m2 >= 1; m2 >>= 1) cs += __shfl_xor(cs, m2, MKV_WAVE);
-        if (lane == 0 && cs) atomic_add_dev(&gc[j >> 6], cs);
+    }
+    if (tid < 64) {
+        const uint32_t c = shc[tid];
+        if (c) atomic_add_dev(&a.state[stream * kStateWords + kCoarseOff + tid], c);
     }
 }
 
@@ -581,13 +583,13 @@ hipError_t launch_sel_emit(const DecArgs& a, int n_streams, hipStream_t s) {
 // =====================================================================================================
 // sparse exact attention over the selected tokens
 // =====================================================================================================
-// One selected token's row, as seen by the 8 lanes of its group: each lane owns c/8 consecutive slots.  The
-// lane loads a fixed shape whatever c is (16 slots of values, 8 index bytes from a 4-byte aligned address);
-// bytes past its slots are ignored, and the store keeps slack after the payload for these over-reads.
-template <int BV>
+// One selected token's row, as seen by the 8 lanes of its group: each lane owns c/8 consecutive slots.  A wave
+// loads one shape for all its tokens, sized by the largest kept count among them (LW value words per lane,
+// enough for that count), plus 8 index bytes from a 4-byte aligned address.  Bytes past a lane's own slots
+// are ignored; the store keeps slack after the payload for these over-reads.
+template <int LW>
 struct RowBuf {
-    static constexpr int VW = 16 * BV / 4;   // value words per lane (16 slots)
-    uint32_t v[VW];
+    uint32_t v[LW];
     uint32_t ix[2];
 };
 
@@ -596,17 +598,22 @@ struct RowMeta {
     uint64_t iaddr;   // first index byte of the token's row (unused when c == 128)
 };
 
-template <int BV>
-__device__ __forceinline__ void load_row(RowBuf<BV>& rb, const uint8_t* payload, uint64_t vrow, uint64_t irow, int lc,
-                                         int sl, bool ok) {
+template <int BV, int LW>
+__device__ __forceinline__ void load_row(RowBuf<LW>& rb, const uint8_t* payload, const RowMeta& rm, int lc, int sl,
+                                         bool ok) {
     const int nsl_shift = lc - 3;                       // log2 of slots per lane
-    const uint8_t* va = ok ? payload + vrow + (size_t)(sl << nsl_shift) * BV : payload;
-    const uint64_t ib = irow + (uint64_t)(sl << nsl_shift);
+    const uint8_t* va = ok ? payload + rm.vaddr + (size_t)(sl << nsl_shift) * BV : payload;
+    const uint64_t ib = rm.iaddr + (uint64_t)(sl << nsl_shift);
     const uint8_t* ia = ok ? payload + (ib & ~3ull) : payload;
+    if constexpr (LW >= 4) {
 #pragma unroll
-    for (int j = 0; j < RowBuf<BV>::VW / 4; ++j) {
-        const u32x4 x = reinterpret_cast<const u32x4*>(va)[j];
-        rb.v[4 * j] = x.x; rb.v[4 * j + 1] = x.y; rb.v[4 * j + 2] = x.z; rb.v[4 * j + 3] = x.w;
+        for (int j = 0; j < LW / 4; ++j) {
+            const u32x4 x = reinterpret_cast<const u32x4*>(va)[j];
+            rb.v[4 * j] = x.x; rb.v[4 * j + 1] = x.y; rb.v[4 * j + 2] = x.z; rb.v[4 * j + 3] = x.w;
+        }
+    } else {
+        const u32x2 x = *reinterpret_cast<const u32x2*>(va);
+        rb.v[0] = x.x; rb.v[1] = x.y;
     }
     const u32x2 y = *reinterpret_cast<const u32x2*>(ia);
     const int sh = ok ? (int)(ib & 3) * 8 : 0;
@@ -615,8 +622,8 @@ __device__ __forceinline__ void load_row(RowBuf<BV>& rb, const uint8_t* payload,
     rb.ix[1] = sh ? (y.y >> sh) : y.y;
 }
 
-template <int BV>
-__device__ __forceinline__ float row_val(const RowBuf<BV>& rb, int k) {
+template <int BV, int LW>
+__device__ __forceinline__ float row_val(const RowBuf<LW>& rb, int k) {
     if constexpr (BV == 2) return (k & 1) ? __uint_as_float(rb.v[k >> 1] & 0xFFFF0000u) : __uint_as_float(rb.v[k >> 1] << 16);
     else return __uint_as_float(rb.v[k]);
 }
@@ -627,15 +634,172 @@ __device__ __forceinline__ int row_ch(const uint32_t* ix, int lc, int sl, int k)
     return (ix[k >> 2] >> (8 * (k & 3))) & 0xFF;
 }
 
+constexpr int kDenseRow = MKV_D + 4;   // dense value row: 128 channels, a dummy column, 16-byte aligned rows
+
+// G consecutive floats of the channel-major query table (one LDS read for G = 2, 4; two for G = 8)
+template <int G>
+__device__ __forceinline__ void load_q(const float* qt, int ch, float (&q)[G]) {
+    if constexpr (G == 1) {
+        q[0] = qt[ch];
+    } else if constexpr (G == 2) {
+        const float2 x = *reinterpret_cast<const float2*>(qt + ch * 2);
+        q[0] = x.x; q[1] = x.y;
+    } else {
+#pragma unroll
+        for (int j = 0; j < G / 4; ++j) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(qt + ch * G + 4 * j);
+            q[4 * j] = x.x; q[4 * j + 1] = x.y; q[4 * j + 2] = x.z; q[4 * j + 3] = x.w;
+        }
+    }
+}
+
+// Zero the value words of this lane past its nk slots (narrow shapes, where every token's slots are indexed).
+template <int BV, int LW>
+__device__ __forceinline__ void mask_tail(RowBuf<LW>& rb, int nk) {
+    constexpr int SPW = 4 / BV;   // slots per word
+#pragma unroll
+    for (int j = 1; j < LW; ++j) rb.v[j] = (j * SPW < nk) ? rb.v[j] : 0u;
+}
+
+// LDS of one attention workgroup (4 waves of 64 tokens)
+template <int G>
+struct AttnLds {
+    float qt[MKV_D * G];          // rotated queries, channel-major
+    float vb[4][8][kDenseRow];    // each wave's dense value rows of one pass (column 128: unused slots)
+    float ps[4][64][G];           // logits, then softmax numerators, of each wave's 64 tokens
+    float wm[4][G], wl[4][G];
+    float wacc[4][G][MKV_D];
+    RowMeta mk[4][64], mv[4][64];
+    int mc[4][64];                // log2 c of K | log2 c of V << 8 | valid << 16
+};
+
+// One wave's 64 tokens: logits, softmax and the weighted value sum.  LW value words per lane cover the wave's
+// largest kept count; NF passes (of 8 tokens) are in flight at a time, and the first value passes are issued
+// before the softmax so that their latency overlaps it.
+template <int BV, int G, int LW>
+__device__ __forceinline__ void attend_wave(AttnLds<G>& L, const uint8_t* payload, int wid, int lane, float (&acc)[G][2],
+                                            float (&mW)[G], float (&lW)[G]) {
+    constexpr int SLOTS = LW * 4 / BV;                       // value slots a lane holds
+    constexpr int NF = LW <= 4 ? 4 : 2;                     // passes in flight (within 128 VGPRs at G = 4)
+    constexpr bool NARROW = LW == 2 * BV;                   // kept counts <= 64: every slot is indexed
+    const int t8 = lane >> 3, sl = lane & 7;
+    const float scale = 1.4426950408889634f * 0.08838834764831845f;   // log2(e) / sqrt(128)
+
+#pragma unroll
+    for (int grp = 0; grp < 8 / NF; ++grp) {
+        RowBuf<LW> kr[NF];
+        int wd[NF];
+#pragma unroll
+        for (int q = 0; q < NF; ++q) {
+            const int tk = (grp * NF + q) * 8 + t8;
+            wd[q] = L.mc[wid][tk];
+            load_row<BV, LW>(kr[q], payload, L.mk[wid][tk], wd[q] & 0xFF, sl, (wd[q] >> 16) & 1);
+        }
+#pragma unroll
+        for (int q = 0; q < NF; ++q) {
+            const int lck = wd[q] & 0xFF, nk = 1 << (lck - 3);
+            float lg[G];
+#pragma unroll
+            for (int h = 0; h < G; ++h) lg[h] = 0.f;
+            if constexpr (NARROW) {
+                // slots past nk hold zeros; their index bytes may be anything, so take 7 bits (a valid channel)
+                mask_tail<BV, LW>(kr[q], nk);
+#pragma unroll
+                for (int k = 0; k < SLOTS; ++k) {
+                    const int ch = (int)__builtin_amdgcn_ubfe(kr[q].ix[k >> 2], 8 * (k & 3), 7);
+                    const float x = row_val<BV, LW>(kr[q], k);
+                    float qq[G];
+                    load_q<G>(L.qt, ch, qq);
+#pragma unroll
+                    for (int h = 0; h < G; ++h) lg[h] = fmaf(qq[h], x, lg[h]);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < SLOTS; ++k) {
+                    const bool on = k < nk;
+                    const int ch = on ? row_ch(kr[q].ix, lck, sl, k) : 0;
+                    const float x = on ? row_val<BV, LW>(kr[q], k) : 0.f;
+                    float qq[G];
+                    load_q<G>(L.qt, ch, qq);
+#pragma unroll
+                    for (int h = 0; h < G; ++h) lg[h] = fmaf(qq[h], x, lg[h]);
+                }
+            }
+            const bool valid = (wd[q] >> 16) & 1;
+#pragma unroll
+            for (int h = 0; h < G; ++h) {
+                const float v = sum8(lg[h]);
+                if (sl == 0) L.ps[wid][(grp * NF + q) * 8 + t8][h] = valid ? v * scale : -INFINITY;
+            }
+        }
+    }
+
+    RowBuf<LW> vr[NF];
+    int wv[NF];
+    auto issue_v = [&](int grp) {
+#pragma unroll
+        for (int q = 0; q < NF; ++q) {
+            const int tk = (grp * NF + q) * 8 + t8;
+            wv[q] = L.mc[wid][tk];
+            load_row<BV, LW>(vr[q], payload, L.mv[wid][tk], (wv[q] >> 8) & 0xFF, sl, (wv[q] >> 16) & 1);
+        }
+    };
+    issue_v(0);
+    wave_lds_sync();
+
+    // ---- softmax over the wave's tokens, one lane per token ----
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        const float x = L.ps[wid][lane][h];
+        const float M = wave_max(x);
+        const float e = (M == -INFINITY) ? 0.f : exp2f(x - M);
+        mW[h] = M;
+        lW[h] = wave_sum(e);
+        L.ps[wid][lane][h] = e;
+    }
+    wave_lds_sync();
+
+    // ---- weighted sum of the sparse value rows; lane owns channels 2*lane, 2*lane+1 ----
+    float* dense = L.vb[wid][t8];
+#pragma unroll
+    for (int grp = 0; grp < 8 / NF; ++grp) {
+        if (grp > 0) issue_v(grp);
+#pragma unroll
+        for (int q = 0; q < NF; ++q) {
+            const int pass = grp * NF + q;
+#pragma unroll
+            for (int j = 0; j < MKV_D / 8; j += 4)
+                *reinterpret_cast<f32x4*>(&dense[sl * 16 + j]) = f32x4{0.f, 0.f, 0.f, 0.f};
+            wave_lds_sync();
+            {
+                const bool valid = (wv[q] >> 16) & 1;
+                const int lcv = (wv[q] >> 8) & 0xFF, nv = valid ? 1 << (lcv - 3) : 0;
+                // every slot writes; unused ones (and invalid tokens) go to the dummy column
+#pragma unroll
+                for (int k = 0; k < SLOTS; ++k) {
+                    const int ch = k < nv ? row_ch(vr[q].ix, lcv, sl, k) : MKV_D;
+                    dense[ch] = row_val<BV, LW>(vr[q], k);
+                }
+            }
+            wave_lds_sync();
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const float2 v = *reinterpret_cast<const float2*>(&L.vb[wid][t][2 * lane]);
+#pragma unroll
+                for (int h = 0; h < G; ++h) {
+                    const float pp = L.ps[wid][pass * 8 + t][h];
+                    acc[h][0] = fmaf(pp, v.x, acc[h][0]);
+                    acc[h][1] = fmaf(pp, v.y, acc[h][1]);
+                }
+            }
+            wave_lds_sync();
+        }
+    }
+}
+
 template <int BV, int G>
 __global__ __launch_bounds__(256) void k_attend(DecArgs a) {
-    __shared__ __attribute__((aligned(16))) float qt[MKV_D * G];
-    __shared__ __attribute__((aligned(16))) float vb[4][8][MKV_D];
-    __shared__ float ps[4][64][G];            // logits, then softmax numerators, of each wave's 64 tokens
-    __shared__ float wm[4][G], wl[4][G];
-    __shared__ float wacc[4][G][MKV_D];
-    __shared__ RowMeta mk[4][64], mv[4][64];
-    __shared__ int mc[4][64];                 // log2 c of K | log2 c of V << 8 | valid << 16
+    __shared__ __attribute__((aligned(16))) AttnLds<G> L;
     const int b = blockIdx.x;
     const int r = find_slot(a.t_ablk, a.B, b);
     const int n = a.t_n[r], T = a.t_T[r], Sr = (n + MKV_SEG - 1) / MKV_SEG;
@@ -644,11 +808,11 @@ __global__ __launch_bounds__(256) void k_attend(DecArgs a) {
     const int g = local / nach, chunk = local - g * nach;
     const int stream = r * a.Hkv + g, Hq = a.G * a.Hkv;
     const int tid = threadIdx.x, wid = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int t8 = lane >> 3, sl = lane & 7;
     for (int i = tid; i < MKV_D * G; i += 256) {
         const int h = i >> 7, ch = i & 127;
-        qt[ch * G + h] = a.qp[((size_t)r * Hq + g * G + h) * MKV_D + ch];
+        L.qt[ch * G + h] = a.qp[((size_t)r * Hq + g * G + h) * MKV_D + ch];
     }
+    int lcmax;
     {   // this lane's token: list entry, segments, row addresses
         const int32_t* list = a.sel_int + (size_t)stream * a.sel_int_stride;
         const int li = chunk * kAttnChunk + wid * 64 + lane;
@@ -666,133 +830,45 @@ __global__ __launch_bounds__(256) void k_attend(DecArgs a) {
             v_.vaddr = ov + ((uint64_t)tt << lcv) * BV;
             v_.iaddr = ov + ((uint64_t)ns << lcv) * BV + ((uint64_t)tt << lcv);
             word = lck | (lcv << 8) | (1 << 16);
+            lcmax = max(lck, lcv);
         } else {
-            word = 7 | (7 << 8);
+            word = 3 | (3 << 8);
+            lcmax = 3;
         }
-        mk[wid][lane] = k_;
-        mv[wid][lane] = v_;
-        mc[wid][lane] = word;
+        L.mk[wid][lane] = k_;
+        L.mv[wid][lane] = v_;
+        L.mc[wid][lane] = word;
     }
+    const bool wide = __ballot(lcmax == 7) != 0;   // some token of the wave keeps all 128 channels
     __syncthreads();
-    const float scale = 1.4426950408889634f * 0.08838834764831845f;   // log2(e) / sqrt(128)
-    const bool wide = __builtin_amdgcn_readfirstlane(__ballot((mc[wid][lane] & 0xFF) == 7 ||
-                                                              ((mc[wid][lane] >> 8) & 0xFF) == 7) != 0);
 
-    // ---- logits of the wave's 64 tokens: 8 lanes per token, four passes of rows in flight ----
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        RowBuf<BV> kr[4];
-        int wd[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int tk = (half * 4 + q) * 8 + t8;
-            wd[q] = mc[wid][tk];
-            const RowMeta km = mk[wid][tk];
-            load_row<BV>(kr[q], a.payload, km.vaddr, km.iaddr, wd[q] & 0xFF, sl, (wd[q] >> 16) & 1);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int lck = wd[q] & 0xFF, nk = 1 << (lck - 3);
-            float lg[G];
-#pragma unroll
-            for (int h = 0; h < G; ++h) lg[h] = 0.f;
-#pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                if (k < 8 || wide) {
-                    const bool on = k < nk;
-                    const int ch = on ? row_ch(kr[q].ix, lck, sl, k) : 0;
-                    const float x = on ? row_val<BV>(kr[q], k) : 0.f;
-#pragma unroll
-                    for (int h = 0; h < G; ++h) lg[h] = fmaf(qt[ch * G + h], x, lg[h]);
-                }
-            }
-            const bool valid = (wd[q] >> 16) & 1;
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float v = sum8(lg[h]);
-                if (sl == 0) ps[wid][(half * 4 + q) * 8 + t8][h] = valid ? v * scale : -INFINITY;
-            }
-        }
-    }
-    wave_lds_sync();
-
-    // ---- softmax over the wave's tokens, one lane per token ----
-    float mW[G], lW[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        const float x = ps[wid][lane][h];
-        const float M = wave_max(x);
-        const float e = (M == -INFINITY) ? 0.f : exp2f(x - M);
-        mW[h] = M;
-        lW[h] = wave_sum(e);
-        ps[wid][lane][h] = e;
-    }
-    wave_lds_sync();
-
-    // ---- weighted sum of the sparse value rows; lane owns channels 2*lane, 2*lane+1 ----
-    float acc[G][2];
+    float acc[G][2], mW[G], lW[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) { acc[h][0] = 0.f; acc[h][1] = 0.f; }
-    float* dense = vb[wid][t8];
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        RowBuf<BV> vr[4];
-        int wd[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int tk = (half * 4 + q) * 8 + t8;
-            wd[q] = mc[wid][tk];
-            const RowMeta vm = mv[wid][tk];
-            load_row<BV>(vr[q], a.payload, vm.vaddr, vm.iaddr, (wd[q] >> 8) & 0xFF, sl, (wd[q] >> 16) & 1);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int pass = half * 4 + q;
-            *reinterpret_cast<f32x4*>(&dense[sl * 16 + 0]) = f32x4{0.f, 0.f, 0.f, 0.f};
-            *reinterpret_cast<f32x4*>(&dense[sl * 16 + 4]) = f32x4{0.f, 0.f, 0.f, 0.f};
-            *reinterpret_cast<f32x4*>(&dense[sl * 16 + 8]) = f32x4{0.f, 0.f, 0.f, 0.f};
-            *reinterpret_cast<f32x4*>(&dense[sl * 16 + 12]) = f32x4{0.f, 0.f, 0.f, 0.f};
-            wave_lds_sync();
-            if ((wd[q] >> 16) & 1) {
-                const int lcv = (wd[q] >> 8) & 0xFF, nv = 1 << (lcv - 3);
-#pragma unroll
-                for (int k = 0; k < 16; ++k)
-                    if ((k < 8 || wide) && k < nv) dense[row_ch(vr[q].ix, lcv, sl, k)] = row_val<BV>(vr[q], k);
-            }
-            wave_lds_sync();
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const float2 v = *reinterpret_cast<const float2*>(&vb[wid][t][2 * lane]);
-#pragma unroll
-                for (int h = 0; h < G; ++h) {
-                    const float pp = ps[wid][pass * 8 + t][h];
-                    acc[h][0] = fmaf(pp, v.x, acc[h][0]);
-                    acc[h][1] = fmaf(pp, v.y, acc[h][1]);
-                }
-            }
-            wave_lds_sync();
-        }
-    }
+    // value words per lane: c/8 slots of BV bytes for the wave's largest c (at least 8 bytes)
+    if (!wide) attend_wave<BV, G, 2 * BV>(L, a.payload, wid, lane, acc, mW, lW);
+    else attend_wave<BV, G, 4 * BV>(L, a.payload, wid, lane, acc, mW, lW);
+
     if (lane == 0) {
 #pragma unroll
-        for (int h = 0; h < G; ++h) { wm[wid][h] = mW[h]; wl[wid][h] = lW[h]; }
+        for (int h = 0; h < G; ++h) { L.wm[wid][h] = mW[h]; L.wl[wid][h] = lW[h]; }
     }
 #pragma unroll
-    for (int h = 0; h < G; ++h) { wacc[wid][h][2 * lane] = acc[h][0]; wacc[wid][h][2 * lane + 1] = acc[h][1]; }
+    for (int h = 0; h < G; ++h) { L.wacc[wid][h][2 * lane] = acc[h][0]; L.wacc[wid][h][2 * lane + 1] = acc[h][1]; }
     __syncthreads();
     for (int i = tid; i < G * MKV_D; i += 256) {
         const int h = i >> 7, ch = i & 127;
         float M = -INFINITY;
 #pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) M = fmaxf(M, wm[w2][h]);
+        for (int w2 = 0; w2 < 4; ++w2) M = fmaxf(M, L.wm[w2][h]);
         float O = 0.f, Ls = 0.f;
         if (M != -INFINITY) {
 #pragma unroll
             for (int w2 = 0; w2 < 4; ++w2) {
-                if (wm[w2][h] != -INFINITY) {
-                    const float f = exp2f(wm[w2][h] - M);
-                    O = fmaf(wacc[w2][h][ch], f, O);
-                    Ls = fmaf(wl[w2][h], f, Ls);
+                if (L.wm[w2][h] != -INFINITY) {
+                    const float f = exp2f(L.wm[w2][h] - M);
+                    O = fmaf(L.wacc[w2][h][ch], f, O);
+                    Ls = fmaf(L.wl[w2][h], f, Ls);
                 }
             }
         }
