@@ -272,7 +272,14 @@ __device__ __forceinline__ int count_ge16(const uint32_t* w, uint32_t cand) {
 // Largest code k the vector admits (keep[k] channels hold >= frac of its energy); thr[k] <- the magnitude of its
 // keep[k]-th largest value.  Thresholds are searched bit by bit, only over the bits where the lower end of the
 // range and the vector's largest magnitude differ; smaller counts are searched above the previous threshold.
-__device__ __forceinline__ int vector_decide8(const uint32_t* w, const CmpArgs& a, uint32_t* thr) {
+// Called by every thread of the workgroup (64 vectors of one segment): before searching level k >= 2 the
+// workgroup checks whether some valid vector already cannot reach it, either because it failed level k-1 or
+// because the top keep[k] energy is bounded by E_{k-1} - (keep[k-1] - keep[k]) * t_{k-1}^2 (each of the dropped
+// values is at least t_{k-1}) and that bound is below the target.  Then no vector's result at level k can
+// change the segment's code, and the search stops for the whole workgroup.  s_fail: per-level flags, zero on
+// entry.
+__device__ __forceinline__ int vector_decide8(const uint32_t* w, const CmpArgs& a, uint32_t* thr, bool valid,
+                                              int* s_fail) {
     double e = 0.0;
     u16x2 mx2 = {0, 0}, mn2 = {0x7FFF, 0x7FFF};
 #pragma unroll
@@ -289,8 +296,16 @@ __device__ __forceinline__ int vector_decide8(const uint32_t* w, const CmpArgs& 
     const uint32_t mx = max8u(max((uint32_t)mx2.x, (uint32_t)mx2.y));
     uint32_t lo_end = min8u(min((uint32_t)mn2.x, (uint32_t)mn2.y));
     int best = 0;
+    double ec_prev = e_all, tv_prev = 0.0;
     for (int k = 1; k < a.n_keep; ++k) {
         const int c = a.keep[k];
+        if (k >= 2) {
+            // the margin keeps fp64 rounding of the bound from ever flagging a vector that reaches level k
+            const double ub = ec_prev - (double)(a.keep[k - 1] - c) * (tv_prev * tv_prev);
+            if (valid && (best < k - 1 || ub + 1e-10 * e_all < bound)) s_fail[k] = 1;
+            __syncthreads();
+            if (s_fail[k]) break;
+        }
         const uint32_t diff = lo_end ^ mx;
         uint32_t t = mx;
         if (diff) {
@@ -314,6 +329,8 @@ __device__ __forceinline__ int vector_decide8(const uint32_t* w, const CmpArgs& 
         thr[k] = t;
         if (ec >= bound) best = k;
         lo_end = t;
+        ec_prev = ec;
+        tv_prev = tv;
     }
     return best;
 }
@@ -363,12 +380,15 @@ __device__ __forceinline__ int segment_code8(int best, bool valid, int* s_code) 
 // =====================================================================================================
 constexpr int XS = 136;   // LDS row stride in u16 (272 B: 16-B aligned, skews banks between rows)
 
+// Four waves per SIMD (128 registers) so that two workgroups share a CU and one's MFMA rotation overlaps the
+// other's threshold search; the compiler keeps part of the basis fragments in scratch to fit.
 template <bool PACK>
-__global__ __launch_bounds__(512) void k_cmp_bf16(CmpArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_cmp_bf16(CmpArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t xs[2][64 * XS];
     __shared__ __attribute__((aligned(16))) uint16_t xh[64 * XS];
     __shared__ __attribute__((aligned(16))) uint8_t stg[64 * 64 * 3];
     __shared__ int s_code[8];
+    __shared__ int s_fail[2][4];   // per segment parity: levels some vector cannot reach
 
     const Tile t = cmp_tile(a);
     const int tid = threadIdx.x, lane = tid & 63, wid = uni(tid >> 6);
@@ -418,6 +438,7 @@ __global__ __launch_bounds__(512) void k_cmp_bf16(CmpArgs a) {
         load_tile(t.s0);
         store_tile(xs[0]);
     }
+    if (tid < 8) s_fail[tid >> 2][tid & 3] = 0;
     uint64_t wg_bytes = 0;                                  // decide: payload bytes of this workgroup
     uint64_t wg_off = PACK ? a.wg_total[blockIdx.x] : 0;    // pack: offset of this workgroup's first segment
 
@@ -427,6 +448,8 @@ __global__ __launch_bounds__(512) void k_cmp_bf16(CmpArgs a) {
         const int64_t tokS = t.tok0 + (int64_t)s * MKV_SEG;
         const int64_t gs = t.seg0 + s;
         __syncthreads();
+        // the other parity's flags were last read in the previous segment, before this barrier
+        if (tid < 4) s_fail[cur ^ 1][tid] = 0;
         const bool more = s + 1 < t.s1;
         if (more) load_tile(s + 1);
         const uint16_t* X = xs[cur];
@@ -461,7 +484,7 @@ __global__ __launch_bounds__(512) void k_cmp_bf16(CmpArgs a) {
         }
         if (!PACK) {
             uint32_t thr[4] = {0, 0, 0, 0};
-            const int best = vector_decide8(w, a, thr);
+            const int best = vector_decide8(w, a, thr, valid, s_fail[cur]);
             const int code = segment_code8(best, valid, s_code);
             if (valid && p == 0) {
                 uint16_t* tp = a.thr + thr_index(a, t, tokS + v);
