@@ -159,13 +159,15 @@ mkv_status mkv_decode_attn(const mkv_store* store, const void* q, int32_t n_q_he
 const char* mkv_last_error(void);
 
 /* ---- kernel timing (for benchmarks) --------------------------------------------------------------------
- * While profiling is on, every kernel the library launches is bracketed by two HIP events recorded on the
- * launch stream.  mkv_profile_stop synchronises those events and returns, per kernel id, the summed
- * duration in milliseconds and the launch count (arrays of MKV_PROFILE_KERNELS entries), then clears them.
- * At most max_launches launches are timed per session (later launches run untimed).  Not thread-safe with
- * respect to concurrent library calls from other threads. */
+ * While profiling is on, every kernel the library launches whose id has its bit set in kernel_mask (bit i =
+ * id i, see mkv_kernel_name) is bracketed by two HIP events recorded on the launch stream; other kernels run
+ * untimed, so timing one kernel adds only its own two event records to the stream.  mkv_profile_stop
+ * synchronises those events and returns, per kernel id, the summed duration in milliseconds and the launch
+ * count (arrays of MKV_PROFILE_KERNELS entries), then clears them.  At most max_launches launches are timed
+ * per session (later launches run untimed).  Not thread-safe with respect to concurrent library calls from
+ * other threads. */
 #define MKV_PROFILE_KERNELS 16
-mkv_status mkv_profile_start(int32_t max_launches);
+mkv_status mkv_profile_start(int32_t max_launches, uint32_t kernel_mask);
 mkv_status mkv_profile_stop(double* total_ms, int32_t* launches);
 const char* mkv_kernel_name(int32_t kernel_id);   /* NULL when the id is unused */
 

@@ -12,7 +12,7 @@ from __future__ import annotations
 
 import ctypes
 import os
-from ctypes import POINTER, byref, c_char_p, c_double, c_int32, c_int64, c_size_t, c_uint64, c_void_p
+from ctypes import POINTER, byref, c_char_p, c_double, c_int32, c_int64, c_size_t, c_uint32, c_uint64, c_void_p
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmkv.so")
@@ -75,7 +75,7 @@ SIGNATURES = {
     "mkv_decode_attn": (c_int32, [c_void_p, c_void_p, c_int32, POINTER(c_int32), c_void_p, c_void_p, c_int32,
                                   c_void_p, c_size_t, c_void_p]),
     "mkv_last_error": (c_char_p, []),
-    "mkv_profile_start": (c_int32, [c_int32]),
+    "mkv_profile_start": (c_int32, [c_int32, c_uint32]),
     "mkv_profile_stop": (c_int32, [POINTER(c_double), POINTER(c_int32)]),
     "mkv_kernel_name": (c_char_p, [c_int32]),
 }
@@ -284,8 +284,18 @@ def mkv_decode_attn(store: Store, q, T, out=None, sel=None, sel_stride=None, ws=
     return out, sel
 
 
-def mkv_profile_start(max_launches: int = 1 << 20):
-    _check(lib().mkv_profile_start(int(max_launches)))
+def mkv_profile_start(max_launches: int = 1 << 20, kernels=None):
+    """Times the library's kernel launches until mkv_profile_stop; kernels: names to time (default: all)."""
+    if kernels is None:
+        mask = 0xFFFFFFFF
+    else:
+        names = [mkv_kernel_name(i) for i in range(PROFILE_KERNELS)]
+        mask = 0
+        for k in kernels:
+            if k not in names:
+                raise ValueError(f"unknown kernel {k!r}")
+            mask |= 1 << names.index(k)
+    _check(lib().mkv_profile_start(int(max_launches), c_uint32(mask)))
 
 
 def mkv_profile_stop():

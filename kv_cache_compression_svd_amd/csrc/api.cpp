@@ -46,6 +46,7 @@ struct Profiler {
     std::mutex mu;
     bool on = false;
     int max_launches = 0;
+    uint32_t mask = 0;              // kernel ids to time
     struct Rec { int kid; hipEvent_t a, b; };
     std::vector<Rec> recs;
     std::vector<hipEvent_t> pool;   // created events, reused across sessions
@@ -57,7 +58,7 @@ struct Timed {
     hipStream_t s;
     hipEvent_t a = nullptr, b = nullptr;
     Timed(int k, hipStream_t st) : kid(k), s(st) {
-        if (!g_prof.on) return;
+        if (!g_prof.on || !((g_prof.mask >> k) & 1u)) return;
         std::lock_guard<std::mutex> lk(g_prof.mu);
         if ((int)g_prof.recs.size() >= g_prof.max_launches) return;
         while (g_prof.pool.size() < g_prof.used + 2) {
@@ -512,12 +513,13 @@ mkv_status mkv_decode_attn(const mkv_store* s, const void* q, int32_t n_q_heads,
 }
 
 // ---- profiling --------------------------------------------------------------------------------------------
-mkv_status mkv_profile_start(int32_t max_launches) {
+mkv_status mkv_profile_start(int32_t max_launches, uint32_t kernel_mask) {
     if (max_launches < 0) return fail(MKV_E_ARG, "max_launches must be >= 0");
     std::lock_guard<std::mutex> lk(g_prof.mu);
     g_prof.recs.clear();
     g_prof.used = 0;
     g_prof.max_launches = max_launches;
+    g_prof.mask = kernel_mask;
     g_prof.on = true;
     return MKV_OK;
 }
