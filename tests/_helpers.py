@@ -65,9 +65,41 @@ def segment_id(X, r, h, s, S, Hkv, seg_base, S_r):
     return X * S + Hkv * seg_base[r] + h * S_r[r] + s
 
 
+def _parse_segment(payload: np.ndarray, off: int, ns: int, c: int, dtype: str):
+    """(channel indices [ns][c], values [ns][c] as float64) of one segment whose bytes start at payload[off]."""
+    bv = 2 if dtype == "bf16" else 4
+    vb = payload[off:off + ns * c * bv]
+    v = W.to_f64(vb.view(np.uint16 if bv == 2 else np.float32).reshape(ns, c), dtype)
+    if c < D:
+        idx = payload[off + ns * c * bv: off + ns * c * (bv + 1)].reshape(ns, c).astype(np.int64)
+        assert np.all(np.diff(idx, axis=1) > 0), "channel indices must ascend"
+    else:
+        idx = np.broadcast_to(np.arange(D), (ns, D))
+    return idx, v
+
+
+def _stream_from(payload, codes, seg_off, pay_base, keep, r, h, X, S, Hkv, cu, dtype) -> Stream:
+    n, S_r, seg_base = seg_counts(cu)
+    nr = int(n[r])
+    mask = np.zeros((nr, D), dtype=bool)
+    vals = np.zeros((nr, D))
+    cs = np.zeros(int(S_r[r]), dtype=np.int64)
+    cds = np.zeros(int(S_r[r]), dtype=np.int64)
+    for s in range(int(S_r[r])):
+        g = segment_id(X, r, h, s, S, Hkv, seg_base, S_r)
+        code = int(codes[g])
+        c = keep[code]
+        cds[s], cs[s] = code, c
+        ns = min(SEG, nr - s * SEG)
+        idx, v = _parse_segment(payload, int(seg_off[g]) - pay_base, ns, c, dtype)
+        rows = np.arange(s * SEG, s * SEG + ns)[:, None]
+        mask[rows, idx] = True
+        vals[rows, idx] = v
+    return Stream(nr, D, cds, cs, mask, vals)
+
+
 def read_store(store, dtype: str) -> dict:
     """Copies a device store to the host and decodes it into {(r, h, X): Stream}; also returns raw arrays."""
-    import torch
     info = store.view()
     keep = tuple(info.policy.keep[i] for i in range(info.policy.n_keep))
     S = int(info.segments_per_tensor)
@@ -81,38 +113,62 @@ def read_store(store, dtype: str) -> dict:
     seg_off = buf[o_off:o_off + 16 * S].view(np.uint64).copy()
     total = int(buf[0:8].view(np.uint64)[0])
     payload = buf[o_pay:o_pay + total]
-    bv = 2 if dtype == "bf16" else 4
     cu = store.cu
-    n, S_r, seg_base = seg_counts(cu)
+    n, _, _ = seg_counts(cu)
     out = {}
     for r in range(len(n)):
         for h in range(Hkv):
             for X in (0, 1):
-                nr = int(n[r])
-                mask = np.zeros((nr, D), dtype=bool)
-                vals = np.zeros((nr, D))
-                cs = np.zeros(int(S_r[r]), dtype=np.int64)
-                cds = np.zeros(int(S_r[r]), dtype=np.int64)
-                for s in range(int(S_r[r])):
-                    g = segment_id(X, r, h, s, S, Hkv, seg_base, S_r)
-                    code = int(codes[g])
-                    c = keep[code]
-                    cds[s], cs[s] = code, c
-                    ns = min(SEG, nr - s * SEG)
-                    off = int(seg_off[g])
-                    vb = payload[off:off + ns * c * bv]
-                    v = W.to_f64(vb.view(np.uint16 if bv == 2 else np.float32).reshape(ns, c), dtype)
-                    if c < D:
-                        idx = payload[off + ns * c * bv: off + ns * c * (bv + 1)].reshape(ns, c).astype(np.int64)
-                    else:
-                        idx = np.broadcast_to(np.arange(D), (ns, D))
-                    rows = np.arange(s * SEG, s * SEG + ns)[:, None]
-                    mask[rows, idx] = True
-                    vals[rows, idx] = v
-                    if c < D:
-                        assert np.all(np.diff(idx, axis=1) > 0), "channel indices must ascend"
-                out[(r, h, X)] = Stream(nr, D, cds, cs, mask, vals)
+                out[(r, h, X)] = _stream_from(payload, codes, seg_off, 0, keep, r, h, X, S, Hkv, cu, dtype)
     return {"streams": out, "codes": codes, "seg_off": seg_off, "total": total, "S": S}
+
+
+class StoreReader:
+    """Reads a large device store piecewise: its metadata once, then one stream's payload at a time."""
+
+    def __init__(self, store, dtype: str):
+        info = store.view()
+        self.store, self.dtype = store, dtype
+        self.keep = tuple(info.policy.keep[i] for i in range(info.policy.n_keep))
+        self.S = int(info.segments_per_tensor)
+        self.Hkv = int(info.n_kv_heads)
+        base = store.buf.data_ptr()
+        self.o_pay = info.payload - base
+        o_codes, o_off = info.codes - base, info.seg_off - base
+        self.codes = store.buf[o_codes:o_codes + 2 * self.S].cpu().numpy().copy()
+        self.seg_off = store.buf[o_off:o_off + 16 * self.S].cpu().numpy().view(np.uint64).copy()
+        self.total = int(store.buf[0:8].cpu().numpy().view(np.uint64)[0])
+        self.cu = store.cu
+
+    def segment_bytes(self, bv: int) -> np.ndarray:
+        """Payload bytes of every segment implied by its code (K segments, then V segments)."""
+        n, S_r, seg_base = seg_counts(self.cu)
+        ns = np.zeros(2 * self.S, dtype=np.int64)
+        for X in (0, 1):
+            for r in range(len(n)):
+                per = np.full(int(S_r[r]), SEG, dtype=np.int64)
+                if S_r[r]:
+                    per[-1] = int(n[r]) - (int(S_r[r]) - 1) * SEG
+                for h in range(self.Hkv):
+                    g0 = segment_id(X, r, h, 0, self.S, self.Hkv, seg_base, S_r)
+                    ns[g0:g0 + int(S_r[r])] = per
+        c = np.asarray(self.keep, dtype=np.int64)[self.codes.astype(np.int64)]
+        return ns * c * (bv + (c < D))
+
+    def stream(self, r: int, h: int, X: int) -> Stream:
+        n, S_r, seg_base = seg_counts(self.cu)
+        if S_r[r] == 0:
+            return Stream(0, D, np.zeros(0, np.int64), np.zeros(0, np.int64), np.zeros((0, D), bool), np.zeros((0, D)))
+        g0 = segment_id(X, r, h, 0, self.S, self.Hkv, seg_base, S_r)
+        g1 = g0 + int(S_r[r]) - 1
+        bv = 2 if self.dtype == "bf16" else 4
+        if getattr(self, "_sizes", None) is None:
+            self._sizes = self.segment_bytes(bv)
+        last = int(self._sizes[g1])
+        lo, hi = int(self.seg_off[g0]), int(self.seg_off[g1]) + last
+        payload = self.store.buf[self.o_pay + lo:self.o_pay + hi].cpu().numpy()
+        return _stream_from(payload, self.codes, self.seg_off, lo, self.keep, r, h, X, self.S, self.Hkv,
+                            self.cu, self.dtype)
 
 
 def pack_oracle_store(streams: dict, cu, Hkv: int, dtype: str, keep: tuple):
@@ -152,7 +208,9 @@ def upload_oracle_store(streams, inp: W.Inputs, keep, device="cuda"):
     dt = mkv.MKV_BF16 if inp.dtype == "bf16" else mkv.MKV_FP32
     pol = mkv.SegPolicy.make(keep)
     sb, _ = mkv.mkv_compress_bytes(None, None, inp.cu_seqlens, pol, n_kv_heads=w.n_kv_heads, dtype=dt)
-    buf = torch.zeros(sb, dtype=torch.uint8, device=device)
+    raw = torch.zeros(sb + 256, dtype=torch.uint8, device=device)
+    pad = (-raw.data_ptr()) % 256          # the library wants 256-byte alignment (host buffers may lack it)
+    buf = raw[pad:pad + sb]
     store = mkv.mkv_store_attach(inp.cu_seqlens, w.n_kv_heads, dt, pol, inp.basis is not None, buf)
     info = store.view()
     codes, seg_off, payload = pack_oracle_store(streams, inp.cu_seqlens, w.n_kv_heads, inp.dtype, keep)
@@ -192,6 +250,50 @@ def check_selection(sel_row: np.ndarray, ref_sel: np.ndarray, scores: np.ndarray
         bad = diff[np.abs(scores[diff] - sT) > band * abs(sT)]
         assert bad.size == 0, f"selection differs outside the near-tie band at tokens {bad[:10]}"
     return int(diff.size)
+
+
+def valid_selections(scores: np.ndarray, T_eff: int, band=1e-5, cap=64):
+    """Every selection the near-tie rule accepts, in ascending order: the tokens scoring above the band around
+    the T-th score, plus any choice of the remaining count among the tokens inside it.  The score estimate is
+    a sum over the group's heads, so a token at the threshold can still weigh in one head's softmax: each
+    accepted selection has its own exact output.  None when there are more than ``cap`` selections."""
+    from itertools import combinations
+    from math import comb
+    if T_eff == 0:
+        return [np.zeros(0, dtype=np.int64)]
+    sT = kth_score(scores, T_eff)
+    tol = band * abs(sT)
+    above = np.nonzero(scores > sT + tol)[0]
+    inband = np.nonzero(np.abs(scores - sT) <= tol)[0]
+    k = T_eff - above.size
+    if comb(inband.size, k) > cap:
+        return None
+    return [np.sort(np.concatenate([above, np.asarray(c, dtype=np.int64)])) for c in combinations(inband, k)]
+
+
+def check_decode_unit(sel_row, out_rows, q_group, basis_k, basis_v, kstream, vstream, T_eff: int) -> int:
+    """One (request, KV head) unit against the oracle on the same store: the selection must be one the
+    near-tie rule accepts, and the output must match the oracle's output for that same accepted selection
+    (the oracle enumerates the accepted selections itself).  Returns the number of tokens that differ from
+    the oracle's own first choice; -1 when the band held too many ties to enumerate (output not compared)."""
+    from oracle import attend, decode_unit, rotate_queries
+    res = decode_unit(q_group, basis_k, basis_v, kstream, vstream, T_eff)
+    nd = check_selection(sel_row, res["sel"], res["scores"], T_eff)
+    if nd == 0:
+        check_out(out_rows, res["out"])
+        return 0
+    sels = valid_selections(res["scores"], T_eff)
+    if sels is None:
+        return -1
+    got = np.asarray(sel_row[:T_eff], dtype=np.int64)
+    match = [s for s in sels if np.array_equal(s, got)]
+    assert match, "selection is not one of the accepted near-tie selections"
+    qp = rotate_queries(q_group, basis_k)
+    ref = attend(qp, kstream.vals[match[0]], vstream.vals[match[0]])
+    if basis_v is not None:
+        ref = ref @ np.asarray(basis_v, dtype=np.float64).T
+    check_out(out_rows, ref)
+    return nd
 
 
 def check_out(out: np.ndarray, ref: np.ndarray, rel=2e-3):

@@ -13,8 +13,8 @@ import pytest
 
 import oracle
 import workloads as W
-from _helpers import (check_out, check_selection, inputs_to_torch, prerotated_inputs, read_store,
-                      upload_oracle_store)
+from _helpers import (check_decode_unit, check_out, check_selection, inputs_to_torch, prerotated_inputs,
+                      read_store, upload_oracle_store)
 
 pytestmark = pytest.mark.gpu
 
@@ -120,9 +120,11 @@ def test_compress_p3_svd_basis(mkv, name, div):
     assert tok_diff <= max(4, 0.02 * tok_total)
 
 
-def _decode_compare(mkv, inp, store, q, ref_streams, strict_out=True):
+def _decode_compare(mkv, inp, store, q, ref_streams):
+    """Decodes on the GPU and checks every (request, KV head) unit against the oracle decoding the same
+    store: an accepted selection (near ties) and the oracle's output for it.  Returns the number of units
+    whose selection differs inside the near-tie band."""
     import torch
-    res = oracle.decode_all(inp, ref_streams)
     out, sel = mkv.mkv_decode_attn(store, q, inp.T)
     torch.cuda.synchronize()
     out = out.cpu().numpy().astype(np.float64)
@@ -130,15 +132,17 @@ def _decode_compare(mkv, inp, store, q, ref_streams, strict_out=True):
     w = inp.workload
     G = w.group
     ndiff_units = 0
-    for (r, h), rr in res.items():
+    for r in range(w.batch):
         n = int(inp.cu_seqlens[r + 1] - inp.cu_seqlens[r])
         te = min(int(inp.T[r]), n)
-        nd = check_selection(sel[r, h], rr["sel"], rr["scores"], te)
-        o = out[r, h * G:(h + 1) * G]
-        if nd == 0 or te >= 64:
-            check_out(o, rr["out"])
-        else:
-            ndiff_units += 1
+        for h in range(w.n_kv_heads):
+            qg = W.to_f64(inp.q[r, h * G:(h + 1) * G, :], inp.dtype)
+            bk = None if inp.basis is None else inp.basis[r, h, 0]
+            bvv = None if inp.basis is None else inp.basis[r, h, 1]
+            nd = check_decode_unit(sel[r, h], out[r, h * G:(h + 1) * G], qg, bk, bvv, ref_streams[(r, h, 0)],
+                                   ref_streams[(r, h, 1)], te)
+            assert nd >= 0, f"too many near-tie selections to enumerate at unit {(r, h)}"
+            ndiff_units += nd > 0
     return ndiff_units
 
 
