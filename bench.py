@@ -178,6 +178,34 @@ def main():
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
     score_kern = mkv.mkv_profile_stop()
 
+    # uncompressed baseline on the same inputs (an extra): bf16 only
+    dense_base = None
+    if w.dtype == "bf16":
+        dws = torch.empty(mkv.mkv_dense_decode_workspace_bytes(K, V, inp.cu_seqlens, w.n_q_heads), dtype=torch.uint8,
+                          device=dev)
+        dout = torch.empty_like(out)
+
+        def dstep():
+            mkv.mkv_dense_decode_attn(K, V, inp.cu_seqlens, q, out=dout, ws=dws)
+
+        for _ in range(args.warmup):
+            dstep()
+        torch.cuda.synchronize()
+        mkv.mkv_profile_start(kernels=["dense_attend"])
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dstep()
+        torch.cuda.synchronize()
+        dms = (time.perf_counter() - t0) * 1e3 / args.steps
+        dk = mkv.mkv_profile_stop()
+        d_attend_ms = dk["dense_attend"][0] / max(dk["dense_attend"][1], 1)
+        dense_bytes = dense + w.batch * w.n_q_heads * 128 * (bv + 4)
+        dense_base = {"ms_per_step": dms, "context_tokens_per_s": total_tokens / (dms * 1e-3),
+                      "alg_bytes": dense_bytes, "attend_kernel_ms": d_attend_ms,
+                      "attend_kernel_GBps": dense_bytes / (d_attend_ms * 1e-3) / 1e9,
+                      "attend_kernel_frac_of_hbm_peak": dense_bytes / (d_attend_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                      "compressed_speedup": dms / ms}
+
     sel_np = sel.cpu().numpy()
     # V payload actually gathered: rows of the selected tokens
     n = np.diff(inp.cu_seqlens)
@@ -234,6 +262,7 @@ def main():
                      "rotation_TFLOPs": rot_flops / (compress_ms * 1e-3) / 1e12,
                      "rotation_frac_of_bf16_mfma_peak": rot_flops / (compress_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
                      "kernels_avg_ms": {k: v[0] / max(v[1], 1) for k, v in c_kern.items()}},
+        "dense_baseline": dense_base,
         "input_generation_s": t_gen,
     }
     if not args.no_cpu_baseline:

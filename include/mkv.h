@@ -155,6 +155,20 @@ mkv_status mkv_decode_attn(const mkv_store* store, const void* q, int32_t n_q_he
                            float* out, int32_t* sel, int32_t sel_stride, void* ws, size_t ws_bytes,
                            mkv_stream_t stream);
 
+/* ---- uncompressed baseline ---------------------------------------------------------------------------------
+ * Decode attention over the uncompressed bf16 K/V of the descriptor (no rotation, no channel or token
+ * selection): for request r and query head h of KV head g = h / (n_q_heads/n_kv_heads),
+ *   out_h = sum over all n_r tokens j of softmax_j(q_h . k_j / sqrt(128)) * v_j.
+ * The pages compare their compressed attention with such an uncompressed baseline (section 1, Observation &
+ * Approach 2, where uncompressed decode attention is profiled as memory-bound).
+ *   kv   bf16 only (MKV_E_UNSUPPORTED otherwise); K and V [dev] as in the descriptor.
+ *   q    [dev] bf16 [batch][n_q_heads][128]; n_q_heads a multiple of n_kv_heads, group of 1, 2, 4 or 8.
+ *   out  [dev] float32 [batch][n_q_heads][128]; an empty request gets zeros.
+ *   ws   [dev] >= mkv_dense_decode_workspace_bytes, 256-byte aligned; contents are scratch. */
+mkv_status mkv_dense_decode_workspace_bytes(const mkv_kv_desc* kv, int32_t n_q_heads, size_t* ws_bytes);
+mkv_status mkv_dense_decode_attn(const mkv_kv_desc* kv, const void* q, int32_t n_q_heads, float* out, void* ws,
+                                 size_t ws_bytes, mkv_stream_t stream);
+
 /* Text of the last error on the calling thread; valid until the next call on that thread. */
 const char* mkv_last_error(void);
 

@@ -74,6 +74,8 @@ SIGNATURES = {
     "mkv_decode_workspace_bytes": (c_int32, [c_void_p, c_int32, POINTER(c_int32), POINTER(c_size_t)]),
     "mkv_decode_attn": (c_int32, [c_void_p, c_void_p, c_int32, POINTER(c_int32), c_void_p, c_void_p, c_int32,
                                   c_void_p, c_size_t, c_void_p]),
+    "mkv_dense_decode_workspace_bytes": (c_int32, [c_void_p, c_int32, POINTER(c_size_t)]),
+    "mkv_dense_decode_attn": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
     "mkv_last_error": (c_char_p, []),
     "mkv_profile_start": (c_int32, [c_int32, c_uint32]),
     "mkv_profile_stop": (c_int32, [POINTER(c_double), POINTER(c_int32)]),
@@ -282,6 +284,34 @@ def mkv_decode_attn(store: Store, q, T, out=None, sel=None, sel_stride=None, ws=
     _check(lib().mkv_decode_attn(store.handle, _ptr(q), int(Hq), tp, _ptr(out), _ptr(sel), int(stride), _ptr(ws),
                                  c_size_t(ws.numel()), _stream_ptr(stream)))
     return out, sel
+
+
+def mkv_dense_decode_workspace_bytes(K, V, cu_seqlens, n_q_heads: int) -> int:
+    d, cu = _kv_desc(K, V, cu_seqlens)
+    v = c_size_t()
+    _check(lib().mkv_dense_decode_workspace_bytes(byref(d), int(n_q_heads), byref(v)))
+    return int(v.value)
+
+
+def mkv_dense_decode_attn(K, V, cu_seqlens, q, out=None, ws=None, stream=None):
+    """Uncompressed decode attention (the baseline): out float32 [batch][n_q_heads][128] for bf16 K, V
+    [tokens][n_kv_heads][128] and q [batch][n_q_heads][128] (all CUDA)."""
+    torch = _torch()
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous() or not q.is_cuda:
+        raise ValueError("q must be a contiguous CUDA tensor [batch][n_q_heads][128]")
+    d, cu = _kv_desc(K, V, cu_seqlens)
+    B, Hq = q.shape[0], q.shape[1]
+    if B != d.batch:
+        raise ValueError(f"q has batch {B}, cu_seqlens {d.batch}")
+    if _dtype_code(q) != d.dtype:
+        raise TypeError("q must have the dtype of K and V")
+    if out is None:
+        out = torch.empty((B, Hq, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if ws is None:
+        ws = torch.empty(mkv_dense_decode_workspace_bytes(K, V, cu_seqlens, Hq), dtype=torch.uint8, device=q.device)
+    _check(lib().mkv_dense_decode_attn(byref(d), _ptr(q), int(Hq), _ptr(out), _ptr(ws), c_size_t(ws.numel()),
+                                       _stream_ptr(stream)))
+    return out
 
 
 def mkv_profile_start(max_launches: int = 1 << 20, kernels=None):

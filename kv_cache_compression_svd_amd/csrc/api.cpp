@@ -37,10 +37,11 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ---- kernel timing --------------------------------------------------------------------------------------
 enum KernelId {
     K_UPLOAD = 0, K_CMP_DECIDE, K_CMP_SCAN, K_CMP_PACK, K_DEC_PREP, K_SCORE, K_SEL_COLLECT, K_SEL_EMIT,
-    K_ATTEND, K_COMBINE, K_COUNT
+    K_ATTEND, K_COMBINE, K_DENSE_ATTEND, K_DENSE_COMBINE, K_COUNT
 };
 const char* kKernelNames[K_COUNT] = {"upload", "compress_decide", "compress_scan", "compress_pack", "decode_prep",
-                                     "score", "select_collect", "select_emit", "attend", "combine"};
+                                     "score", "select_collect", "select_emit", "attend", "combine",
+                                     "dense_attend", "dense_combine"};
 
 struct Profiler {
     std::mutex mu;
@@ -493,6 +494,7 @@ mkv_status mkv_decode_attn(const mkv_store* s, const void* q, int32_t n_q_heads,
     a.state = reinterpret_cast<uint32_t*>(w + P.o_state);
     a.L = reinterpret_cast<uint2*>(w + P.o_L);
     a.part = reinterpret_cast<float*>(w + P.o_part);
+    a.achunk = kAttnChunk;
 
     // per-request tables: the first kUploadWords words ride on the prep kernel, the rest on upload launches
     int32_t* tdst = reinterpret_cast<int32_t*>(w + P.o_tab);
@@ -509,6 +511,99 @@ mkv_status mkv_decode_attn(const mkv_store* s, const void* q, int32_t n_q_heads,
     if ((st = run(K_SEL_EMIT, stream, [&] { return launch_sel_emit(a, streams, stream); }))) return st;
     if ((st = run(K_ATTEND, stream, [&] { return launch_attend(a, (int)P.n_ablk, stream); }))) return st;
     if ((st = run(K_COMBINE, stream, [&] { return launch_combine(a, streams, stream); }))) return st;
+    return MKV_OK;
+}
+
+// ---- uncompressed baseline --------------------------------------------------------------------------------
+namespace {
+
+struct DensePlan {
+    int32_t G = 0;
+    std::vector<int32_t> tab;    // n | tok0 | T (= n) | first workgroup [B+1]
+    int64_t n_blk = 0;
+    uint64_t o_tab = 0, o_part = 0, bytes = 0;
+};
+
+mkv_status plan_dense(const mkv_kv_desc* kv, int32_t n_q_heads, bool need_data, Shape* sh, DensePlan* P) {
+    mkv_status st = check_kv(kv, need_data, sh);
+    if (st) return st;
+    if (sh->dtype != MKV_BF16) return fail(MKV_E_UNSUPPORTED, "the uncompressed baseline takes bf16 K/V only");
+    if (n_q_heads < 1 || n_q_heads % sh->Hkv != 0)
+        return fail(MKV_E_ARG, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)", n_q_heads, sh->Hkv);
+    P->G = n_q_heads / sh->Hkv;
+    if (P->G != 1 && P->G != 2 && P->G != 4 && P->G != 8)
+        return fail(MKV_E_UNSUPPORTED, "query heads per KV head must be 1, 2, 4 or 8 (got %d)", P->G);
+    const int B = sh->B;
+    P->tab.assign(4 * B + 1, 0);
+    int64_t blk = 0;
+    for (int r = 0; r < B; ++r) {
+        const int64_t n = sh->cu[r + 1] - sh->cu[r];
+        P->tab[r] = (int32_t)n;
+        P->tab[B + r] = (int32_t)sh->cu[r];
+        P->tab[2 * B + r] = (int32_t)n;
+        P->tab[3 * B + r] = (int32_t)blk;
+        blk += (int64_t)sh->Hkv * cdiv(n, kDenseChunk);
+    }
+    P->tab[4 * B] = (int32_t)blk;
+    if (blk > INT32_MAX) return fail(MKV_E_UNSUPPORTED, "too many workgroups");
+    P->n_blk = blk;
+    P->o_tab = 0;
+    P->o_part = align_up(4 * P->tab.size());
+    P->bytes = align_up(P->o_part + 4ull * std::max<int64_t>(blk, 1) * P->G * (MKV_HEAD_DIM + 2));
+    return MKV_OK;
+}
+
+}  // namespace
+
+mkv_status mkv_dense_decode_workspace_bytes(const mkv_kv_desc* kv, int32_t n_q_heads, size_t* ws_bytes) {
+    Shape sh;
+    DensePlan P;
+    mkv_status st = plan_dense(kv, n_q_heads, false, &sh, &P);
+    if (st) return st;
+    if (!ws_bytes) return fail(MKV_E_ARG, "ws_bytes is NULL");
+    *ws_bytes = P.bytes;
+    return MKV_OK;
+}
+
+mkv_status mkv_dense_decode_attn(const mkv_kv_desc* kv, const void* q, int32_t n_q_heads, float* out, void* ws,
+                                 size_t ws_bytes, mkv_stream_t stream_) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    Shape sh;
+    DensePlan P;
+    mkv_status st = plan_dense(kv, n_q_heads, true, &sh, &P);
+    if (st) return st;
+    if (!q || !out) return fail(MKV_E_ARG, "q and out must be non-NULL");
+    if (!ws) return fail(MKV_E_ARG, "ws is NULL");
+    if (!aligned(ws)) return fail(MKV_E_ARG, "ws must be 256-byte aligned");
+    if (ws_bytes < P.bytes) return fail(MKV_E_ARG, "ws_bytes %zu < required %llu", ws_bytes, (unsigned long long)P.bytes);
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    int32_t* tb = reinterpret_cast<int32_t*>(w + P.o_tab);
+    if ((st = upload_words(tb, P.tab, 0, stream))) return st;
+    const int B = sh.B;
+    DenseArgs d;
+    d.B = B;
+    d.Hkv = sh.Hkv;
+    d.G = P.G;
+    d.K = static_cast<const uint16_t*>(kv->K);
+    d.V = static_cast<const uint16_t*>(kv->V);
+    d.q = static_cast<const uint16_t*>(q);
+    d.t_n = tb;
+    d.t_tok0 = tb + B;
+    d.t_dblk = tb + 3 * B;
+    d.part = reinterpret_cast<float*>(w + P.o_part);
+    if ((st = run(K_DENSE_ATTEND, stream, [&] { return launch_dense_attend(d, (int)P.n_blk, stream); }))) return st;
+    DecArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.B = B;
+    a.Hkv = sh.Hkv;
+    a.G = P.G;
+    a.out = out;
+    a.t_n = tb;
+    a.t_T = tb + 2 * B;
+    a.t_ablk = tb + 3 * B;
+    a.part = d.part;
+    a.achunk = kDenseChunk;
+    if ((st = run(K_DENSE_COMBINE, stream, [&] { return launch_combine(a, B * sh.Hkv, stream); }))) return st;
     return MKV_OK;
 }
 

@@ -887,7 +887,7 @@ __global__ __launch_bounds__(256) void k_combine(DecArgs a) {
     __shared__ float bsh[MKV_D * (MKV_D + 1)];
     const int stream = blockIdx.x, r = stream / a.Hkv, g = stream - r * a.Hkv;
     const int n = a.t_n[r], T = (n > 0) ? a.t_T[r] : 0;
-    const int nach = (T + kAttnChunk - 1) / kAttnChunk;
+    const int nach = (T + a.achunk - 1) / a.achunk;
     const int first = a.t_ablk[r] + g * nach;
     const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int Hq = a.G * a.Hkv;

@@ -11,6 +11,7 @@ constexpr int kStateWords = 128;        // per (request, KV head) selection stat
 constexpr int kCoarseOff = 64;          // coarse histogram (top 6 key bits) inside the state words
 constexpr int kKeysPerBlock = 4096;     // keys per workgroup in the selection passes
 constexpr int kAttnChunk = 256;         // selected tokens per attention workgroup
+constexpr int kDenseChunk = 512;        // tokens per workgroup of the uncompressed baseline
 
 // selection state words
 enum { ST_P1 = 1, ST_NGT = 2, ST_NCAND = 3, ST_NEED = 4, ST_GTFILL = 5, ST_CFILL = 6 };
@@ -77,6 +78,7 @@ struct DecArgs {
     uint32_t* state;            // [B*Hkv][16]
     uint2* L;                   // same indexing as keys: taken tokens, then candidates, as (token index, key)
     float* part;                // [n_ablk][G][130]
+    int32_t achunk;             // tokens per attention partial (the combine kernel's chunk)
 };
 
 hipError_t launch_dec_prep(const DecArgs& a, const Upload& tab, hipStream_t s);
@@ -85,5 +87,19 @@ hipError_t launch_sel_collect(const DecArgs& a, int n_blocks, hipStream_t s);
 hipError_t launch_sel_emit(const DecArgs& a, int n_streams, hipStream_t s);
 hipError_t launch_attend(const DecArgs& a, int n_blocks, hipStream_t s);
 hipError_t launch_combine(const DecArgs& a, int n_streams, hipStream_t s);
+
+// ---- uncompressed baseline ------------------------------------------------------------------------------
+struct DenseArgs {
+    int32_t B, Hkv, G;
+    const uint16_t* K;          // bf16 [tokens][Hkv][128]
+    const uint16_t* V;
+    const uint16_t* q;          // bf16 [B][Hq][128]
+    const int32_t* t_n;         // per request: context
+    const int32_t* t_tok0;      // per request: first token
+    const int32_t* t_dblk;      // [B+1] first workgroup of each request (Hkv * chunks per request)
+    float* part;                // [blocks][G][130]
+};
+
+hipError_t launch_dense_attend(const DenseArgs& a, int n_blocks, hipStream_t s);
 
 }  // namespace mkv

@@ -23,5 +23,6 @@ force on tiny inputs, library routines for the special cases that reduce to them
 from .rounding import rne, rne_bf16, rne_f32  # noqa: F401
 from .compress import (Policy, DEFAULT_POLICY, Stream, rotate_round, channel_order, kept_energy,  # noqa: F401
                        vector_min_keep, compress_stream, compress_all)
-from .decode import (rotate_queries, scores, select_top, attend, decode_unit, decode_all)  # noqa: F401
+from .decode import (rotate_queries, scores, select_top, attend, decode_unit, decode_all,  # noqa: F401
+                     dense_decode_unit)
 from .sizes import stream_payload_bytes, store_payload_bytes, dense_kv_bytes, segment_meta_bytes  # noqa: F401

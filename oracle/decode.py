@@ -65,6 +65,16 @@ def decode_unit(q: np.ndarray, basis_k, basis_v, kstream: Stream, vstream: Strea
     return {"out": out, "sel": sel, "scores": s, "qbar": qbar}
 
 
+def dense_decode_unit(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
+    """The uncompressed baseline the pages compare against (section 1, Observation & Approach 2): exact softmax
+    attention of the group's queries q [G][d] over every stored token's full key and value rows k, v [n][d]
+    (no rotation, no selection).  An empty context gives zeros."""
+    q = np.asarray(q, dtype=np.float64)
+    if k.shape[0] == 0:
+        return np.zeros_like(q)
+    return attend(q, np.asarray(k, dtype=np.float64), np.asarray(v, dtype=np.float64))
+
+
 def decode_all(inputs, streams: dict, units=None) -> dict:
     """Decode step for every (request, KV group) of a ``workloads.Inputs`` whose compressed streams are in
     ``streams`` ({(r, h, X): Stream}).  Returns {(r, h): decode_unit result}."""

@@ -11,7 +11,8 @@ too slow for whole stores at these sizes, so it checks:
     error can move, a differing code only where some vector's energy ratio is within that error of the target;
   - sampled (request, KV head) units: with the oracle decoding the GPU's own store of that unit (read back
     piecewise), the selection must be one the near-tie rule accepts and the output must match the oracle's
-    output for that accepted selection.
+    output for that accepted selection; the uncompressed baseline (bf16 workloads) must match the oracle's
+    exact attention over the unit's full rows.
 """
 import os
 
@@ -20,7 +21,7 @@ import pytest
 
 import oracle
 import workloads as W
-from _helpers import SEG, StoreReader, check_decode_unit, inputs_to_torch, seg_counts
+from _helpers import SEG, StoreReader, check_decode_unit, check_out, inputs_to_torch, seg_counts
 
 pytestmark = pytest.mark.gpu
 
@@ -97,6 +98,9 @@ def test_full_size_sampled_parity(mkv, full_inputs, name):
     store_buf = torch.empty(sb, dtype=torch.uint8, device="cuda")
     scratch = torch.empty(tb, dtype=torch.uint8, device="cuda")
     store = mkv.mkv_compress(K, V, inp.cu_seqlens, basis, policy, store_buf=store_buf, scratch=scratch)
+    dense = None
+    if inp.dtype == "bf16":   # the uncompressed baseline on the same inputs
+        dense = mkv.mkv_dense_decode_attn(K, V, inp.cu_seqlens, q).cpu().numpy().astype(np.float64)
     del K, V, scratch
     T = inp.T
     te = np.minimum(T, np.diff(inp.cu_seqlens))
@@ -138,6 +142,10 @@ def test_full_size_sampled_parity(mkv, full_inputs, name):
                                streams[0], streams[1], int(te[r]))
         assert nd >= 0, f"too many near-tie selections to enumerate at unit {(r, h)}"
         near_ties += nd
+        if dense is not None:
+            k = W.to_f64(inp.K[cu[r]:cu[r + 1], h, :], inp.dtype)
+            v = W.to_f64(inp.V[cu[r]:cu[r + 1], h, :], inp.dtype)
+            check_out(dense[r, h * G:(h + 1) * G], oracle.dense_decode_unit(qg, k, v))
     print(f"{name}: {seg_checked} sampled segments, {code_diff} with another code (near the target); "
           f"{near_ties} tokens swapped inside the near-tie band")
     assert code_diff <= 1

@@ -187,3 +187,26 @@ def test_selection_and_strategy_invariants(n, T, seed, dt):
             if smaller:
                 cs = max(smaller)
                 assert (srt[:, :cs].sum(axis=1) < 0.9 * tot * (1 + 1e-15)).any()
+
+
+@pytest.mark.parametrize("n", [1, 7, 300])
+def test_dense_baseline_equals_torch_sdpa(n):
+    from oracle import dense_decode_unit
+    rng = np.random.default_rng(100 + n)
+    k, v = rng.standard_normal((n, 128)), rng.standard_normal((n, 128))
+    q = rng.standard_normal((4, 128))
+    np.testing.assert_allclose(dense_decode_unit(q, k, v), _sdpa(q, k, v), rtol=1e-12, atol=1e-13)
+
+
+def test_dense_baseline_special_cases():
+    from oracle import dense_decode_unit
+    rng = np.random.default_rng(7)
+    v = rng.standard_normal((50, 128))
+    q = rng.standard_normal((2, 128))
+    # one token: its value row, whatever the query
+    np.testing.assert_array_equal(dense_decode_unit(q, rng.standard_normal((1, 128)), v[:1]), np.repeat(v[:1], 2, 0))
+    # all keys zero: uniform weights, the mean value row
+    np.testing.assert_allclose(dense_decode_unit(q, np.zeros((50, 128)), v), np.repeat(v.mean(0)[None], 2, 0),
+                               rtol=1e-13, atol=1e-14)
+    # empty context: zeros
+    assert not dense_decode_unit(q, np.zeros((0, 128)), np.zeros((0, 128))).any()
