@@ -29,7 +29,11 @@ import workloads as W  # noqa: E402
 HBM_PEAK_GBPS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 METRIC = "compressed decode-attn context tokens/s per layer; achieved HBM GB/s vs peak"
-KERNEL_SOURCES = ["kv_cache_compression_svd_amd/csrc/decode.hip", "kv_cache_compression_svd_amd/csrc/common.cuh"]
+# sources whose hash a counter summary in profiles/ must carry to be used (the kernel and its shared header)
+KERNEL_SOURCES = {
+    "score": ["kv_cache_compression_svd_amd/csrc/decode.hip", "kv_cache_compression_svd_amd/csrc/common.cuh"],
+    "dense_attend": ["kv_cache_compression_svd_amd/csrc/dense.hip", "kv_cache_compression_svd_amd/csrc/common.cuh"],
+}
 
 
 def parse():
@@ -44,18 +48,18 @@ def parse():
     return ap.parse_args()
 
 
-def source_hash() -> str:
+def source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
-    """HBM bytes per score launch from the committed rocprofv3 counter summary, when it was taken on the
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter summary, when it was taken on the
     current kernel source; otherwise None."""
-    path = os.path.join(ROOT, "profiles", f"score_{workload}_pmc.txt")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -63,7 +67,7 @@ def read_traffic(workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("source_sha256_16") != source_hash():
+    if vals.get("source_sha256_16") != source_hash(kernel):
         return None
     try:
         return float(vals["traffic_bytes_per_dispatch"])
@@ -204,6 +208,7 @@ def main():
                       "alg_bytes": dense_bytes, "attend_kernel_ms": d_attend_ms,
                       "attend_kernel_GBps": dense_bytes / (d_attend_ms * 1e-3) / 1e9,
                       "attend_kernel_frac_of_hbm_peak": dense_bytes / (d_attend_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                      "attend_kernel_traffic": read_traffic("dense_attend", args.workload),
                       "compressed_speedup": dms / ms}
 
     sel_np = sel.cpu().numpy()
@@ -226,7 +231,7 @@ def main():
     score_avg = score_ms / max(score_n, 1)
     score_alg = k_payload + 9 * S + w.batch * w.n_kv_heads * 128 * 4
     achieved = score_alg / (score_avg * 1e-3) / 1e9
-    traffic = read_traffic(args.workload)
+    traffic = read_traffic("score", args.workload)
 
     result = {
         "metric": METRIC,
