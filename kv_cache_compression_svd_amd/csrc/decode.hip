@@ -58,27 +58,27 @@ __device__ __forceinline__ int64_t key_base(const DecArgs& a, int r, int g, int 
 // =====================================================================================================
 // prep
 // =====================================================================================================
+// Four workgroups per stream, one per quarter of the 128 output channels: q' = q @ B_K and Qbar for 32
+// columns, a quarter of the stream's histogram cleared; the first workgroup also clears the selection state,
+// and workgroup 0 of the grid writes the uploaded table words.
 __global__ __launch_bounds__(256) void k_dec_prep(DecArgs a, Upload tab) {
-    __shared__ __attribute__((aligned(16))) float bs[MKV_D * MKV_D];
+    constexpr int QC = MKV_D / 4;                    // output columns per workgroup
+    __shared__ __attribute__((aligned(16))) float bs[MKV_D][QC];
     __shared__ float qs[MKV_MAX_GROUP_DEV][MKV_D];
-    __shared__ float qo[MKV_MAX_GROUP_DEV][MKV_D];
+    __shared__ float qo[MKV_MAX_GROUP_DEV][QC];
     const int tid = threadIdx.x;
     if (blockIdx.x == 0)
         for (int i = tid; i < tab.n; i += 256) tab.dst[i] = tab.w[i];
-    const int stream = blockIdx.x, r = stream / a.Hkv, g = stream - r * a.Hkv;
+    const int stream = blockIdx.x >> 2, qd = blockIdx.x & 3, r = stream / a.Hkv, g = stream - r * a.Hkv;
     const int G = a.G, Hq = a.G * a.Hkv;
-    u32x4* hz = reinterpret_cast<u32x4*>(a.hist + (size_t)stream * kHistBins);
-    for (int i = tid; i < kHistBins / 4; i += 256) hz[i] = u32x4{0u, 0u, 0u, 0u};
-    if (tid < kStateWords) a.state[stream * kStateWords + tid] = 0u;
     const float* Bk = a.basis ? a.basis + ((((size_t)r * a.Hkv + g) * 2) << 14) : nullptr;
-    if (Bk) {
-        const f32x4* src = reinterpret_cast<const f32x4*>(Bk);
-        f32x4* dst = reinterpret_cast<f32x4*>(bs);
-        f32x4 v[16];
+    f32x4 v[4];
+    if (Bk) {   // rows 0..127, columns [32 qd, 32 qd + 32): 1024 16-byte pieces, 4 per thread
 #pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = src[tid + 256 * j];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) dst[tid + 256 * j] = v[j];
+        for (int j = 0; j < 4; ++j) {
+            const int idx = tid + 256 * j, row = idx >> 3, c4 = idx & 7;
+            v[j] = *reinterpret_cast<const f32x4*>(Bk + row * MKV_D + QC * qd + 4 * c4);
+        }
     }
     for (int i = tid; i < G * MKV_D; i += 256) {
         const int h = i >> 7, c = i & 127;
@@ -86,30 +86,39 @@ __global__ __launch_bounds__(256) void k_dec_prep(DecArgs a, Upload tab) {
         qs[h][c] = a.dtype == 1 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qi])
                                 : reinterpret_cast<const float*>(a.q)[qi];
     }
+    reinterpret_cast<u32x4*>(a.hist + (size_t)stream * kHistBins + qd * (kHistBins / 4))[tid] = u32x4{0u, 0u, 0u, 0u};
+    if (qd == 0 && tid < kStateWords) a.state[stream * kStateWords + tid] = 0u;
+    if (Bk) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int idx = tid + 256 * j, row = idx >> 3, c4 = idx & 7;
+            *reinterpret_cast<f32x4*>(&bs[row][4 * c4]) = v[j];
+        }
+    }
     __syncthreads();
-    const int i = tid & 127;
-    for (int h = tid >> 7; h < G; h += 2) {
+    for (int o = tid; o < G * QC; o += 256) {
+        const int h = o / QC, col = o - h * QC;
         float acc;
         if (Bk) {
             acc = 0.f;
 #pragma unroll 8
-            for (int k = 0; k < MKV_D; ++k) acc = fmaf(qs[h][k], bs[k * MKV_D + i], acc);
+            for (int k = 0; k < MKV_D; ++k) acc = fmaf(qs[h][k], bs[k][col], acc);
         } else {
-            acc = qs[h][i];
+            acc = qs[h][QC * qd + col];
         }
-        qo[h][i] = acc;
-        a.qp[((size_t)r * Hq + g * G + h) * MKV_D + i] = acc;
+        qo[h][col] = acc;
+        a.qp[((size_t)r * Hq + g * G + h) * MKV_D + QC * qd + col] = acc;
     }
     __syncthreads();
-    if (tid < MKV_D) {
+    if (tid < QC) {
         float qb = 0.f;
         for (int h = 0; h < G; ++h) qb += qo[h][tid];
-        a.qbar[(size_t)stream * MKV_D + tid] = qb;
+        a.qbar[(size_t)stream * MKV_D + QC * qd + tid] = qb;
     }
 }
 
 hipError_t launch_dec_prep(const DecArgs& a, const Upload& tab, hipStream_t s) {
-    hipLaunchKernelGGL(k_dec_prep, dim3(a.B * a.Hkv), dim3(256), 0, s, a, tab);
+    hipLaunchKernelGGL(k_dec_prep, dim3(4 * a.B * a.Hkv), dim3(256), 0, s, a, tab);
     return hipGetLastError();
 }
 
@@ -389,6 +398,13 @@ __global__ __launch_bounds__(256) void k_sel_collect(DecArgs a) {
     const KBlock k = kblock(a);
     const int tid = threadIdx.x;
     const uint32_t T = (uint32_t)a.t_T[k.r];
+    // the block's keys do not depend on the threshold: their loads are issued first and overlap its search
+    const int lo = k.kb * kKeysPerBlock + 16 * tid;
+    const u32x4* keys4 = reinterpret_cast<const u32x4*>(a.keys + k.keybase);
+    const int last4 = (((k.n + 63) & ~63) >> 2) - 1;
+    u32x4 kv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) kv[q] = keys4[min((lo >> 2) + q, last4)];
     if (tid < 4) res[tid] = 0u;
     __syncthreads();
     if (tid < 64) find_threshold(a, k.stream, T, res);
@@ -396,14 +412,10 @@ __global__ __launch_bounds__(256) void k_sel_collect(DecArgs a) {
     const uint32_t p1 = res[0], ngt = res[1];
     uint32_t* st = a.state + k.stream * kStateWords;
     if (k.kb == 0 && tid < 4) st[ST_P1 + tid] = res[tid];
-    const int lo = k.kb * kKeysPerBlock + 16 * tid;
-    const u32x4* keys4 = reinterpret_cast<const u32x4*>(a.keys + k.keybase);
-    const int last4 = (((k.n + 63) & ~63) >> 2) - 1;
     uint32_t kk[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const u32x4 v = keys4[min((lo >> 2) + q, last4)];
-        kk[4 * q] = v.x; kk[4 * q + 1] = v.y; kk[4 * q + 2] = v.z; kk[4 * q + 3] = v.w;
+        kk[4 * q] = kv[q].x; kk[4 * q + 1] = kv[q].y; kk[4 * q + 2] = kv[q].z; kk[4 * q + 3] = kv[q].w;
     }
     uint32_t gm = 0, cm = 0;
 #pragma unroll
