@@ -211,6 +211,29 @@ def main():
                       "attend_kernel_traffic": read_traffic("dense_attend", args.workload),
                       "compressed_speedup": dms / ms}
 
+    # Gram matrices for basis refresh on the same inputs (an extra): bf16 only
+    gram_res = None
+    if w.dtype == "bf16":
+        gout = torch.empty((w.batch, w.n_kv_heads, 2, 128, 128), dtype=torch.float32, device=dev)
+        for _ in range(2):
+            mkv.mkv_gram(K, V, inp.cu_seqlens, out=gout)
+        torch.cuda.synchronize()
+        mkv.mkv_profile_start(kernels=["gram", "gram_reduce"])
+        g_reps = 5
+        t0 = time.perf_counter()
+        for _ in range(g_reps):
+            mkv.mkv_gram(K, V, inp.cu_seqlens, out=gout)
+        torch.cuda.synchronize()
+        gms = (time.perf_counter() - t0) * 1e3 / g_reps
+        gk = mkv.mkv_profile_stop()
+        g_kern_ms = gk["gram"][0] / max(gk["gram"][1], 1)
+        gram_flops = 2.0 * 2 * total_tokens * w.n_kv_heads * 128 * 128
+        gram_res = {"ms": gms, "gram_kernel_ms": g_kern_ms, "alg_bytes": dense,
+                    "gram_kernel_GBps": dense / (g_kern_ms * 1e-3) / 1e9,
+                    "gram_kernel_frac_of_hbm_peak": dense / (g_kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                    "gram_kernel_TFLOPs": gram_flops / (g_kern_ms * 1e-3) / 1e12,
+                    "reduce_ms": gk["gram_reduce"][0] / max(gk["gram_reduce"][1], 1)}
+
     sel_np = sel.cpu().numpy()
     # V payload actually gathered: rows of the selected tokens
     n = np.diff(inp.cu_seqlens)
@@ -268,6 +291,7 @@ def main():
                      "rotation_frac_of_bf16_mfma_peak": rot_flops / (compress_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
                      "kernels_avg_ms": {k: v[0] / max(v[1], 1) for k, v in c_kern.items()}},
         "dense_baseline": dense_base,
+        "gram": gram_res,
         "input_generation_s": t_gen,
     }
     if not args.no_cpu_baseline:

@@ -169,6 +169,18 @@ mkv_status mkv_dense_decode_workspace_bytes(const mkv_kv_desc* kv, int32_t n_q_h
 mkv_status mkv_dense_decode_attn(const mkv_kv_desc* kv, const void* q, int32_t n_q_heads, float* out, void* ws,
                                  size_t ws_bytes, mkv_stream_t stream);
 
+/* ---- basis refresh -----------------------------------------------------------------------------------------
+ * Gram matrices G = X^T X of every (request, KV head, tensor) stream X of bf16 K/V.  The pages rotate the KV
+ * cache by an SVD basis computed off the decoding path (section 1, Observation & Approach 1 and 2); the right
+ * singular vectors of X are the eigenvectors of G, so a caller refreshes a stream's basis by decomposing G
+ * (a 128 x 128 symmetric matrix) and ordering the eigenvectors by decreasing eigenvalue.
+ *   kv   bf16 only (MKV_E_UNSUPPORTED otherwise); K and V [dev] as in the descriptor.
+ *   gram [dev] float32 [batch][n_kv_heads][2][128][128] (K's matrix, then V's), 256-byte aligned, fully written;
+ *        an empty request gets zeros.  Products of bf16 values are exact; the sums are float32 (MFMA).
+ *   ws   [dev] >= mkv_gram_workspace_bytes, 256-byte aligned; contents are scratch. */
+mkv_status mkv_gram_workspace_bytes(const mkv_kv_desc* kv, size_t* ws_bytes);
+mkv_status mkv_gram(const mkv_kv_desc* kv, float* gram, void* ws, size_t ws_bytes, mkv_stream_t stream);
+
 /* Text of the last error on the calling thread; valid until the next call on that thread. */
 const char* mkv_last_error(void);
 

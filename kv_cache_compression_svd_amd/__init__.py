@@ -76,6 +76,8 @@ SIGNATURES = {
                                   c_void_p, c_size_t, c_void_p]),
     "mkv_dense_decode_workspace_bytes": (c_int32, [c_void_p, c_int32, POINTER(c_size_t)]),
     "mkv_dense_decode_attn": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "mkv_gram_workspace_bytes": (c_int32, [c_void_p, POINTER(c_size_t)]),
+    "mkv_gram": (c_int32, [c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "mkv_last_error": (c_char_p, []),
     "mkv_profile_start": (c_int32, [c_int32, c_uint32]),
     "mkv_profile_stop": (c_int32, [POINTER(c_double), POINTER(c_int32)]),
@@ -312,6 +314,32 @@ def mkv_dense_decode_attn(K, V, cu_seqlens, q, out=None, ws=None, stream=None):
     _check(lib().mkv_dense_decode_attn(byref(d), _ptr(q), int(Hq), _ptr(out), _ptr(ws), c_size_t(ws.numel()),
                                        _stream_ptr(stream)))
     return out
+
+
+def mkv_gram(K, V, cu_seqlens, out=None, ws=None, stream=None):
+    """X^T X (float32 [batch][n_kv_heads][2][128][128]) of every (request, KV head, tensor) stream of bf16 K, V."""
+    torch = _torch()
+    d, cu = _kv_desc(K, V, cu_seqlens)
+    if out is None:
+        out = torch.empty((d.batch, d.n_kv_heads, 2, HEAD_DIM, HEAD_DIM), dtype=torch.float32, device=K.device)
+    if ws is None:
+        v = c_size_t()
+        _check(lib().mkv_gram_workspace_bytes(byref(d), byref(v)))
+        ws = torch.empty(v.value, dtype=torch.uint8, device=K.device)
+    _check(lib().mkv_gram(byref(d), _ptr(out), _ptr(ws), c_size_t(ws.numel()), _stream_ptr(stream)))
+    return out
+
+
+def svd_basis_from_gram(gram):
+    """Rotation bases from Gram matrices (any [..., 128, 128] tensor or array): the eigenvectors by decreasing
+    eigenvalue, as float32 columns, computed in float64 on the host.  Returns a CPU float32 tensor."""
+    import numpy as np
+    torch = _torch()
+    g = gram.detach().cpu().numpy().astype(np.float64) if hasattr(gram, "detach") else np.asarray(gram, np.float64)
+    w, vecs = np.linalg.eigh(g)
+    order = np.argsort(-w, axis=-1, kind="stable")
+    vecs = np.take_along_axis(vecs, order[..., None, :], axis=-1)
+    return torch.from_numpy(np.ascontiguousarray(vecs.astype(np.float32)))
 
 
 def mkv_profile_start(max_launches: int = 1 << 20, kernels=None):

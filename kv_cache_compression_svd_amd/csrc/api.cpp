@@ -37,11 +37,11 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ---- kernel timing --------------------------------------------------------------------------------------
 enum KernelId {
     K_UPLOAD = 0, K_CMP_DECIDE, K_CMP_SCAN, K_CMP_PACK, K_DEC_PREP, K_SCORE, K_SEL_COLLECT, K_SEL_EMIT,
-    K_ATTEND, K_COMBINE, K_DENSE_ATTEND, K_DENSE_COMBINE, K_COUNT
+    K_ATTEND, K_COMBINE, K_DENSE_ATTEND, K_DENSE_COMBINE, K_GRAM, K_GRAM_REDUCE, K_COUNT
 };
 const char* kKernelNames[K_COUNT] = {"upload", "compress_decide", "compress_scan", "compress_pack", "decode_prep",
                                      "score", "select_collect", "select_emit", "attend", "combine",
-                                     "dense_attend", "dense_combine"};
+                                     "dense_attend", "dense_combine", "gram", "gram_reduce"};
 
 struct Profiler {
     std::mutex mu;
@@ -604,6 +604,78 @@ mkv_status mkv_dense_decode_attn(const mkv_kv_desc* kv, const void* q, int32_t n
     a.part = d.part;
     a.achunk = kDenseChunk;
     if ((st = run(K_DENSE_COMBINE, stream, [&] { return launch_combine(a, B * sh.Hkv, stream); }))) return st;
+    return MKV_OK;
+}
+
+// ---- Gram matrices for basis refresh ----------------------------------------------------------------------
+namespace {
+
+struct GramPlan {
+    std::vector<int32_t> tab;    // n | tok0 | first workgroup [B+1]
+    int64_t n_blk = 0;
+    uint64_t o_tab = 0, o_part = 0, bytes = 0;
+};
+
+mkv_status plan_gram(const mkv_kv_desc* kv, bool need_data, Shape* sh, GramPlan* P) {
+    mkv_status st = check_kv(kv, need_data, sh);
+    if (st) return st;
+    if (sh->dtype != MKV_BF16) return fail(MKV_E_UNSUPPORTED, "the Gram matrices take bf16 K/V only");
+    const int B = sh->B;
+    P->tab.assign(3 * B + 1, 0);
+    int64_t blk = 0;
+    for (int r = 0; r < B; ++r) {
+        const int64_t n = sh->cu[r + 1] - sh->cu[r];
+        P->tab[r] = (int32_t)n;
+        P->tab[B + r] = (int32_t)sh->cu[r];
+        P->tab[2 * B + r] = (int32_t)blk;
+        blk += 2ll * sh->Hkv * cdiv(n, kGramChunk);
+    }
+    P->tab[3 * B] = (int32_t)blk;
+    if (blk > INT32_MAX || 32ll * B * sh->Hkv > INT32_MAX) return fail(MKV_E_UNSUPPORTED, "too many workgroups");
+    P->n_blk = blk;
+    P->o_part = align_up(4 * P->tab.size());
+    P->bytes = align_up(P->o_part + 4ull * MKV_HEAD_DIM * MKV_HEAD_DIM * std::max<int64_t>(blk, 1));
+    return MKV_OK;
+}
+
+}  // namespace
+
+mkv_status mkv_gram_workspace_bytes(const mkv_kv_desc* kv, size_t* ws_bytes) {
+    Shape sh;
+    GramPlan P;
+    mkv_status st = plan_gram(kv, false, &sh, &P);
+    if (st) return st;
+    if (!ws_bytes) return fail(MKV_E_ARG, "ws_bytes is NULL");
+    *ws_bytes = P.bytes;
+    return MKV_OK;
+}
+
+mkv_status mkv_gram(const mkv_kv_desc* kv, float* gram, void* ws, size_t ws_bytes, mkv_stream_t stream_) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    Shape sh;
+    GramPlan P;
+    mkv_status st = plan_gram(kv, true, &sh, &P);
+    if (st) return st;
+    if (!gram) return fail(MKV_E_ARG, "gram is NULL");
+    if (!ws) return fail(MKV_E_ARG, "ws is NULL");
+    if (!aligned(ws) || !aligned(gram)) return fail(MKV_E_ARG, "ws and gram must be 256-byte aligned");
+    if (ws_bytes < P.bytes) return fail(MKV_E_ARG, "ws_bytes %zu < required %llu", ws_bytes, (unsigned long long)P.bytes);
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    int32_t* tb = reinterpret_cast<int32_t*>(w + P.o_tab);
+    if ((st = upload_words(tb, P.tab, 0, stream))) return st;
+    const int B = sh.B;
+    GramArgs g;
+    g.B = B;
+    g.Hkv = sh.Hkv;
+    g.K = static_cast<const uint16_t*>(kv->K);
+    g.V = static_cast<const uint16_t*>(kv->V);
+    g.t_n = tb;
+    g.t_tok0 = tb + B;
+    g.t_gblk = tb + 2 * B;
+    g.part = reinterpret_cast<float*>(w + P.o_part);
+    g.gram = gram;
+    if ((st = run(K_GRAM, stream, [&] { return launch_gram(g, (int)P.n_blk, stream); }))) return st;
+    if ((st = run(K_GRAM_REDUCE, stream, [&] { return launch_gram_reduce(g, stream); }))) return st;
     return MKV_OK;
 }
 

@@ -12,6 +12,7 @@ constexpr int kCoarseOff = 64;          // coarse histogram (top 6 key bits) ins
 constexpr int kKeysPerBlock = 4096;     // keys per workgroup in the selection passes
 constexpr int kAttnChunk = 256;         // selected tokens per attention workgroup
 constexpr int kDenseChunk = 512;        // tokens per workgroup of the uncompressed baseline
+constexpr int kGramChunk = 16384;       // tokens per workgroup of the Gram matrices
 
 // selection state words
 enum { ST_P1 = 1, ST_NGT = 2, ST_NCAND = 3, ST_NEED = 4, ST_GTFILL = 5, ST_CFILL = 6 };
@@ -101,5 +102,20 @@ struct DenseArgs {
 };
 
 hipError_t launch_dense_attend(const DenseArgs& a, int n_blocks, hipStream_t s);
+
+// ---- Gram matrices for basis refresh --------------------------------------------------------------------
+struct GramArgs {
+    int32_t B, Hkv;
+    const uint16_t* K;          // bf16 [tokens][Hkv][128]
+    const uint16_t* V;
+    const int32_t* t_n;         // per request: context
+    const int32_t* t_tok0;      // per request: first token
+    const int32_t* t_gblk;      // [B+1] first workgroup of each request (Hkv * 2 * chunks per request)
+    float* part;                // [blocks][128][128] per-chunk partials
+    float* gram;                // [B][Hkv][2][128][128]
+};
+
+hipError_t launch_gram(const GramArgs& a, int n_blocks, hipStream_t s);
+hipError_t launch_gram_reduce(const GramArgs& a, hipStream_t s);
 
 }  // namespace mkv

@@ -26,3 +26,4 @@ from .compress import (Policy, DEFAULT_POLICY, Stream, rotate_round, channel_ord
 from .decode import (rotate_queries, scores, select_top, attend, decode_unit, decode_all,  # noqa: F401
                      dense_decode_unit)
 from .sizes import stream_payload_bytes, store_payload_bytes, dense_kv_bytes, segment_meta_bytes  # noqa: F401
+from .basis import gram, gram_abs  # noqa: F401

@@ -210,3 +210,26 @@ def test_dense_baseline_special_cases():
                                rtol=1e-13, atol=1e-14)
     # empty context: zeros
     assert not dense_decode_unit(q, np.zeros((0, 128)), np.zeros((0, 128))).any()
+
+
+def test_gram_against_outer_products_and_invariants():
+    from oracle import gram, gram_abs
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((37, 128))
+    g = gram(x)
+    brute = np.zeros((128, 128))
+    for t in range(x.shape[0]):
+        for i in range(128):
+            brute[i] += x[t, i] * x[t]
+    np.testing.assert_allclose(g, brute, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(g, g.T)
+    assert abs(np.trace(g) - np.sum(x * x)) <= 1e-10 * np.sum(x * x)
+    assert np.linalg.eigvalsh(g).min() > -1e-9                      # positive semi-definite
+    q, _ = np.linalg.qr(rng.standard_normal((128, 128)))             # orthonormal rows: G = I
+    np.testing.assert_allclose(gram(q), np.eye(128), atol=1e-12)
+    assert np.all(gram_abs(x) >= np.abs(g) - 1e-12)
+    # the eigenvectors of X^T X by decreasing eigenvalue are the right singular vectors of X
+    w, v = np.linalg.eigh(g)
+    _, sv, vt = np.linalg.svd(x, full_matrices=True)
+    np.testing.assert_allclose(np.sqrt(np.maximum(w[::-1][:37], 0)), sv, rtol=1e-9)
+    np.testing.assert_allclose(np.abs(v[:, ::-1][:, :37].T @ vt[:37].T), np.eye(37), atol=1e-7)
