@@ -33,6 +33,7 @@ METRIC = "compressed decode-attn context tokens/s per layer; achieved HBM GB/s v
 KERNEL_SOURCES = {
     "score": ["kv_cache_compression_svd_amd/csrc/decode.hip", "kv_cache_compression_svd_amd/csrc/common.cuh"],
     "dense_attend": ["kv_cache_compression_svd_amd/csrc/dense.hip", "kv_cache_compression_svd_amd/csrc/common.cuh"],
+    "gram": ["kv_cache_compression_svd_amd/csrc/gram.hip", "kv_cache_compression_svd_amd/csrc/common.cuh"],
 }
 
 
@@ -232,6 +233,7 @@ def main():
                     "gram_kernel_GBps": dense / (g_kern_ms * 1e-3) / 1e9,
                     "gram_kernel_frac_of_hbm_peak": dense / (g_kern_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                     "gram_kernel_TFLOPs": gram_flops / (g_kern_ms * 1e-3) / 1e12,
+                    "gram_kernel_traffic": read_traffic("gram", args.workload),
                     "reduce_ms": gk["gram_reduce"][0] / max(gk["gram_reduce"][1], 1)}
 
     sel_np = sel.cpu().numpy()
