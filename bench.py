@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workers", type=int, default=min(16, os.cpu_count() or 1))
+    ap.add_argument("--no-layers", dest="layers", action="store_false",
+                    help="skip the layer-batched extra (32 layers x 32768 tokens in one call)")
     return ap.parse_args()
 
 
@@ -104,6 +106,11 @@ def main():
     t_gen = time.time()
     inp = W.generate(w, basis="svd", workers=args.workers)
     t_gen = time.time() - t_gen
+    # layer-batched extra: the 32 layers of a Llama-3.1-8B-shaped model at 32768 tokens as one store (generated
+    # here, before the GPU is touched, like the main inputs)
+    lw = W.Workload("llama_32_layers", 32, 32, 8, (32768,) * 32, "bf16", (2048,) * 32, "per_request", 50,
+                    "the 32 layers of one 32768-token request, one store")
+    linp = W.generate(lw, basis="svd", workers=args.workers) if args.layers else None
 
     import torch
     import kv_cache_compression_svd_amd as mkv
@@ -236,6 +243,8 @@ def main():
                     "gram_kernel_traffic": read_traffic("gram", args.workload),
                     "reduce_ms": gk["gram_reduce"][0] / max(gk["gram_reduce"][1], 1)}
 
+    layer_res = layer_batched(mkv, torch, dev, linp, args) if linp is not None else None
+
     sel_np = sel.cpu().numpy()
     # V payload actually gathered: rows of the selected tokens
     n = np.diff(inp.cu_seqlens)
@@ -294,11 +303,47 @@ def main():
                      "kernels_avg_ms": {k: v[0] / max(v[1], 1) for k, v in c_kern.items()}},
         "dense_baseline": dense_base,
         "gram": gram_res,
+        "layer_batched": layer_res,
         "input_generation_s": t_gen,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def layer_batched(mkv, torch, dev, linp, args):
+    """All layers of one request decoded by one call (the layers are the store's requests) against one call
+    for a single layer: the batched call amortises launches and fills the GPU."""
+    from _helpers import inputs_to_torch
+    lw = linp.workload
+    n = lw.ctx[0]
+    K, V, q, basis = inputs_to_torch(linp, dev)
+    store = mkv.mkv_compress(K, V, linp.cu_seqlens, basis)
+    one = mkv.mkv_compress(K[:n].contiguous(), V[:n].contiguous(), linp.cu_seqlens[:2], basis[:1].contiguous())
+    q1 = q[:1].contiguous()
+    del K, V
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / args.steps
+
+    out = torch.empty((lw.batch, lw.n_q_heads, 128), dtype=torch.float32, device=dev)
+    ws = torch.empty(mkv.mkv_decode_workspace_bytes(store, lw.n_q_heads, linp.T), dtype=torch.uint8, device=dev)
+    out1 = torch.empty((1, lw.n_q_heads, 128), dtype=torch.float32, device=dev)
+    ws1 = torch.empty(mkv.mkv_decode_workspace_bytes(one, lw.n_q_heads, linp.T[:1]), dtype=torch.uint8, device=dev)
+    ms_all = timed(lambda: mkv.mkv_decode_attn(store, q, linp.T, out=out, ws=ws, return_sel=False))
+    ms_one = timed(lambda: mkv.mkv_decode_attn(one, q1, linp.T[:1], out=out1, ws=ws1, return_sel=False))
+    return {"layers": lw.batch, "context": n, "T": int(linp.T[0]), "ms_one_layer_one_call": ms_one,
+            "ms_all_layers_one_call": ms_all, "ms_per_layer_batched": ms_all / lw.batch,
+            "speedup_vs_one_call_per_layer": lw.batch * ms_one / ms_all,
+            "context_tokens_per_s_batched": lw.batch * n / (ms_all * 1e-3),
+            "context_tokens_per_s_one_layer": n / (ms_one * 1e-3)}
 
 
 def cpu_baseline(inp, seconds: float):
