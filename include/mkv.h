@@ -94,8 +94,9 @@ mkv_status mkv_compress_bytes(const mkv_kv_desc* kv, const mkv_seg_policy* polic
  *   `stream`; decode calls enqueued after it on the same stream see the finished store.
  * Store layout (all offsets from store_buf, see mkv_store_view): a segment is 64 consecutive tokens of one
  * (request r, KV head h, tensor X) stream from token 0 on, the last one shorter when n_r % 64 != 0.  Segments
- * are numbered X*S + n_kv_heads*seg_base[r] + h*S_r + s with S_r = ceil(n_r/64), seg_base[r] = sum_{r'<r} S_r',
- * S = n_kv_heads * sum_r S_r.  Segment g has a uint8 code (index into policy.keep, c = keep[code]) and a uint64
+ * are numbered X*S + n_kv_heads*seg_base[r] + h*S_r + s with S_r = ceil(cap_r/64), seg_base[r] = sum_{r'<r} S_r',
+ * S = n_kv_heads * sum_r S_r, where cap_r is request r's token capacity (its context n_r, unless the store is
+ * growable; slots past the context are unused).  Segment g has a uint8 code (index into policy.keep, c = keep[code]) and a uint64
  * byte offset into the payload; its payload is [n_s][c] values of the storage dtype, followed, when c < 128, by
  * [n_s][c] uint8 channel indices; each token's channels are in ascending order and values follow that order. */
 mkv_status mkv_compress(const mkv_kv_desc* kv, const float* basis, const mkv_seg_policy* policy,
@@ -123,6 +124,9 @@ typedef struct {
     void* payload_total;         /* [dev] uint64: payload bytes in use, written by mkv_compress */
     uint64_t payload_capacity;   /* bytes available at payload */
     uint64_t store_bytes;        /* bytes of the whole store buffer */
+    const int64_t* cu_capacity;  /* [host] [batch+1] prefix sums of the token capacities; segment slots follow
+                                    them (equal to cu_seqlens unless the store is growable) */
+    int32_t growable;            /* built with mkv_compress_growable: accepts mkv_append */
 } mkv_store_info;
 
 /* Device addresses and host metadata of a store (for tests, export, and custom consumers). */

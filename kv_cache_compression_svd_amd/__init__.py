@@ -57,7 +57,8 @@ class StoreInfo(ctypes.Structure):
                 ("policy", SegPolicy), ("has_basis", c_int32), ("total_tokens", c_int64),
                 ("segments_per_tensor", c_int64), ("cu_seqlens", POINTER(c_int64)), ("codes", c_void_p),
                 ("seg_off", c_void_p), ("basis", c_void_p), ("payload", c_void_p), ("payload_total", c_void_p),
-                ("payload_capacity", c_uint64), ("store_bytes", c_uint64)]
+                ("payload_capacity", c_uint64), ("store_bytes", c_uint64), ("cu_capacity", POINTER(c_int64)),
+                ("growable", c_int32)]
 
 
 # Every symbol include/mkv.h declares, with its ctypes signature.

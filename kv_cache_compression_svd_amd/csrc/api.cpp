@@ -124,11 +124,41 @@ mkv_status check_policy(const mkv_seg_policy* p, mkv_dtype dt) {
 struct Shape {
     int32_t B = 0, Hkv = 0;
     mkv_dtype dtype = MKV_BF16;
-    std::vector<int64_t> cu;
+    std::vector<int64_t> cu;       // current tokens: prefix sums
     int64_t total = 0;
-    int64_t S = 0;                 // segments per tensor
-    std::vector<int32_t> segbase;  // per request
+    // Segment slots come from the capacities (the current contexts unless the store is growable), so that
+    // appended tokens never move another stream's slots.
+    std::vector<int64_t> cap;      // per request: token capacity (>= its context)
+    std::vector<int32_t> scap;     // per request: segment slots per stream, ceil(cap / 64)
+    std::vector<int32_t> segbase;  // per request: slots of the earlier requests (per KV head)
+    int64_t total_cap = 0;
+    int64_t S = 0;                 // segment slots per tensor
+    bool growable = false;
 };
+
+// Segment slots from capacities (cap NULL: the current contexts).
+mkv_status set_capacity(Shape* sh, const int64_t* cap) {
+    sh->cap.resize(sh->B);
+    sh->scap.resize(sh->B);
+    sh->segbase.resize(sh->B);
+    int64_t segs = 0, tot = 0;
+    for (int r = 0; r < sh->B; ++r) {
+        const int64_t n = sh->cu[r + 1] - sh->cu[r];
+        const int64_t c = cap ? cap[r] : n;
+        if (c < n) return fail(MKV_E_ARG, "capacity[%d] = %lld is below its context %lld", r, (long long)c, (long long)n);
+        sh->cap[r] = c;
+        sh->scap[r] = (int32_t)cdiv(c, MKV_SEG_LEN);
+        sh->segbase[r] = (int32_t)segs;
+        segs += sh->scap[r];
+        tot += c;
+    }
+    if (tot * (int64_t)sh->Hkv >= (int64_t)INT32_MAX)
+        return fail(MKV_E_UNSUPPORTED, "capacity tokens x KV heads must stay below 2^31 (got %lld)", (long long)(tot * sh->Hkv));
+    sh->total_cap = tot;
+    sh->S = segs * sh->Hkv;
+    sh->growable = cap != nullptr;
+    return MKV_OK;
+}
 
 mkv_status check_kv(const mkv_kv_desc* kv, bool need_data, Shape* sh) {
     if (!kv) return fail(MKV_E_ARG, "kv descriptor is NULL");
@@ -142,34 +172,35 @@ mkv_status check_kv(const mkv_kv_desc* kv, bool need_data, Shape* sh) {
     sh->Hkv = kv->n_kv_heads;
     sh->dtype = kv->dtype;
     sh->cu.assign(kv->cu_seqlens, kv->cu_seqlens + kv->batch + 1);
-    sh->segbase.resize(kv->batch);
-    int64_t segs = 0;
-    for (int r = 0; r < kv->batch; ++r) {
-        const int64_t n = sh->cu[r + 1] - sh->cu[r];
-        if (n < 0) return fail(MKV_E_ARG, "cu_seqlens must be non-decreasing (request %d)", r);
-        sh->segbase[r] = (int32_t)segs;
-        segs += cdiv(n, MKV_SEG_LEN);
-    }
+    for (int r = 0; r < kv->batch; ++r)
+        if (sh->cu[r + 1] < sh->cu[r]) return fail(MKV_E_ARG, "cu_seqlens must be non-decreasing (request %d)", r);
     sh->total = sh->cu[kv->batch];
     if (sh->total * (int64_t)sh->Hkv >= (int64_t)INT32_MAX)
         return fail(MKV_E_UNSUPPORTED, "total tokens x KV heads must stay below 2^31 (got %lld)", (long long)(sh->total * sh->Hkv));
-    sh->S = segs * sh->Hkv;
     if (need_data && sh->total > 0 && (!kv->K || !kv->V)) return fail(MKV_E_ARG, "K and V must be non-NULL");
-    return MKV_OK;
+    return set_capacity(sh, nullptr);
 }
 
 struct StoreLayout {
-    uint64_t codes, seg_off, basis, payload, capacity, bytes;
+    uint64_t codes, seg_off, basis, payload, capacity;
+    uint64_t open_pack, open_rows, open_bytes;   // growable stores: per-stream open-segment areas (0 otherwise)
+    uint64_t bytes;
 };
 
+// Depends on the capacities only (never on the current contexts), so appends keep every offset.
 StoreLayout store_layout(const Shape& sh) {
     StoreLayout L;
     L.codes = kAlign;   // first 256 bytes: header (payload bytes in use)
     L.seg_off = align_up(L.codes + 2 * (uint64_t)sh.S);
     L.basis = align_up(L.seg_off + 16 * (uint64_t)sh.S);
     L.payload = align_up(L.basis + (uint64_t)sh.B * sh.Hkv * 2 * MKV_HEAD_DIM * MKV_HEAD_DIM * sizeof(float));
-    L.capacity = 2ull * sh.Hkv * (uint64_t)sh.total * MKV_HEAD_DIM * dtype_bytes(sh.dtype);
-    L.bytes = L.payload + L.capacity + kAlign;   // slack: fixed-shape row loads may read past the last row
+    L.capacity = 2ull * sh.Hkv * (uint64_t)sh.total_cap * MKV_HEAD_DIM * dtype_bytes(sh.dtype);
+    // an open segment holds at most 64 rows, packed or raw: 64 * 128 values
+    L.open_bytes = sh.growable ? (uint64_t)MKV_SEG_LEN * MKV_HEAD_DIM * dtype_bytes(sh.dtype) : 0;
+    const uint64_t streams = 2ull * sh.B * sh.Hkv;
+    L.open_pack = L.payload + L.capacity;          // packed open segments, addressed like payload (seg_off)
+    L.open_rows = L.open_pack + streams * L.open_bytes;
+    L.bytes = L.open_rows + streams * L.open_bytes + kAlign;   // slack: fixed-shape row loads may read past
     return L;
 }
 
@@ -192,7 +223,7 @@ struct ScratchLayout {
 ScratchLayout scratch_layout(const Shape& sh) {
     ScratchLayout L;
     L.tab = 0;
-    L.thr = align_up(sizeof(int32_t) * (4ull * sh.B + 1));
+    L.thr = align_up(sizeof(int32_t) * (5ull * sh.B + 1));
     L.wg = align_up(L.thr + 2ull * sh.total * sh.Hkv * 4 * sizeof(uint16_t));
     L.bytes = L.wg + 2ull * std::max<int64_t>(cmp_plan(sh).nblk, 1) * sizeof(uint64_t);
     return L;
@@ -208,6 +239,7 @@ struct mkv_store {
     int32_t has_basis = 0;
     StoreLayout lay;
     uint8_t* base = nullptr;
+    std::vector<int64_t> cu_cap;   // prefix sums of the capacities (for mkv_store_view)
 };
 
 // ======================================================================================================
@@ -247,6 +279,8 @@ static mkv_status make_handle(const Shape& sh, const mkv_seg_policy* policy, int
     h->has_basis = has_basis;
     h->lay = store_layout(sh);
     h->base = static_cast<uint8_t*>(buf);
+    h->cu_cap.assign(1, 0);
+    for (int r = 0; r < sh.B; ++r) h->cu_cap.push_back(h->cu_cap.back() + sh.cap[r]);
     *out = h;
     return MKV_OK;
 }
@@ -270,17 +304,18 @@ mkv_status mkv_compress(const mkv_kv_desc* kv, const float* basis, const mkv_seg
     uint8_t* base = static_cast<uint8_t*>(store_buf);
     uint8_t* scr = static_cast<uint8_t*>(scratch);
     const int64_t spw = cmp_plan(sh).spw;
-    std::vector<int32_t> tab(4 * sh.B + 1);
+    std::vector<int32_t> tab(5 * sh.B + 1);
     int64_t nblk = 0;
     for (int r = 0; r < sh.B; ++r) {
         const int64_t n = sh.cu[r + 1] - sh.cu[r];
         tab[r] = (int32_t)sh.cu[r];
         tab[sh.B + r] = (int32_t)n;
         tab[2 * sh.B + r] = sh.segbase[r];
-        tab[3 * sh.B + r] = (int32_t)nblk;
+        tab[3 * sh.B + r] = sh.scap[r];
+        tab[4 * sh.B + r] = (int32_t)nblk;
         nblk += (int64_t)sh.Hkv * cdiv(cdiv(n, MKV_SEG_LEN), spw);
     }
-    tab[4 * sh.B] = (int32_t)nblk;
+    tab[5 * sh.B] = (int32_t)nblk;
     if (2 * nblk > INT32_MAX) return fail(MKV_E_UNSUPPORTED, "too many workgroups");
 
     if ((st = upload_words(reinterpret_cast<int32_t*>(scr + SL.tab), tab, 0, stream))) return st;
@@ -351,6 +386,8 @@ mkv_status mkv_store_view(const mkv_store* s, mkv_store_info* info) {
     info->payload_total = s->base;
     info->payload_capacity = s->lay.capacity;
     info->store_bytes = s->lay.bytes;
+    info->cu_capacity = s->cu_cap.data();
+    info->growable = s->sh.growable ? 1 : 0;
     return MKV_OK;
 }
 
@@ -388,11 +425,14 @@ mkv_status plan_decode(const mkv_store* s, int32_t n_q_heads, const int32_t* T, 
     const int B = sh.B;
     // segments per score workgroup, a multiple of 4 (one segment per wave at a time): about 16K workgroups for
     // long contexts
-    P->spw = (int32_t)(std::max<int64_t>(4, std::min<int64_t>(16, sh.S / 16384)) & ~3ll);
-    P->tab.assign(6 * B + 2, 0);
+    int64_t s_cur = 0;   // segments in use (the capacity may hold more)
+    for (int r = 0; r < B; ++r) s_cur += (int64_t)sh.Hkv * cdiv(sh.cu[r + 1] - sh.cu[r], MKV_SEG_LEN);
+    P->spw = (int32_t)(std::max<int64_t>(4, std::min<int64_t>(16, s_cur / 16384)) & ~3ll);
+    P->tab.assign(7 * B + 2, 0);
     int32_t* tn = P->tab.data();
     int32_t* tseg = tn + B;
-    int32_t* ttok = tseg + B;
+    int32_t* tscap = tseg + B;
+    int32_t* ttok = tscap + B;
     int32_t* tT = ttok + B;
     int32_t* tkb = tT + B;
     int32_t* tab_ = tkb + B + 1;
@@ -403,6 +443,7 @@ mkv_status plan_decode(const mkv_store* s, int32_t n_q_heads, const int32_t* T, 
         const int64_t te = std::min<int64_t>(T[r], n);
         tn[r] = (int32_t)n;
         tseg[r] = sh.segbase[r];
+        tscap[r] = sh.scap[r];
         ttok[r] = (int32_t)kpad;          // keys of request r start at Hkv * (earlier contexts padded to 64)
         kpad += cdiv(n, 64) * 64;
         tT[r] = (int32_t)te;
@@ -481,10 +522,11 @@ mkv_status mkv_decode_attn(const mkv_store* s, const void* q, int32_t n_q_heads,
     const int32_t* tb = reinterpret_cast<const int32_t*>(w + P.o_tab);
     a.t_n = tb;
     a.t_segbase = tb + sh.B;
-    a.t_tokbase = tb + 2 * sh.B;
-    a.t_T = tb + 3 * sh.B;
-    a.t_kblk = tb + 4 * sh.B;
-    a.t_ablk = tb + 5 * sh.B + 1;
+    a.t_scap = tb + 2 * sh.B;
+    a.t_tokbase = tb + 3 * sh.B;
+    a.t_T = tb + 4 * sh.B;
+    a.t_kblk = tb + 5 * sh.B;
+    a.t_ablk = tb + 6 * sh.B + 1;
     a.spw = P.spw;
     a.sgx = P.sgx;
     a.qp = reinterpret_cast<float*>(w + P.o_qp);

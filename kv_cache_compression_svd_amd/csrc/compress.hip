@@ -37,7 +37,8 @@ __device__ __forceinline__ Tile cmp_tile(const CmpArgs& a) {
     const int32_t* tokbase = a.tab;
     const int32_t* nn = a.tab + a.B;
     const int32_t* segbase = a.tab + 2 * a.B;
-    const int32_t* cblk = a.tab + 3 * a.B;
+    const int32_t* scap = a.tab + 3 * a.B;
+    const int32_t* cblk = a.tab + 4 * a.B;
     Tile t;
     t.X = blockIdx.x / a.nblk;
     const int b = blockIdx.x - t.X * a.nblk;
@@ -51,7 +52,7 @@ __device__ __forceinline__ Tile cmp_tile(const CmpArgs& a) {
     t.s0 = chunk * a.spw;
     t.s1 = min(Sr, t.s0 + a.spw);
     t.tok0 = tokbase[t.r];
-    t.seg0 = (int64_t)t.X * a.S + (int64_t)a.Hkv * segbase[t.r] + (int64_t)t.h * Sr;
+    t.seg0 = (int64_t)t.X * a.S + (int64_t)a.Hkv * segbase[t.r] + (int64_t)t.h * scap[t.r];
     return t;
 }
 

@@ -258,7 +258,7 @@ __global__ __launch_bounds__(256) void k_score(DecArgs a) {
     const int n = a.t_n[r], Sr = (n + MKV_SEG - 1) / MKV_SEG, gs = (Sr + a.spw - 1) / a.spw;
     if (i >= gs) return;                        // whole workgroup, before any barrier
     const int stride = 4 * gs;
-    const int64_t seg0 = (int64_t)a.Hkv * a.t_segbase[r] + (int64_t)g * Sr;
+    const int64_t seg0 = (int64_t)a.Hkv * a.t_segbase[r] + (int64_t)g * a.t_scap[r];
     const int64_t keybase = key_base(a, r, g, n);
     const int tid = threadIdx.x;
     int nloc = 0;                               // valid slots form a prefix of [0, spw)
@@ -814,7 +814,7 @@ __global__ __launch_bounds__(256) void k_attend(DecArgs a) {
     __shared__ __attribute__((aligned(16))) AttnLds<G> L;
     const int b = blockIdx.x;
     const int r = find_slot(a.t_ablk, a.B, b);
-    const int n = a.t_n[r], T = a.t_T[r], Sr = (n + MKV_SEG - 1) / MKV_SEG;
+    const int n = a.t_n[r], T = a.t_T[r];
     const int nach = (T + kAttnChunk - 1) / kAttnChunk;
     const int local = b - a.t_ablk[r];
     const int g = local / nach, chunk = local - g * nach;
@@ -833,7 +833,7 @@ __global__ __launch_bounds__(256) void k_attend(DecArgs a) {
         RowMeta k_{0, 0}, v_{0, 0};
         if (j >= 0) {
             const int s = j >> 6, tt = j & 63, ns = min(MKV_SEG, n - s * MKV_SEG);
-            const int64_t gk = (int64_t)a.Hkv * a.t_segbase[r] + (int64_t)g * Sr + s, gv = a.S + gk;
+            const int64_t gk = (int64_t)a.Hkv * a.t_segbase[r] + (int64_t)g * a.t_scap[r] + s, gv = a.S + gk;
             const int ck = a.keep[a.codes[gk]], cv = a.keep[a.codes[gv]];
             const uint64_t ok_ = a.seg_off[gk], ov = a.seg_off[gv];
             const int lck = 31 - __clz(ck), lcv = 31 - __clz(cv);

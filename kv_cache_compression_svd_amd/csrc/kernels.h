@@ -28,7 +28,7 @@ struct CmpArgs {
     const void* K;
     const void* V;
     const float* basis;         // [B][Hkv][2][128][128] or null (inputs already rotated)
-    const int32_t* tab;         // tok_base[B] | n[B] | seg_base[B] | cblk_base[B+1]
+    const int32_t* tab;         // tok_base[B] | n[B] | seg_base[B] | slots per stream[B] | cblk_base[B+1]
     int32_t B, Hkv, spw, nblk;  // spw: segments per workgroup; nblk: workgroups per tensor
     int64_t S;                  // segments per tensor
     int64_t total_tokens;
@@ -62,10 +62,11 @@ struct DecArgs {
     int32_t sel_stride;
     int32_t* sel_int;           // internal selection lists [B*Hkv][sel_int_stride]
     int32_t sel_int_stride;
-    // per-request tables (device): n | seg_base | key base (sum of earlier contexts padded to 64 tokens) |
-    // T_eff | kblk_base | ablk_base
+    // per-request tables (device): n | seg_base | segment slots per stream | key base (sum of earlier contexts
+    // padded to 64 tokens) | T_eff | kblk_base | ablk_base
     const int32_t* t_n;
     const int32_t* t_segbase;
+    const int32_t* t_scap;
     const int32_t* t_tokbase;
     const int32_t* t_T;
     const int32_t* t_kblk;

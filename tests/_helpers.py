@@ -78,14 +78,16 @@ def _parse_segment(payload: np.ndarray, off: int, ns: int, c: int, dtype: str):
     return idx, v
 
 
-def _stream_from(payload, codes, seg_off, pay_base, keep, r, h, X, S, Hkv, cu, dtype) -> Stream:
-    n, S_r, seg_base = seg_counts(cu)
+def _stream_from(payload, codes, seg_off, pay_base, keep, r, h, X, S, Hkv, cu, dtype, cu_cap=None) -> Stream:
+    """Stream (r, h, X) of a store: cu gives the tokens in use, cu_cap the capacities the segment slots follow."""
+    n, S_use, _ = seg_counts(cu)
+    _, S_r, seg_base = seg_counts(cu if cu_cap is None else cu_cap)
     nr = int(n[r])
     mask = np.zeros((nr, D), dtype=bool)
     vals = np.zeros((nr, D))
-    cs = np.zeros(int(S_r[r]), dtype=np.int64)
-    cds = np.zeros(int(S_r[r]), dtype=np.int64)
-    for s in range(int(S_r[r])):
+    cs = np.zeros(int(S_use[r]), dtype=np.int64)
+    cds = np.zeros(int(S_use[r]), dtype=np.int64)
+    for s in range(int(S_use[r])):
         g = segment_id(X, r, h, s, S, Hkv, seg_base, S_r)
         code = int(codes[g])
         c = keep[code]
@@ -112,14 +114,16 @@ def read_store(store, dtype: str) -> dict:
     codes = buf[o_codes:o_codes + 2 * S].copy()
     seg_off = buf[o_off:o_off + 16 * S].view(np.uint64).copy()
     total = int(buf[0:8].view(np.uint64)[0])
-    payload = buf[o_pay:o_pay + total]
-    cu = store.cu
+    payload = buf[o_pay:]          # packed segments, then (growable stores) the open-segment areas
+    B = int(info.batch)
+    cu = np.array([info.cu_seqlens[i] for i in range(B + 1)], dtype=np.int64)
+    cu_cap = np.array([info.cu_capacity[i] for i in range(B + 1)], dtype=np.int64)
     n, _, _ = seg_counts(cu)
     out = {}
     for r in range(len(n)):
         for h in range(Hkv):
             for X in (0, 1):
-                out[(r, h, X)] = _stream_from(payload, codes, seg_off, 0, keep, r, h, X, S, Hkv, cu, dtype)
+                out[(r, h, X)] = _stream_from(payload, codes, seg_off, 0, keep, r, h, X, S, Hkv, cu, dtype, cu_cap)
     return {"streams": out, "codes": codes, "seg_off": seg_off, "total": total, "S": S}
 
 
@@ -138,37 +142,43 @@ class StoreReader:
         self.codes = store.buf[o_codes:o_codes + 2 * self.S].cpu().numpy().copy()
         self.seg_off = store.buf[o_off:o_off + 16 * self.S].cpu().numpy().view(np.uint64).copy()
         self.total = int(store.buf[0:8].cpu().numpy().view(np.uint64)[0])
-        self.cu = store.cu
+        B = int(info.batch)
+        self.cu = np.array([info.cu_seqlens[i] for i in range(B + 1)], dtype=np.int64)
+        self.cu_cap = np.array([info.cu_capacity[i] for i in range(B + 1)], dtype=np.int64)
 
     def segment_bytes(self, bv: int) -> np.ndarray:
-        """Payload bytes of every segment implied by its code (K segments, then V segments)."""
-        n, S_r, seg_base = seg_counts(self.cu)
+        """Payload bytes of every segment slot implied by its code (K slots, then V slots; 0 for unused slots)."""
+        n, S_use, _ = seg_counts(self.cu)
+        _, S_r, seg_base = seg_counts(self.cu_cap)
         ns = np.zeros(2 * self.S, dtype=np.int64)
         for X in (0, 1):
             for r in range(len(n)):
-                per = np.full(int(S_r[r]), SEG, dtype=np.int64)
-                if S_r[r]:
-                    per[-1] = int(n[r]) - (int(S_r[r]) - 1) * SEG
+                per = np.full(int(S_use[r]), SEG, dtype=np.int64)
+                if S_use[r]:
+                    per[-1] = int(n[r]) - (int(S_use[r]) - 1) * SEG
                 for h in range(self.Hkv):
                     g0 = segment_id(X, r, h, 0, self.S, self.Hkv, seg_base, S_r)
-                    ns[g0:g0 + int(S_r[r])] = per
-        c = np.asarray(self.keep, dtype=np.int64)[self.codes.astype(np.int64)]
+                    ns[g0:g0 + int(S_use[r])] = per
+        c = np.asarray(self.keep, dtype=np.int64)[self.codes.astype(np.int64) % len(self.keep)]
         return ns * c * (bv + (c < D))
 
     def stream(self, r: int, h: int, X: int) -> Stream:
-        n, S_r, seg_base = seg_counts(self.cu)
-        if S_r[r] == 0:
+        n, S_use, _ = seg_counts(self.cu)
+        _, S_r, seg_base = seg_counts(self.cu_cap)
+        if S_use[r] == 0:
             return Stream(0, D, np.zeros(0, np.int64), np.zeros(0, np.int64), np.zeros((0, D), bool), np.zeros((0, D)))
         g0 = segment_id(X, r, h, 0, self.S, self.Hkv, seg_base, S_r)
-        g1 = g0 + int(S_r[r]) - 1
+        g1 = g0 + int(S_use[r]) - 1
         bv = 2 if self.dtype == "bf16" else 4
         if getattr(self, "_sizes", None) is None:
             self._sizes = self.segment_bytes(bv)
-        last = int(self._sizes[g1])
-        lo, hi = int(self.seg_off[g0]), int(self.seg_off[g1]) + last
+        # the stream's segments lie in one payload range unless appends placed some elsewhere
+        offs = self.seg_off[g0:g1 + 1].astype(np.int64)
+        lo = int(offs.min())
+        hi = int(max(int(o) + int(sz) for o, sz in zip(offs, self._sizes[g0:g1 + 1])))
         payload = self.store.buf[self.o_pay + lo:self.o_pay + hi].cpu().numpy()
         return _stream_from(payload, self.codes, self.seg_off, lo, self.keep, r, h, X, self.S, self.Hkv,
-                            self.cu, self.dtype)
+                            self.cu, self.dtype, self.cu_cap)
 
 
 def pack_oracle_store(streams: dict, cu, Hkv: int, dtype: str, keep: tuple):
