@@ -245,6 +245,31 @@ def main():
 
     layer_res = layer_batched(mkv, torch, dev, linp, args) if linp is not None else None
 
+    # incremental append (an extra): a growable store of the same inputs with room for 256 more tokens per
+    # request; one append call adds a token to every request (each call re-compresses every open segment)
+    append_res = None
+    if w.dtype == "bf16":
+        n_ctx = np.diff(inp.cu_seqlens)
+        gst = mkv.mkv_compress(K, V, inp.cu_seqlens, basis, policy, capacity=n_ctx + 256)
+        newK = K[:w.batch * 1].reshape(w.batch, w.n_kv_heads, 128).contiguous()
+        newV = V[:w.batch * 1].reshape(w.batch, w.n_kv_heads, 128).contiguous()
+        aws = torch.empty(64 * 1024, dtype=torch.uint8, device=dev)
+        for _ in range(4):
+            mkv.mkv_append(gst, newK, newV, ws=aws)
+        torch.cuda.synchronize()
+        mkv.mkv_profile_start(kernels=["append"])
+        n_app = 64
+        t0 = time.perf_counter()
+        for _ in range(n_app):
+            mkv.mkv_append(gst, newK, newV, ws=aws)
+        torch.cuda.synchronize()
+        a_ms = (time.perf_counter() - t0) * 1e3 / n_app
+        ak = mkv.mkv_profile_stop()
+        append_res = {"ms_per_append_call": a_ms, "append_kernel_ms": ak["append"][0] / max(ak["append"][1], 1),
+                      "tokens_per_call": w.batch, "streams_recompressed_per_call": 2 * w.batch * w.n_kv_heads,
+                      "appended_tokens_per_s": w.batch / (a_ms * 1e-3)}
+        del gst
+
     sel_np = sel.cpu().numpy()
     # V payload actually gathered: rows of the selected tokens
     n = np.diff(inp.cu_seqlens)
@@ -304,6 +329,7 @@ def main():
         "dense_baseline": dense_base,
         "gram": gram_res,
         "layer_batched": layer_res,
+        "append": append_res,
         "input_generation_s": t_gen,
     }
     if not args.no_cpu_baseline:

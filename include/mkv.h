@@ -103,6 +103,33 @@ mkv_status mkv_compress(const mkv_kv_desc* kv, const float* basis, const mkv_seg
                         void* store_buf, size_t store_bytes, void* scratch, size_t scratch_bytes,
                         mkv_stream_t stream, mkv_store** out);
 
+/* ---- growing stores (incremental append) ---------------------------------------------------------------
+ * A growable store keeps room for tokens appended while decoding: segment slots and packed-payload room for
+ * capacity[r] >= n_r tokens of each request (host [batch]), and for every (request, KV head, tensor) stream an
+ * open-segment area holding the original rows of its last, unfinished segment and that segment's packed form.
+ * The pages keep newly generated KV vectors in a GPU-side buffer and fold them into the compressed cache off
+ * the critical path (section 1, Observation & Approach 2).  Here each append re-compresses the stream's open
+ * segment by the segment rule over its tokens so far (same rotation, selection and packing as mkv_compress),
+ * and the append that completes a segment (64 tokens) seals it into the payload.  After any sequence of
+ * appends, every segment holds exactly what mkv_compress would build from the extended contexts: the same
+ * code, channels and values; only payload offsets differ.  bf16 only (MKV_E_UNSUPPORTED otherwise).
+ * mkv_compress_growable is mkv_compress with capacities; the sizes come from mkv_compress_bytes_growable. */
+mkv_status mkv_compress_bytes_growable(const mkv_kv_desc* kv, const mkv_seg_policy* policy, const int64_t* capacity,
+                                       size_t* store_bytes, size_t* scratch_bytes);
+mkv_status mkv_compress_growable(const mkv_kv_desc* kv, const float* basis, const mkv_seg_policy* policy,
+                                 const int64_t* capacity, void* store_buf, size_t store_bytes, void* scratch,
+                                 size_t scratch_bytes, mkv_stream_t stream, mkv_store** out);
+
+/* Appends one token to every request r with active[r] != 0 (active: [host] [batch], or NULL for every request):
+ * K_new[r][h] and V_new[r][h] ([dev] [batch][n_kv_heads][128] bf16, unrotated like the K/V given to
+ * mkv_compress) become token n_r of request r, and the handle's contexts advance.  Fails with MKV_E_ARG before
+ * enqueueing anything if the store is not growable or a listed request is at its capacity.  Work is enqueued
+ * on `stream`; decode calls enqueued after it on the same stream see the new tokens.  Calls that overlap on one
+ * store race.  ws [dev] >= mkv_append_workspace_bytes, 256-byte aligned. */
+mkv_status mkv_append_workspace_bytes(const mkv_store* store, size_t* ws_bytes);
+mkv_status mkv_append(mkv_store* store, const void* K_new, const void* V_new, const int32_t* active, void* ws,
+                      size_t ws_bytes, mkv_stream_t stream);
+
 /* Wraps a handle around a store buffer that already holds a store of the documented layout for this shape
  * (e.g. one restored from a file or written by a test).  kv->K and kv->V are ignored.  has_basis says whether
  * the buffer's basis region is valid.  Enqueues nothing. */

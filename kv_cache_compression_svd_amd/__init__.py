@@ -69,6 +69,12 @@ SIGNATURES = {
                                c_void_p, POINTER(c_void_p)]),
     "mkv_store_attach": (c_int32, [POINTER(KVDesc), POINTER(SegPolicy), c_int32, c_void_p, c_size_t,
                                    POINTER(c_void_p)]),
+    "mkv_compress_bytes_growable": (c_int32, [POINTER(KVDesc), POINTER(SegPolicy), POINTER(c_int64),
+                                              POINTER(c_size_t), POINTER(c_size_t)]),
+    "mkv_compress_growable": (c_int32, [POINTER(KVDesc), c_void_p, POINTER(SegPolicy), POINTER(c_int64), c_void_p,
+                                        c_size_t, c_void_p, c_size_t, c_void_p, POINTER(c_void_p)]),
+    "mkv_append_workspace_bytes": (c_int32, [c_void_p, POINTER(c_size_t)]),
+    "mkv_append": (c_int32, [c_void_p, c_void_p, c_void_p, POINTER(c_int32), c_void_p, c_size_t, c_void_p]),
     "mkv_store_view": (c_int32, [c_void_p, POINTER(StoreInfo)]),
     "mkv_store_payload_bytes": (c_int32, [c_void_p, c_void_p, POINTER(c_uint64)]),
     "mkv_store_destroy": (c_int32, [c_void_p]),
@@ -217,14 +223,24 @@ def mkv_compress_bytes(K, V, cu_seqlens, policy: SegPolicy | None = None, n_kv_h
 
 
 def mkv_compress(K, V, cu_seqlens, basis=None, policy: SegPolicy | None = None, stream=None, store_buf=None,
-                 scratch=None) -> Store:
+                 scratch=None, capacity=None) -> Store:
     """Compress K, V ([tokens][n_kv_heads][128], bf16 or float32, CUDA) with the per-(request, KV head, tensor)
-    bases ``basis`` (float32 [batch][n_kv_heads][2][128][128] CUDA, or None for already-rotated inputs)."""
+    bases ``basis`` (float32 [batch][n_kv_heads][2][128][128] CUDA, or None for already-rotated inputs).
+    ``capacity`` (per-request token counts >= the contexts) builds a growable store that mkv_append extends."""
+    import numpy as np
     torch = _torch()
     policy = policy or mkv_default_policy()
     d, cu = _kv_desc(K, V, cu_seqlens)
     sb, tb = c_size_t(), c_size_t()
-    _check(lib().mkv_compress_bytes(byref(d), byref(policy), byref(sb), byref(tb)))
+    cap = None
+    if capacity is not None:
+        cap = np.ascontiguousarray(np.asarray(capacity, dtype=np.int64))
+        if cap.shape != (d.batch,):
+            raise ValueError("capacity must hold one token count per request")
+        _check(lib().mkv_compress_bytes_growable(byref(d), byref(policy), cap.ctypes.data_as(POINTER(c_int64)),
+                                                 byref(sb), byref(tb)))
+    else:
+        _check(lib().mkv_compress_bytes(byref(d), byref(policy), byref(sb), byref(tb)))
     if basis is not None:
         if basis.dtype != torch.float32 or not basis.is_contiguous() or not basis.is_cuda or \
                 tuple(basis.shape) != (d.batch, d.n_kv_heads, 2, HEAD_DIM, HEAD_DIM):
@@ -234,10 +250,41 @@ def mkv_compress(K, V, cu_seqlens, basis=None, policy: SegPolicy | None = None, 
     if scratch is None:
         scratch = torch.empty(max(tb.value, 1), dtype=torch.uint8, device=K.device)
     h = c_void_p()
-    _check(lib().mkv_compress(byref(d), _ptr(basis), byref(policy), _ptr(store_buf), c_size_t(store_buf.numel()),
-                              _ptr(scratch), c_size_t(scratch.numel()), _stream_ptr(stream), byref(h)))
+    if cap is not None:
+        _check(lib().mkv_compress_growable(byref(d), _ptr(basis), byref(policy), cap.ctypes.data_as(POINTER(c_int64)),
+                                           _ptr(store_buf), c_size_t(store_buf.numel()), _ptr(scratch),
+                                           c_size_t(scratch.numel()), _stream_ptr(stream), byref(h)))
+    else:
+        _check(lib().mkv_compress(byref(d), _ptr(basis), byref(policy), _ptr(store_buf), c_size_t(store_buf.numel()),
+                                  _ptr(scratch), c_size_t(scratch.numel()), _stream_ptr(stream), byref(h)))
     # scratch must outlive the asynchronous kernels: keep it until the store is dropped
     return Store(h, store_buf, cu, d.n_kv_heads, d.dtype, policy, keep_alive=(scratch,))
+
+
+def mkv_append(store: Store, K_new, V_new, active=None, ws=None, stream=None):
+    """Appends one token per active request (all when ``active`` is None) to a growable store: K_new, V_new are
+    [batch][n_kv_heads][128] CUDA tensors of the store's dtype.  Updates ``store.cu``."""
+    import numpy as np
+    torch = _torch()
+    B, H = len(store.cu) - 1, store.n_kv_heads
+    for t in (K_new, V_new):
+        if tuple(t.shape) != (B, H, HEAD_DIM) or not t.is_contiguous() or not t.is_cuda or _dtype_code(t) != store.dtype:
+            raise ValueError("K_new and V_new must be contiguous CUDA tensors [batch][n_kv_heads][128] of the store's dtype")
+    act = None
+    if active is not None:
+        act = np.ascontiguousarray(np.asarray(active, dtype=np.int32))
+        if act.shape != (B,):
+            raise ValueError("active must hold one flag per request")
+    if ws is None:
+        v = c_size_t()
+        _check(lib().mkv_append_workspace_bytes(store.handle, byref(v)))
+        ws = torch.empty(v.value, dtype=torch.uint8, device=K_new.device)
+    _check(lib().mkv_append(store.handle, _ptr(K_new), _ptr(V_new),
+                            None if act is None else act.ctypes.data_as(POINTER(c_int32)), _ptr(ws),
+                            c_size_t(ws.numel()), _stream_ptr(stream)))
+    info = store.view()
+    store.cu = np.array([info.cu_seqlens[i] for i in range(B + 1)], dtype=np.int64)
+    return store
 
 
 def mkv_store_attach(cu_seqlens, n_kv_heads: int, dtype: int, policy: SegPolicy, has_basis: bool, store_buf) -> Store:

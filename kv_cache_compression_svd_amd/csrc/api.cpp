@@ -37,11 +37,11 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ---- kernel timing --------------------------------------------------------------------------------------
 enum KernelId {
     K_UPLOAD = 0, K_CMP_DECIDE, K_CMP_SCAN, K_CMP_PACK, K_DEC_PREP, K_SCORE, K_SEL_COLLECT, K_SEL_EMIT,
-    K_ATTEND, K_COMBINE, K_DENSE_ATTEND, K_DENSE_COMBINE, K_GRAM, K_GRAM_REDUCE, K_COUNT
+    K_ATTEND, K_COMBINE, K_DENSE_ATTEND, K_DENSE_COMBINE, K_GRAM, K_GRAM_REDUCE, K_APPEND, K_COUNT
 };
 const char* kKernelNames[K_COUNT] = {"upload", "compress_decide", "compress_scan", "compress_pack", "decode_prep",
                                      "score", "select_collect", "select_emit", "attend", "combine",
-                                     "dense_attend", "dense_combine", "gram", "gram_reduce"};
+                                     "dense_attend", "dense_combine", "gram", "gram_reduce", "append"};
 
 struct Profiler {
     std::mutex mu;
@@ -258,16 +258,38 @@ void mkv_default_policy(mkv_seg_policy* p) {
 
 const char* mkv_last_error(void) { return g_err.c_str(); }
 
-mkv_status mkv_compress_bytes(const mkv_kv_desc* kv, const mkv_seg_policy* policy, size_t* store_bytes,
-                              size_t* scratch_bytes) {
-    Shape sh;
-    mkv_status st = check_kv(kv, false, &sh);
+static mkv_status shape_for(const mkv_kv_desc* kv, const mkv_seg_policy* policy, const int64_t* capacity,
+                            bool need_data, Shape* sh) {
+    mkv_status st = check_kv(kv, need_data, sh);
     if (st) return st;
-    if ((st = check_policy(policy, sh.dtype))) return st;
+    if ((st = check_policy(policy, sh->dtype))) return st;
+    if (capacity) {
+        if (sh->dtype != MKV_BF16) return fail(MKV_E_UNSUPPORTED, "growable stores take bf16 K/V only");
+        if ((st = set_capacity(sh, capacity))) return st;
+    }
+    return MKV_OK;
+}
+
+static mkv_status compress_bytes(const mkv_kv_desc* kv, const mkv_seg_policy* policy, const int64_t* capacity,
+                                 size_t* store_bytes, size_t* scratch_bytes) {
+    Shape sh;
+    mkv_status st = shape_for(kv, policy, capacity, false, &sh);
+    if (st) return st;
     if (!store_bytes || !scratch_bytes) return fail(MKV_E_ARG, "output pointers are NULL");
     *store_bytes = store_layout(sh).bytes;
     *scratch_bytes = scratch_layout(sh).bytes;
     return MKV_OK;
+}
+
+mkv_status mkv_compress_bytes(const mkv_kv_desc* kv, const mkv_seg_policy* policy, size_t* store_bytes,
+                              size_t* scratch_bytes) {
+    return compress_bytes(kv, policy, nullptr, store_bytes, scratch_bytes);
+}
+
+mkv_status mkv_compress_bytes_growable(const mkv_kv_desc* kv, const mkv_seg_policy* policy, const int64_t* capacity,
+                                       size_t* store_bytes, size_t* scratch_bytes) {
+    if (!capacity) return fail(MKV_E_ARG, "capacity is NULL");
+    return compress_bytes(kv, policy, capacity, store_bytes, scratch_bytes);
 }
 
 static mkv_status make_handle(const Shape& sh, const mkv_seg_policy* policy, int32_t has_basis, void* buf,
@@ -285,14 +307,13 @@ static mkv_status make_handle(const Shape& sh, const mkv_seg_policy* policy, int
     return MKV_OK;
 }
 
-mkv_status mkv_compress(const mkv_kv_desc* kv, const float* basis, const mkv_seg_policy* policy, void* store_buf,
-                        size_t store_bytes, void* scratch, size_t scratch_bytes, mkv_stream_t stream_,
-                        mkv_store** out) {
+static mkv_status compress(const mkv_kv_desc* kv, const float* basis, const mkv_seg_policy* policy,
+                           const int64_t* capacity, void* store_buf, size_t store_bytes, void* scratch,
+                           size_t scratch_bytes, mkv_stream_t stream_, mkv_store** out) {
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
     Shape sh;
-    mkv_status st = check_kv(kv, true, &sh);
+    mkv_status st = shape_for(kv, policy, capacity, true, &sh);
     if (st) return st;
-    if ((st = check_policy(policy, sh.dtype))) return st;
     if (!out) return fail(MKV_E_ARG, "out is NULL");
     if (!store_buf || !scratch) return fail(MKV_E_ARG, "store_buf and scratch must be non-NULL");
     if (!aligned(store_buf) || !aligned(scratch)) return fail(MKV_E_ARG, "store_buf and scratch must be 256-byte aligned");
@@ -346,12 +367,89 @@ mkv_status mkv_compress(const mkv_kv_desc* kv, const float* basis, const mkv_seg
     for (int k = 0; k < 4; ++k) a.keep[k] = k < policy->n_keep ? policy->keep[k] : 0;
     a.n_keep = policy->n_keep;
     a.frac = policy->energy_frac;
+    if (sh.growable) {
+        a.open_rows = reinterpret_cast<uint16_t*>(base + L.open_rows);
+        a.open_elems = (int64_t)(L.open_bytes / 2);
+    }
     const int dt = sh.dtype == MKV_BF16 ? 1 : 0;
     uint64_t* total = reinterpret_cast<uint64_t*>(base);
     if ((st = run(K_CMP_DECIDE, stream, [&] { return launch_cmp_decide(a, dt, stream); }))) return st;
     if ((st = run(K_CMP_SCAN, stream, [&] { return launch_cmp_scan(a.wg_total, 2 * nblk, total, stream); }))) return st;
     if ((st = run(K_CMP_PACK, stream, [&] { return launch_cmp_pack(a, dt, stream); }))) return st;
     return make_handle(sh, policy, basis ? 1 : 0, store_buf, out);
+}
+
+mkv_status mkv_compress(const mkv_kv_desc* kv, const float* basis, const mkv_seg_policy* policy, void* store_buf,
+                        size_t store_bytes, void* scratch, size_t scratch_bytes, mkv_stream_t stream,
+                        mkv_store** out) {
+    return compress(kv, basis, policy, nullptr, store_buf, store_bytes, scratch, scratch_bytes, stream, out);
+}
+
+mkv_status mkv_compress_growable(const mkv_kv_desc* kv, const float* basis, const mkv_seg_policy* policy,
+                                 const int64_t* capacity, void* store_buf, size_t store_bytes, void* scratch,
+                                 size_t scratch_bytes, mkv_stream_t stream, mkv_store** out) {
+    if (!capacity) return fail(MKV_E_ARG, "capacity is NULL");
+    return compress(kv, basis, policy, capacity, store_buf, store_bytes, scratch, scratch_bytes, stream, out);
+}
+
+mkv_status mkv_append_workspace_bytes(const mkv_store* s, size_t* ws_bytes) {
+    if (!s || !ws_bytes) return fail(MKV_E_ARG, "store and ws_bytes must be non-NULL");
+    *ws_bytes = align_up(16ull * s->sh.B);
+    return MKV_OK;
+}
+
+mkv_status mkv_append(mkv_store* s, const void* K_new, const void* V_new, const int32_t* active, void* ws,
+                      size_t ws_bytes, mkv_stream_t stream_) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    if (!s) return fail(MKV_E_ARG, "store is NULL");
+    Shape& sh = s->sh;
+    if (!sh.growable) return fail(MKV_E_ARG, "the store was not built growable (mkv_compress_growable)");
+    if (!K_new || !V_new) return fail(MKV_E_ARG, "K_new and V_new must be non-NULL");
+    if (!ws || !aligned(ws)) return fail(MKV_E_ARG, "ws must be non-NULL and 256-byte aligned");
+    if (ws_bytes < align_up(16ull * sh.B)) return fail(MKV_E_ARG, "ws_bytes %zu too small", ws_bytes);
+    std::vector<int32_t> tab;
+    for (int r = 0; r < sh.B; ++r) {
+        if (active && !active[r]) continue;
+        const int64_t n = sh.cu[r + 1] - sh.cu[r];
+        if (n + 1 > sh.cap[r]) return fail(MKV_E_ARG, "request %d is at its capacity (%lld tokens)", r, (long long)sh.cap[r]);
+        tab.push_back(r);
+        tab.push_back((int32_t)n);
+        tab.push_back(sh.Hkv * sh.segbase[r]);
+        tab.push_back(sh.scap[r]);
+    }
+    const int n_req = (int)(tab.size() / 4);
+    if (n_req == 0) return MKV_OK;
+    int32_t* tdev = static_cast<int32_t*>(ws);
+    mkv_status st;
+    if ((st = upload_words(tdev, tab, 0, stream))) return st;
+    const StoreLayout& L = s->lay;
+    CmpArgs a;
+    std::memset(&a, 0, sizeof a);
+    for (int k = 0; k < 4; ++k) a.keep[k] = k < s->policy.n_keep ? s->policy.keep[k] : 0;
+    a.n_keep = s->policy.n_keep;
+    a.frac = s->policy.energy_frac;
+    AppendArgs x;
+    x.Kn = static_cast<const uint16_t*>(K_new);
+    x.Vn = static_cast<const uint16_t*>(V_new);
+    x.basis = s->has_basis ? reinterpret_cast<const float*>(s->base + L.basis) : nullptr;
+    x.tab = tdev;
+    x.Hkv = sh.Hkv;
+    x.S = sh.S;
+    x.codes = s->base + L.codes;
+    x.seg_off = reinterpret_cast<uint64_t*>(s->base + L.seg_off);
+    x.payload = s->base + L.payload;
+    x.open_pack = L.open_pack - L.payload;
+    x.open_bytes = L.open_bytes;
+    x.open_rows = reinterpret_cast<uint16_t*>(s->base + L.open_rows);
+    x.total = reinterpret_cast<unsigned long long*>(s->base);
+    if ((st = run(K_APPEND, stream, [&] { return launch_cmp_append(a, x, n_req, stream); }))) return st;
+    // the listed requests now hold one more token
+    std::vector<int64_t> n(sh.B);
+    for (int r = 0; r < sh.B; ++r) n[r] = sh.cu[r + 1] - sh.cu[r];
+    for (int i = 0; i < n_req; ++i) n[tab[4 * i]] += 1;
+    for (int r = 0; r < sh.B; ++r) sh.cu[r + 1] = sh.cu[r] + n[r];
+    sh.total = sh.cu[sh.B];
+    return MKV_OK;
 }
 
 mkv_status mkv_store_attach(const mkv_kv_desc* kv, const mkv_seg_policy* policy, int32_t has_basis, void* store_buf,

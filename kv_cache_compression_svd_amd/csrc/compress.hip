@@ -381,6 +381,50 @@ __device__ __forceinline__ int segment_code8(int best, bool valid, int* s_code) 
 // =====================================================================================================
 constexpr int XS = 136;   // LDS row stride in u16 (272 B: 16-B aligned, skews banks between rows)
 
+// MFMA B fragments of basis columns [16 wid, 16 wid + 16): the float32 basis split into three bf16 parts
+// (hi + mid + lo), so that the bf16 products summed in float32 reproduce the float32 basis.  The same
+// arithmetic, in the same order, as the compressor's inline copy (so appended segments match compressed ones).
+__device__ __forceinline__ void basis_frags(const float* Bm, int wid, int lane, bf16x8 (&bh)[4], bf16x8 (&bmid)[4],
+                                            bf16x8 (&blo)[4]) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int k = 32 * ks + (lane >> 4) * 8 + i;
+            const int col = 16 * wid + (lane & 15);
+            const float v = Bm[k * MKV_D + col];
+            const uint32_t hb = f32_to_bf16_rne(v);
+            const float r1 = v - bf16_to_f32(hb);
+            const uint32_t mb = f32_to_bf16_rne(r1);
+            const float r2 = r1 - bf16_to_f32(mb);
+            const uint32_t lb = f32_to_bf16_rne(r2);
+            bh[ks][i] = __builtin_bit_cast(__bf16, (unsigned short)hb);
+            bmid[ks][i] = __builtin_bit_cast(__bf16, (unsigned short)mb);
+            blo[ks][i] = __builtin_bit_cast(__bf16, (unsigned short)lb);
+        }
+}
+
+// Output channels [16 wid, 16 wid + 16) of a 64 x 128 tile: xh = round_bf16(X @ B) (LDS, row stride XS).
+__device__ __forceinline__ void rotate_tile(const uint16_t* X, uint16_t* xh, const bf16x8 (&bh)[4],
+                                            const bf16x8 (&bmid)[4], const bf16x8 (&blo)[4], int wid, int lane) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+        f32x4 am = {0, 0, 0, 0}, ac = {0, 0, 0, 0};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 A = *reinterpret_cast<const bf16x8*>(&X[(16 * mt + (lane & 15)) * XS + 32 * ks + (lane >> 4) * 8]);
+            am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bh[ks], am, 0, 0, 0);
+            ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, blo[ks], ac, 0, 0, 0);
+            ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bmid[ks], ac, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = 16 * mt + (lane >> 4) * 4 + i;
+            xh[row * XS + 16 * wid + (lane & 15)] = (uint16_t)f32_to_bf16_rne(am[i] + ac[i]);
+        }
+    }
+}
+
 // Four waves per SIMD (128 registers) so that two workgroups share a CU and one's MFMA rotation overlaps the
 // other's threshold search; the compiler keeps part of the basis fragments in scratch to fit.
 template <bool PACK>
@@ -396,6 +440,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     const uint16_t* src = reinterpret_cast<const uint16_t*>(t.X ? a.V : a.K);
     const float* Bm = a.basis ? a.basis + ((((size_t)t.r * a.Hkv + t.h) * 2 + t.X) << 14) : nullptr;
 
+    // the basis fragments and the rotation below are written out here rather than through basis_frags() and
+    // rotate_tile(): with the helpers the compiler spills more of this kernel's registers (measured slower)
     bf16x8 bh[4], bmid[4], blo[4];
     if (Bm) {
 #pragma unroll
@@ -502,6 +548,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
             uint8_t* dst = a.payload + wg_off;
             if (tid == 0) a.seg_off[gs] = wg_off;
             wg_off += (uint64_t)ns * c * (2 + (c < MKV_D ? 1 : 0));
+            if (a.open_rows && ns < MKV_SEG && lrow < ns) {
+                // growable store: the stream's unfinished last segment keeps its original rows for appends
+                uint16_t* orow = a.open_rows + (((int64_t)t.r * a.Hkv + t.h) * 2 + t.X) * a.open_elems;
+                u32x4* d = reinterpret_cast<u32x4*>(orow + lrow * MKV_D + lq * 16);
+                const u32x4* q = reinterpret_cast<const u32x4*>(&X[lrow * XS + lq * 16]);
+                d[0] = q[0];
+                d[1] = q[1];
+            }
             if (c == MKV_D) {
                 const int nq = ns * 16;   // 16-byte pieces of ns rows of 256 bytes
                 for (int qd = tid; qd < nq; qd += 512) {
@@ -522,6 +576,101 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         if (more) store_tile(xs[cur ^ 1]);
     }
     if (!PACK && tid == 0) a.wg_total[blockIdx.x] = wg_bytes;
+}
+
+// =====================================================================================================
+// append: one token joins the open (last, unfinished) segment of each listed stream of a growable bf16 store
+// =====================================================================================================
+// One workgroup per (listed request, KV head, tensor).  The open segment's earlier rows (kept unrotated in the
+// store) and the new row form the tile; the tile is rotated, decided and packed by the same code as the
+// compressor, so the segment ends up exactly as compressing the extended context would leave it.  An open
+// segment lives in its stream's open area; the append that completes it (64 tokens) seals it into the payload
+// at a position taken from the payload counter.
+__global__ __launch_bounds__(512) void k_cmp_append(CmpArgs a, AppendArgs x) {
+    __shared__ __attribute__((aligned(16))) uint16_t xs[64 * XS];
+    __shared__ __attribute__((aligned(16))) uint16_t xh[64 * XS];
+    __shared__ __attribute__((aligned(16))) uint8_t stg[64 * 64 * 3];
+    __shared__ int s_code[8];
+    __shared__ int s_fail[4];
+    __shared__ unsigned long long s_pos;
+    const int tid = threadIdx.x, lane = tid & 63, wid = uni(tid >> 6);
+    const int ai = blockIdx.x / (2 * x.Hkv), rem = blockIdx.x - ai * 2 * x.Hkv, h = rem >> 1, X = rem & 1;
+    const int r = x.tab[4 * ai], n_old = x.tab[4 * ai + 1];
+    const int p = n_old & (MKV_SEG - 1), ns = p + 1;
+    const int64_t g = (int64_t)X * x.S + x.tab[4 * ai + 2] + (int64_t)h * x.tab[4 * ai + 3] + (n_old >> 6);
+    const int64_t st = ((int64_t)r * x.Hkv + h) * 2 + X;
+    uint16_t* rows = x.open_rows + st * (int64_t)(x.open_bytes / 2);
+    const uint16_t* nr = (X ? x.Vn : x.Kn) + ((int64_t)r * x.Hkv + h) * MKV_D;
+    const float* Bm = x.basis ? x.basis + ((((size_t)r * x.Hkv + h) * 2 + X) << 14) : nullptr;
+    bf16x8 bh[4], bmid[4], blo[4];
+    if (Bm) basis_frags(Bm, wid, lane, bh, bmid, blo);
+
+    // tile: earlier rows of the open segment, the new row (also kept for later appends), zeros
+    const int lrow = tid >> 3, lq = tid & 7;
+    u32x4 r0 = {0, 0, 0, 0}, r1 = {0, 0, 0, 0};
+    if (lrow < p) {
+        const u32x4* q = reinterpret_cast<const u32x4*>(rows + lrow * MKV_D + lq * 16);
+        r0 = q[0];
+        r1 = q[1];
+    } else if (lrow == p) {
+        const u32x4* q = reinterpret_cast<const u32x4*>(nr + lq * 16);
+        r0 = q[0];
+        r1 = q[1];
+        u32x4* d = reinterpret_cast<u32x4*>(rows + p * MKV_D + lq * 16);
+        d[0] = r0;
+        d[1] = r1;
+    }
+    {
+        u32x4* d = reinterpret_cast<u32x4*>(&xs[lrow * XS + lq * 16]);
+        d[0] = r0;
+        d[1] = r1;
+    }
+    if (tid < 4) s_fail[tid] = 0;
+    __syncthreads();
+    if (Bm) {
+        rotate_tile(xs, xh, bh, bmid, blo, wid, lane);
+        __syncthreads();
+    }
+    const uint16_t* R = Bm ? xh : xs;
+    const int v = tid >> 3, pl = tid & 7;
+    const bool valid = v < ns;
+    uint32_t w[8];
+    {
+        const u32x4* rp = reinterpret_cast<const u32x4*>(&R[v * XS + pl * 16]);
+        const u32x4 x0 = rp[0], x1 = rp[1];
+        w[0] = x0.x; w[1] = x0.y; w[2] = x0.z; w[3] = x0.w;
+        w[4] = x1.x; w[5] = x1.y; w[6] = x1.z; w[7] = x1.w;
+    }
+    uint32_t thr[4] = {0, 0, 0, 0};
+    const int best = vector_decide8(w, a, thr, valid, s_fail);
+    const int code = segment_code8(best, valid, s_code);
+    const int c = a.keep[code];
+    if (tid == 0) {
+        const uint64_t bytes = (uint64_t)ns * c * (2 + (c < MKV_D ? 1 : 0));
+        s_pos = ns == MKV_SEG ? atomicAdd(x.total, (unsigned long long)bytes) : x.open_pack + st * x.open_bytes;
+        x.codes[g] = (uint8_t)code;
+    }
+    if (c < MKV_D && valid) vector_pack8(w, thr[code], c, v, pl, ns, stg);
+    __syncthreads();
+    const uint64_t pos = s_pos;
+    uint8_t* dst = x.payload + pos;
+    if (c == MKV_D) {
+        for (int qd = tid; qd < ns * 16; qd += 512) {
+            const int row = qd >> 4, col = (qd & 15) * 8;
+            *reinterpret_cast<u32x4*>(dst + (size_t)qd * 16) = *reinterpret_cast<const u32x4*>(&R[row * XS + col]);
+        }
+    } else {
+        const int nq = ns * c * 3 / 16;
+        for (int qd = tid; qd < nq; qd += 512)
+            *reinterpret_cast<u32x4*>(dst + (size_t)qd * 16) = *reinterpret_cast<const u32x4*>(stg + (size_t)qd * 16);
+    }
+    if (tid == 0) x.seg_off[g] = pos;
+}
+
+hipError_t launch_cmp_append(const CmpArgs& a, const AppendArgs& x, int n_requests, hipStream_t s) {
+    if (n_requests == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_cmp_append, dim3(n_requests * 2 * x.Hkv), dim3(512), 0, s, a, x);
+    return hipGetLastError();
 }
 
 // =====================================================================================================

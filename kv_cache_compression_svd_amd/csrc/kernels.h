@@ -40,9 +40,29 @@ struct CmpArgs {
     int32_t keep[4];
     int32_t n_keep;
     double frac;
+    uint16_t* open_rows;        // growable stores: original rows of each stream's open segment (else null)
+    int64_t open_elems;         // elements per stream in open_rows
+};
+
+// One token appended to each listed request of a growable bf16 store.
+struct AppendArgs {
+    const uint16_t* Kn;         // [B][Hkv][128]
+    const uint16_t* Vn;
+    const float* basis;         // the store's copy, or null
+    const int32_t* tab;         // per listed request: r | its tokens before the append | Hkv * seg_base | slots per stream
+    int32_t Hkv;
+    int64_t S;                  // segment slots per tensor
+    uint8_t* codes;
+    uint64_t* seg_off;
+    uint8_t* payload;
+    uint64_t open_pack;         // offset (from payload) of the per-stream packed open segments
+    uint64_t open_bytes;        // bytes per stream of open_pack and of open_rows
+    uint16_t* open_rows;
+    unsigned long long* total;  // payload bytes in use (header)
 };
 
 hipError_t launch_upload(const Upload& u, hipStream_t s);
+hipError_t launch_cmp_append(const CmpArgs& a, const AppendArgs& x, int n_requests, hipStream_t s);
 hipError_t launch_cmp_decide(const CmpArgs& a, int dtype, hipStream_t s);
 hipError_t launch_cmp_scan(uint64_t* wg_total, int64_t count, uint64_t* total, hipStream_t s);
 hipError_t launch_cmp_pack(const CmpArgs& a, int dtype, hipStream_t s);
