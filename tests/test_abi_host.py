@@ -156,3 +156,25 @@ def test_view_reports_layout():
 def test_kernel_names():
     names = [mkv.mkv_kernel_name(i) for i in range(mkv.PROFILE_KERNELS)]
     assert "score" in names and "attend" in names and names[-1] is None
+
+
+def test_growable_sizes_and_argument_checks():
+    L = mkv.lib()
+    d, cu = _desc(batch=2, cu=(0, 100, 300))
+    p = mkv.mkv_default_policy()
+    cap = np.array([164, 200], dtype=np.int64)
+    sb, tb = ctypes.c_size_t(), ctypes.c_size_t()
+    capp = cap.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    assert L.mkv_compress_bytes_growable(ctypes.byref(d), ctypes.byref(p), capp, ctypes.byref(sb), ctypes.byref(tb)) == mkv.MKV_OK
+    plain = _bytes(d, p)[1].value
+    assert sb.value > plain                       # room for 64 more tokens of request 0 and the open areas
+    small = np.array([99, 300], dtype=np.int64)   # below request 0's context
+    assert L.mkv_compress_bytes_growable(ctypes.byref(d), ctypes.byref(p), small.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                         ctypes.byref(sb), ctypes.byref(tb)) == mkv.MKV_E_ARG
+    d.dtype = mkv.MKV_FP32
+    assert L.mkv_compress_bytes_growable(ctypes.byref(d), ctypes.byref(p), capp, ctypes.byref(sb), ctypes.byref(tb)) == mkv.MKV_E_UNSUPPORTED
+    assert L.mkv_append(None, ctypes.c_void_p(256), ctypes.c_void_p(512), None, ctypes.c_void_p(1024), 4096, None) == mkv.MKV_E_ARG
+    h, _ = _attached(cu=(0, 100, 200), heads=2)   # a plain store refuses appends before enqueueing anything
+    assert L.mkv_append(h, ctypes.c_void_p(256), ctypes.c_void_p(512), None, ctypes.c_void_p(1 << 20), 4096, None) == mkv.MKV_E_ARG
+    assert "growable" in mkv.mkv_last_error()
+    L.mkv_store_destroy(h)
