@@ -154,6 +154,10 @@ typedef struct {
     const int64_t* cu_capacity;  /* [host] [batch+1] prefix sums of the token capacities; segment slots follow
                                     them (equal to cu_seqlens unless the store is growable) */
     int32_t growable;            /* built with mkv_compress_growable: accepts mkv_append */
+    const int32_t* seg_base;     /* [host] [batch] seg_base[r] of the segment numbering above */
+    const int32_t* seg_slots;    /* [host] [batch] S_r of the segment numbering above */
+    const int32_t* basis_slot;   /* [host] [batch] request r's bases are basis[basis_slot[r]] (r, unless a pool view) */
+    int32_t pool_view;           /* made by mkv_pool_view: the buffer regions above are the pool's */
 } mkv_store_info;
 
 /* Device addresses and host metadata of a store (for tests, export, and custom consumers). */
@@ -185,6 +189,81 @@ mkv_status mkv_decode_workspace_bytes(const mkv_store* store, int32_t n_q_heads,
 mkv_status mkv_decode_attn(const mkv_store* store, const void* q, int32_t n_q_heads, const int32_t* T,
                            float* out, int32_t* sel, int32_t sel_stride, void* ws, size_t ws_bytes,
                            mkv_stream_t stream);
+
+/* ---- paged pools -------------------------------------------------------------------------------------------
+ * A pool holds the compressed caches of many requests of one layer in one buffer, for serving: requests are
+ * added (compressed) and removed one by one, and any list of live requests decodes together through a store
+ * view.  Each request's packed segments go into fixed-size pages taken from a free list, so removing a request
+ * returns its pages and later requests reuse them without moving anyone's data; pages follow the compressed
+ * size, so the pool holds as many requests as their compressed bytes allow.  Within a page, a stream's
+ * segments are whole and in order (a segment never straddles two pages).  Every segment holds exactly what
+ * mkv_compress would build for the same request (same code, channels and values); only payload offsets differ,
+ * and decode over a view equals decode over a store of the same requests.
+ * Pool buffer layout (offsets from pool_buf): header, codes uint8 [2][S], seg_off uint64 [2][S] (S =
+ * n_kv_heads * segment_slots), bases float32 [max_requests][n_kv_heads][2][128][128] when has_basis, then
+ * n_pages pages of page_bytes; a request with id i and segment-slot run starting at u numbers its segments
+ * X*S + n_kv_heads*u + h*S_r + s with S_r = ceil(n_r/64), and its bases sit at basis slot i.
+ * Ordering: the pool's host bookkeeping is not thread-safe; pool calls and decode calls on its views must be
+ * ordered by the caller (one stream, or synchronisation), since removing a request lets the next add overwrite
+ * its pages. */
+typedef struct {
+    int32_t n_kv_heads;          /* >= 1 */
+    mkv_dtype dtype;
+    int32_t has_basis;           /* 1: every add passes bases (kept per request); 0: K/V are added pre-rotated */
+    int32_t max_requests;        /* request ids are 0 .. max_requests-1 */
+    int64_t segment_slots;       /* segment slots per (KV head, tensor), shared by the live requests: a request of
+                                    n tokens takes a contiguous run of ceil(n/64) */
+    int64_t n_pages;             /* >= 1 */
+    int64_t page_bytes;          /* multiple of 256, >= 64*128*dtype bytes (one uncompressed segment), <= 2^31 */
+} mkv_pool_desc;
+
+typedef struct mkv_pool mkv_pool;   /* opaque host handle */
+
+typedef struct {
+    mkv_pool_desc desc;
+    int32_t live_requests;
+    int64_t free_pages;
+    int64_t free_segment_slots;  /* per (KV head, tensor), over all free runs */
+    int64_t largest_free_run;    /* the longest run of free segment slots */
+    void* codes;                 /* [dev] the pool's regions (layout above) */
+    void* seg_off;
+    void* basis;                 /* NULL without bases */
+    void* payload;
+    uint64_t pool_bytes;
+} mkv_pool_info;
+
+/* Bytes of a pool buffer for this descriptor.  Host-only. */
+mkv_status mkv_pool_bytes(const mkv_pool_desc* desc, size_t* pool_bytes);
+/* Creates an empty pool over pool_buf ([dev] >= mkv_pool_bytes, 256-byte aligned; it must outlive the pool
+ * and every view).  Host-only: nothing is enqueued, the buffer's contents do not matter. */
+mkv_status mkv_pool_create(const mkv_pool_desc* desc, const mkv_seg_policy* policy, void* pool_buf,
+                           size_t pool_bytes, mkv_pool** out);
+/* Scratch bytes mkv_pool_add needs for this batch of new requests. */
+mkv_status mkv_pool_add_scratch_bytes(const mkv_pool* pool, const mkv_kv_desc* kv, size_t* scratch_bytes);
+/* Compresses the requests of kv (shape checks as mkv_compress; n_kv_heads and dtype must match the pool) into
+ * the pool and writes their ids to ids [host] [kv->batch].  basis: as for mkv_compress, required when the pool
+ * has bases and NULL otherwise; the pool keeps a copy.  SYNCHRONISES `stream` (twice): the pages a request
+ * needs depend on its kept channel counts, so they are read back after the decide pass and handed out on the
+ * host.  Fails with MKV_E_ARG, leaving the pool as it was, when ids, segment slots (a contiguous run per
+ * request) or pages run short; the page check comes after the decide pass has run on the device, every other
+ * check before anything is enqueued.  scratch [dev] >= mkv_pool_add_scratch_bytes, 256-byte aligned. */
+mkv_status mkv_pool_add(mkv_pool* pool, const mkv_kv_desc* kv, const float* basis, void* scratch,
+                        size_t scratch_bytes, mkv_stream_t stream, int32_t* ids);
+/* Returns the listed requests' pages, slots and ids to the pool.  Host-only: the caller makes sure no enqueued
+ * work still reads them (a later add on the same stream is ordered after earlier decodes on it).  Views that
+ * list a removed request must not be used again.  Unknown or repeated ids: MKV_E_ARG, nothing removed. */
+mkv_status mkv_pool_remove(mkv_pool* pool, int32_t n, const int32_t* ids);
+/* A store handle over the listed live requests, in this order (request r of the view is ids[r]), for
+ * mkv_decode_attn, mkv_decode_workspace_bytes and mkv_store_view; release with mkv_store_destroy.  Host-only.
+ * mkv_store_payload_bytes of a view is the listed requests' packed bytes (no synchronisation). */
+mkv_status mkv_pool_view(const mkv_pool* pool, int32_t n, const int32_t* ids, mkv_store** out);
+/* Occupancy and device regions of the pool. */
+mkv_status mkv_pool_stats(const mkv_pool* pool, mkv_pool_info* info);
+/* Tokens, pages and packed payload bytes of one live request (each output pointer may be NULL). */
+mkv_status mkv_pool_request(const mkv_pool* pool, int32_t id, int64_t* n_tokens, int64_t* pages,
+                            uint64_t* payload_bytes);
+/* Frees the host handle only. NULL is accepted. */
+mkv_status mkv_pool_destroy(mkv_pool* pool);
 
 /* ---- uncompressed baseline ---------------------------------------------------------------------------------
  * Decode attention over the uncompressed bf16 K/V of the descriptor (no rotation, no channel or token
@@ -223,7 +302,7 @@ const char* mkv_last_error(void);
  * count (arrays of MKV_PROFILE_KERNELS entries), then clears them.  At most max_launches launches are timed
  * per session (later launches run untimed).  Not thread-safe with respect to concurrent library calls from
  * other threads. */
-#define MKV_PROFILE_KERNELS 16
+#define MKV_PROFILE_KERNELS 32
 mkv_status mkv_profile_start(int32_t max_launches, uint32_t kernel_mask);
 mkv_status mkv_profile_stop(double* total_ms, int32_t* launches);
 const char* mkv_kernel_name(int32_t kernel_id);   /* NULL when the id is unused */

@@ -21,7 +21,7 @@ MKV_OK, MKV_E_ARG, MKV_E_UNSUPPORTED, MKV_E_DEVICE = 0, 1, 2, 3
 MKV_FP32, MKV_BF16 = 0, 1
 HEAD_DIM = 128
 SEG_LEN = 64
-PROFILE_KERNELS = 16
+PROFILE_KERNELS = 32
 
 
 class MkvError(RuntimeError):
@@ -58,7 +58,19 @@ class StoreInfo(ctypes.Structure):
                 ("segments_per_tensor", c_int64), ("cu_seqlens", POINTER(c_int64)), ("codes", c_void_p),
                 ("seg_off", c_void_p), ("basis", c_void_p), ("payload", c_void_p), ("payload_total", c_void_p),
                 ("payload_capacity", c_uint64), ("store_bytes", c_uint64), ("cu_capacity", POINTER(c_int64)),
-                ("growable", c_int32)]
+                ("growable", c_int32), ("seg_base", POINTER(c_int32)), ("seg_slots", POINTER(c_int32)),
+                ("basis_slot", POINTER(c_int32)), ("pool_view", c_int32)]
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [("n_kv_heads", c_int32), ("dtype", c_int32), ("has_basis", c_int32), ("max_requests", c_int32),
+                ("segment_slots", c_int64), ("n_pages", c_int64), ("page_bytes", c_int64)]
+
+
+class PoolInfo(ctypes.Structure):
+    _fields_ = [("desc", PoolDesc), ("live_requests", c_int32), ("free_pages", c_int64),
+                ("free_segment_slots", c_int64), ("largest_free_run", c_int64), ("codes", c_void_p),
+                ("seg_off", c_void_p), ("basis", c_void_p), ("payload", c_void_p), ("pool_bytes", c_uint64)]
 
 
 # Every symbol include/mkv.h declares, with its ctypes signature.
@@ -85,6 +97,15 @@ SIGNATURES = {
     "mkv_dense_decode_attn": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
     "mkv_gram_workspace_bytes": (c_int32, [c_void_p, POINTER(c_size_t)]),
     "mkv_gram": (c_int32, [c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "mkv_pool_bytes": (c_int32, [POINTER(PoolDesc), POINTER(c_size_t)]),
+    "mkv_pool_create": (c_int32, [POINTER(PoolDesc), POINTER(SegPolicy), c_void_p, c_size_t, POINTER(c_void_p)]),
+    "mkv_pool_add_scratch_bytes": (c_int32, [c_void_p, POINTER(KVDesc), POINTER(c_size_t)]),
+    "mkv_pool_add": (c_int32, [c_void_p, POINTER(KVDesc), c_void_p, c_void_p, c_size_t, c_void_p, POINTER(c_int32)]),
+    "mkv_pool_remove": (c_int32, [c_void_p, c_int32, POINTER(c_int32)]),
+    "mkv_pool_view": (c_int32, [c_void_p, c_int32, POINTER(c_int32), POINTER(c_void_p)]),
+    "mkv_pool_stats": (c_int32, [c_void_p, POINTER(PoolInfo)]),
+    "mkv_pool_request": (c_int32, [c_void_p, c_int32, POINTER(c_int64), POINTER(c_int64), POINTER(c_uint64)]),
+    "mkv_pool_destroy": (c_int32, [c_void_p]),
     "mkv_last_error": (c_char_p, []),
     "mkv_profile_start": (c_int32, [c_int32, c_uint32]),
     "mkv_profile_stop": (c_int32, [POINTER(c_double), POINTER(c_int32)]),
@@ -293,6 +314,83 @@ def mkv_store_attach(cu_seqlens, n_kv_heads: int, dtype: int, policy: SegPolicy,
     _check(lib().mkv_store_attach(byref(d), byref(policy), int(bool(has_basis)), _ptr(store_buf),
                                   c_size_t(store_buf.numel()), byref(h)))
     return Store(h, store_buf, cu, n_kv_heads, dtype, policy)
+
+
+class Pool:
+    """A paged pool of compressed requests in one device buffer (a uint8 tensor) with its host handle."""
+
+    def __init__(self, n_kv_heads: int, dtype: int, max_requests: int, segment_slots: int, n_pages: int,
+                 page_bytes: int, has_basis: bool = True, policy: SegPolicy | None = None, device="cuda", buf=None):
+        torch = _torch()
+        self.policy = policy or mkv_default_policy()
+        d = PoolDesc()
+        d.n_kv_heads, d.dtype, d.has_basis, d.max_requests = int(n_kv_heads), int(dtype), int(bool(has_basis)), int(max_requests)
+        d.segment_slots, d.n_pages, d.page_bytes = int(segment_slots), int(n_pages), int(page_bytes)
+        self.desc = d
+        nb = c_size_t()
+        _check(lib().mkv_pool_bytes(byref(d), byref(nb)))
+        self.buf = torch.empty(nb.value, dtype=torch.uint8, device=device) if buf is None else buf
+        self.handle = c_void_p()
+        _check(lib().mkv_pool_create(byref(d), byref(self.policy), _ptr(self.buf), c_size_t(self.buf.numel()),
+                                     byref(self.handle)))
+        self.n_kv_heads, self.dtype = int(n_kv_heads), int(dtype)
+        self._keep = []
+
+    def add(self, K, V, cu_seqlens, basis=None, stream=None, scratch=None):
+        """Compresses the requests of (K, V, cu_seqlens) into the pool; returns their ids (numpy int32).
+        Synchronises the stream."""
+        import numpy as np
+        torch = _torch()
+        d, cu = _kv_desc(K, V, cu_seqlens)
+        if basis is not None and (basis.dtype != torch.float32 or not basis.is_contiguous() or not basis.is_cuda or
+                                  tuple(basis.shape) != (d.batch, d.n_kv_heads, 2, HEAD_DIM, HEAD_DIM)):
+            raise ValueError("basis must be a contiguous CUDA float32 tensor [batch][n_kv_heads][2][128][128]")
+        if scratch is None:
+            v = c_size_t()
+            _check(lib().mkv_pool_add_scratch_bytes(self.handle, byref(d), byref(v)))
+            scratch = torch.empty(max(v.value, 1), dtype=torch.uint8, device=self.buf.device)
+        ids = np.zeros(d.batch, dtype=np.int32)
+        _check(lib().mkv_pool_add(self.handle, byref(d), _ptr(basis), _ptr(scratch), c_size_t(scratch.numel()),
+                                  _stream_ptr(stream), ids.ctypes.data_as(POINTER(c_int32))))
+        return ids
+
+    def remove(self, ids):
+        import numpy as np
+        a = np.ascontiguousarray(np.atleast_1d(np.asarray(ids, dtype=np.int32)))
+        _check(lib().mkv_pool_remove(self.handle, len(a), a.ctypes.data_as(POINTER(c_int32))))
+
+    def view(self, ids) -> Store:
+        """A Store over the listed live requests (in this order) for mkv_decode_attn."""
+        import numpy as np
+        a = np.ascontiguousarray(np.atleast_1d(np.asarray(ids, dtype=np.int32)))
+        h = c_void_p()
+        _check(lib().mkv_pool_view(self.handle, len(a), a.ctypes.data_as(POINTER(c_int32)), byref(h)))
+        st = Store(h, self.buf, None, self.n_kv_heads, self.dtype, self.policy, keep_alive=(self,))
+        info = st.view()
+        st.cu = np.array([info.cu_seqlens[i] for i in range(len(a) + 1)], dtype=np.int64)
+        return st
+
+    def stats(self) -> PoolInfo:
+        info = PoolInfo()
+        _check(lib().mkv_pool_stats(self.handle, byref(info)))
+        return info
+
+    def request(self, rid: int):
+        """(tokens, pages, payload bytes) of a live request."""
+        n, pg, pb = c_int64(), c_int64(), c_uint64()
+        _check(lib().mkv_pool_request(self.handle, int(rid), byref(n), byref(pg), byref(pb)))
+        return int(n.value), int(pg.value), int(pb.value)
+
+    def close(self):
+        if self.handle is not None and self.handle.value:
+            lib().mkv_pool_destroy(self.handle)
+        self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def _T_array(T, batch):

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <new>
 #include <string>
@@ -37,11 +38,14 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ---- kernel timing --------------------------------------------------------------------------------------
 enum KernelId {
     K_UPLOAD = 0, K_CMP_DECIDE, K_CMP_SCAN, K_CMP_PACK, K_DEC_PREP, K_SCORE, K_SEL_COLLECT, K_SEL_EMIT,
-    K_ATTEND, K_COMBINE, K_DENSE_ATTEND, K_DENSE_COMBINE, K_GRAM, K_GRAM_REDUCE, K_APPEND, K_COUNT
+    K_ATTEND, K_COMBINE, K_DENSE_ATTEND, K_DENSE_COMBINE, K_GRAM, K_GRAM_REDUCE, K_APPEND, K_POOL_PLACE, K_POOL_FIX,
+    K_COUNT
 };
+static_assert(K_COUNT <= MKV_PROFILE_KERNELS, "kernel ids must fit the profiling arrays and mask");
 const char* kKernelNames[K_COUNT] = {"upload", "compress_decide", "compress_scan", "compress_pack", "decode_prep",
                                      "score", "select_collect", "select_emit", "attend", "combine",
-                                     "dense_attend", "dense_combine", "gram", "gram_reduce", "append"};
+                                     "dense_attend", "dense_combine", "gram", "gram_reduce", "append", "pool_place",
+                                     "pool_fix"};
 
 struct Profiler {
     std::mutex mu;
@@ -134,6 +138,7 @@ struct Shape {
     int64_t total_cap = 0;
     int64_t S = 0;                 // segment slots per tensor
     bool growable = false;
+    std::vector<int32_t> bslot;    // per request: basis slot (its index, unless the store is a pool view)
 };
 
 // Segment slots from capacities (cap NULL: the current contexts).
@@ -157,6 +162,8 @@ mkv_status set_capacity(Shape* sh, const int64_t* cap) {
     sh->total_cap = tot;
     sh->S = segs * sh->Hkv;
     sh->growable = cap != nullptr;
+    sh->bslot.resize(sh->B);
+    for (int r = 0; r < sh->B; ++r) sh->bslot[r] = r;
     return MKV_OK;
 }
 
@@ -240,6 +247,8 @@ struct mkv_store {
     StoreLayout lay;
     uint8_t* base = nullptr;
     std::vector<int64_t> cu_cap;   // prefix sums of the capacities (for mkv_store_view)
+    bool pool_view = false;
+    uint64_t view_payload = 0;     // pool views: payload bytes of the listed requests
 };
 
 // ======================================================================================================
@@ -486,11 +495,19 @@ mkv_status mkv_store_view(const mkv_store* s, mkv_store_info* info) {
     info->store_bytes = s->lay.bytes;
     info->cu_capacity = s->cu_cap.data();
     info->growable = s->sh.growable ? 1 : 0;
+    info->seg_base = s->sh.segbase.data();
+    info->seg_slots = s->sh.scap.data();
+    info->basis_slot = s->sh.bslot.data();
+    info->pool_view = s->pool_view ? 1 : 0;
     return MKV_OK;
 }
 
 mkv_status mkv_store_payload_bytes(const mkv_store* s, mkv_stream_t stream, uint64_t* bytes) {
     if (!s || !bytes) return fail(MKV_E_ARG, "store and bytes must be non-NULL");
+    if (s->pool_view) {
+        *bytes = s->view_payload;
+        return MKV_OK;
+    }
     hipError_t e = hipMemcpyAsync(bytes, s->base, sizeof(uint64_t), hipMemcpyDeviceToHost, reinterpret_cast<hipStream_t>(stream));
     if (e == hipSuccess) e = hipStreamSynchronize(reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(MKV_E_DEVICE, "payload size read failed: %s", hipGetErrorString(e));
@@ -502,12 +519,424 @@ mkv_status mkv_store_destroy(mkv_store* s) {
     return MKV_OK;
 }
 
+// ---- paged pools -------------------------------------------------------------------------------------------
+namespace {
+
+struct PoolLayout {
+    uint64_t codes, seg_off, basis, payload, bytes;
+};
+
+int64_t pool_max_segment_bytes(mkv_dtype dt) { return (int64_t)MKV_SEG_LEN * MKV_HEAD_DIM * dtype_bytes(dt); }
+
+mkv_status check_pool_desc(const mkv_pool_desc* d) {
+    if (!d) return fail(MKV_E_ARG, "pool descriptor is NULL");
+    if (d->n_kv_heads < 1) return fail(MKV_E_ARG, "n_kv_heads must be >= 1 (got %d)", d->n_kv_heads);
+    if (d->dtype != MKV_BF16 && d->dtype != MKV_FP32) return fail(MKV_E_ARG, "unknown dtype %d", (int)d->dtype);
+    if (d->max_requests < 1) return fail(MKV_E_ARG, "max_requests must be >= 1 (got %d)", d->max_requests);
+    if (d->segment_slots < 0) return fail(MKV_E_ARG, "segment_slots must be >= 0");
+    if (d->segment_slots * (int64_t)d->n_kv_heads >= (int64_t)INT32_MAX)
+        return fail(MKV_E_UNSUPPORTED, "segment_slots x n_kv_heads must stay below 2^31");
+    if (d->n_pages < 1 || d->n_pages >= (int64_t)INT32_MAX) return fail(MKV_E_ARG, "n_pages must be in [1, 2^31)");
+    if (d->page_bytes % kAlign != 0 || d->page_bytes < pool_max_segment_bytes(d->dtype) || d->page_bytes > (1ll << 31))
+        return fail(MKV_E_ARG, "page_bytes (%lld) must be a multiple of 256 in [%lld, 2^31]", (long long)d->page_bytes,
+                    (long long)pool_max_segment_bytes(d->dtype));
+    return MKV_OK;
+}
+
+PoolLayout pool_layout(const mkv_pool_desc& d) {
+    PoolLayout L;
+    const uint64_t S = (uint64_t)d.segment_slots * d.n_kv_heads;
+    L.codes = kAlign;
+    L.seg_off = align_up(L.codes + 2 * S);
+    L.basis = align_up(L.seg_off + 16 * S);
+    L.payload = align_up(L.basis + (d.has_basis ? (uint64_t)d.max_requests * d.n_kv_heads * 2 * MKV_HEAD_DIM *
+                                                     MKV_HEAD_DIM * sizeof(float) : 0));
+    L.bytes = L.payload + (uint64_t)d.n_pages * d.page_bytes + kAlign;   // slack: fixed-shape row loads may read past
+    return L;
+}
+
+// Pages one stream of a request can take: every page holds at least floor(page_bytes / largest segment) whole
+// segments.
+int64_t pool_pages_bound(const mkv_pool_desc& d, int64_t segments) {
+    return cdiv(segments, d.page_bytes / pool_max_segment_bytes(d.dtype));
+}
+
+struct PoolScratch {
+    uint64_t cmp, pages, used, list_base, page_ids, bytes;
+};
+
+PoolScratch pool_scratch_layout(const mkv_pool_desc& d, const Shape& ash) {
+    PoolScratch L;
+    const uint64_t streams = 2ull * ash.B * ash.Hkv;
+    int64_t ids = 0;
+    for (int r = 0; r < ash.B; ++r) ids += 2ll * ash.Hkv * pool_pages_bound(d, cdiv(ash.cu[r + 1] - ash.cu[r], MKV_SEG_LEN));
+    L.cmp = 0;
+    L.pages = align_up(scratch_layout(ash).bytes);
+    L.used = align_up(L.pages + 4 * streams);
+    L.list_base = align_up(L.used + 8 * streams);
+    L.page_ids = align_up(L.list_base + 4 * streams);
+    L.bytes = align_up(L.page_ids + 4 * (uint64_t)std::max<int64_t>(ids, 1));
+    return L;
+}
+
+}  // namespace
+
+struct mkv_pool {
+    mkv_pool_desc d;
+    mkv_seg_policy policy;
+    PoolLayout lay;
+    uint8_t* base = nullptr;
+    std::vector<int32_t> free_pages;           // stack: the next page handed out is at the back
+    std::map<int64_t, int64_t> free_ranges;    // free segment-slot ranges (units of n_kv_heads slots): start -> length
+    struct Req {
+        int64_t n = -1;                        // tokens; -1: the id is free
+        int32_t ubase = 0, scap = 0;           // first slot unit and slots per stream
+        std::vector<int32_t> pages;
+        uint64_t payload = 0;
+    };
+    std::vector<Req> req;
+    std::vector<int32_t> free_ids;             // stack
+    int32_t live = 0;
+};
+
+namespace {
+
+// First fit over the free slot ranges; -1 if no range is long enough.  Empty requests take no slots.
+int64_t pool_take_range(mkv_pool* p, int64_t len) {
+    if (len == 0) return 0;
+    for (auto it = p->free_ranges.begin(); it != p->free_ranges.end(); ++it) {
+        if (it->second < len) continue;
+        const int64_t start = it->first, rest = it->second - len;
+        p->free_ranges.erase(it);
+        if (rest > 0) p->free_ranges[start + len] = rest;
+        return start;
+    }
+    return -1;
+}
+
+void pool_give_range(mkv_pool* p, int64_t start, int64_t len) {
+    if (len == 0) return;
+    auto next = p->free_ranges.lower_bound(start);
+    if (next != p->free_ranges.end() && start + len == next->first) {
+        len += next->second;
+        next = p->free_ranges.erase(next);
+    }
+    if (next != p->free_ranges.begin()) {
+        auto prev = std::prev(next);
+        if (prev->first + prev->second == start) {
+            prev->second += len;
+            return;
+        }
+    }
+    p->free_ranges[start] = len;
+}
+
+// Returns an id (with its slots and pages) to the free lists.
+void pool_release(mkv_pool* p, int32_t id) {
+    mkv_pool::Req& q = p->req[id];
+    pool_give_range(p, q.ubase, q.scap);
+    for (auto it = q.pages.rbegin(); it != q.pages.rend(); ++it) p->free_pages.push_back(*it);
+    q = mkv_pool::Req();
+    p->free_ids.push_back(id);
+    --p->live;
+}
+
+}  // namespace
+
+mkv_status mkv_pool_bytes(const mkv_pool_desc* desc, size_t* pool_bytes) {
+    mkv_status st = check_pool_desc(desc);
+    if (st) return st;
+    if (!pool_bytes) return fail(MKV_E_ARG, "pool_bytes is NULL");
+    *pool_bytes = pool_layout(*desc).bytes;
+    return MKV_OK;
+}
+
+mkv_status mkv_pool_create(const mkv_pool_desc* desc, const mkv_seg_policy* policy, void* pool_buf,
+                           size_t pool_bytes, mkv_pool** out) {
+    mkv_status st = check_pool_desc(desc);
+    if (st) return st;
+    if ((st = check_policy(policy, desc->dtype))) return st;
+    if (!pool_buf || !out) return fail(MKV_E_ARG, "pool_buf and out must be non-NULL");
+    if (!aligned(pool_buf)) return fail(MKV_E_ARG, "pool_buf must be 256-byte aligned");
+    const PoolLayout L = pool_layout(*desc);
+    if (pool_bytes < L.bytes) return fail(MKV_E_ARG, "pool_bytes %zu < required %llu", pool_bytes, (unsigned long long)L.bytes);
+    mkv_pool* p = new (std::nothrow) mkv_pool;
+    if (!p) return fail(MKV_E_ARG, "out of host memory");
+    p->d = *desc;
+    p->policy = *policy;
+    p->lay = L;
+    p->base = static_cast<uint8_t*>(pool_buf);
+    p->free_pages.resize(desc->n_pages);
+    for (int64_t i = 0; i < desc->n_pages; ++i) p->free_pages[i] = (int32_t)(desc->n_pages - 1 - i);   // page 0 first
+    if (desc->segment_slots > 0) p->free_ranges[0] = desc->segment_slots;
+    p->req.resize(desc->max_requests);
+    for (int32_t i = desc->max_requests - 1; i >= 0; --i) p->free_ids.push_back(i);   // id 0 first
+    *out = p;
+    return MKV_OK;
+}
+
+mkv_status mkv_pool_destroy(mkv_pool* p) {
+    delete p;
+    return MKV_OK;
+}
+
+static mkv_status pool_add_shape(const mkv_pool* p, const mkv_kv_desc* kv, bool need_data, Shape* ash) {
+    if (!p) return fail(MKV_E_ARG, "pool is NULL");
+    mkv_status st = check_kv(kv, need_data, ash);
+    if (st) return st;
+    if (ash->Hkv != p->d.n_kv_heads) return fail(MKV_E_ARG, "n_kv_heads %d differs from the pool's %d", ash->Hkv, p->d.n_kv_heads);
+    if (ash->dtype != p->d.dtype) return fail(MKV_E_ARG, "dtype differs from the pool's");
+    return MKV_OK;
+}
+
+mkv_status mkv_pool_add_scratch_bytes(const mkv_pool* p, const mkv_kv_desc* kv, size_t* scratch_bytes) {
+    Shape ash;
+    mkv_status st = pool_add_shape(p, kv, false, &ash);
+    if (st) return st;
+    if (!scratch_bytes) return fail(MKV_E_ARG, "scratch_bytes is NULL");
+    *scratch_bytes = pool_scratch_layout(p->d, ash).bytes;
+    return MKV_OK;
+}
+
+mkv_status mkv_pool_add(mkv_pool* p, const mkv_kv_desc* kv, const float* basis, void* scratch, size_t scratch_bytes,
+                        mkv_stream_t stream_, int32_t* ids) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    Shape ash;
+    mkv_status st = pool_add_shape(p, kv, true, &ash);
+    if (st) return st;
+    if (!ids) return fail(MKV_E_ARG, "ids is NULL");
+    if (!scratch || !aligned(scratch)) return fail(MKV_E_ARG, "scratch must be non-NULL and 256-byte aligned");
+    if ((basis != nullptr) != (p->d.has_basis != 0))
+        return fail(MKV_E_ARG, p->d.has_basis ? "the pool keeps bases: basis must be non-NULL" : "the pool keeps no bases: basis must be NULL");
+    const PoolScratch SL = pool_scratch_layout(p->d, ash);
+    if (scratch_bytes < SL.bytes) return fail(MKV_E_ARG, "scratch_bytes %zu < required %llu", scratch_bytes, (unsigned long long)SL.bytes);
+    const int B = ash.B, Hkv = ash.Hkv;
+    if ((int)p->free_ids.size() < B) return fail(MKV_E_ARG, "the pool has %zu free request ids, %d requested", p->free_ids.size(), B);
+
+    // request ids and segment-slot ranges (host bookkeeping; undone if anything below fails)
+    std::vector<int32_t> got;
+    auto undo = [&] { for (auto it = got.rbegin(); it != got.rend(); ++it) pool_release(p, *it); };
+    for (int r = 0; r < B; ++r) {
+        const int64_t n = ash.cu[r + 1] - ash.cu[r];
+        const int32_t scap = (int32_t)cdiv(n, MKV_SEG_LEN);
+        const int64_t ub = pool_take_range(p, scap);
+        if (ub < 0) {
+            undo();
+            return fail(MKV_E_ARG, "no free run of %d segment slots for request %d (pool segment_slots %lld)", scap, r,
+                        (long long)p->d.segment_slots);
+        }
+        const int32_t id = p->free_ids.back();
+        p->free_ids.pop_back();
+        ++p->live;
+        mkv_pool::Req& q = p->req[id];
+        q.n = n;
+        q.ubase = (int32_t)ub;
+        q.scap = scap;
+        got.push_back(id);
+    }
+
+    uint8_t* scr = static_cast<uint8_t*>(scratch);
+    const ScratchLayout CL = scratch_layout(ash);
+    const int64_t spw = cmp_plan(ash).spw;
+    std::vector<int32_t> tab(5 * B + 1);
+    int64_t nblk = 0;
+    for (int r = 0; r < B; ++r) {
+        const int64_t n = ash.cu[r + 1] - ash.cu[r];
+        tab[r] = (int32_t)ash.cu[r];
+        tab[B + r] = (int32_t)n;
+        tab[2 * B + r] = p->req[got[r]].ubase;
+        tab[3 * B + r] = p->req[got[r]].scap;
+        tab[4 * B + r] = (int32_t)nblk;
+        nblk += (int64_t)Hkv * cdiv(cdiv(n, MKV_SEG_LEN), spw);
+    }
+    tab[5 * B] = (int32_t)nblk;
+    if (2 * nblk > INT32_MAX) { undo(); return fail(MKV_E_UNSUPPORTED, "too many workgroups"); }
+    const int64_t S = p->d.segment_slots * Hkv;
+    const int streams = 2 * B * Hkv;
+
+    CmpArgs a;
+    std::memset(&a, 0, sizeof a);
+    a.K = kv->K;
+    a.V = kv->V;
+    a.basis = basis;            // the caller's copy, indexed like the batch; the pool keeps its own below
+    a.tab = reinterpret_cast<const int32_t*>(scr + CL.tab);
+    a.B = B;
+    a.Hkv = Hkv;
+    a.spw = (int32_t)spw;
+    a.nblk = (int32_t)nblk;
+    a.S = S;
+    a.total_tokens = ash.total;
+    a.codes = p->base + p->lay.codes;
+    a.seg_off = reinterpret_cast<uint64_t*>(p->base + p->lay.seg_off);
+    a.payload = p->base + p->lay.payload;
+    a.thr = reinterpret_cast<uint16_t*>(scr + CL.thr);
+    a.wg_total = reinterpret_cast<uint64_t*>(scr + CL.wg);
+    for (int k = 0; k < 4; ++k) a.keep[k] = k < p->policy.n_keep ? p->policy.keep[k] : 0;
+    a.n_keep = p->policy.n_keep;
+    a.frac = p->policy.energy_frac;
+    a.preplaced = 1;
+    PoolArgs pa;
+    std::memset(&pa, 0, sizeof pa);
+    pa.tab = a.tab;
+    pa.B = B;
+    pa.Hkv = Hkv;
+    pa.bv = dtype_bytes(ash.dtype);
+    pa.S = S;
+    for (int k = 0; k < 4; ++k) pa.keep[k] = a.keep[k];
+    pa.codes = a.codes;
+    pa.seg_off = a.seg_off;
+    pa.page_bytes = (uint64_t)p->d.page_bytes;
+    pa.pages = reinterpret_cast<int32_t*>(scr + SL.pages);
+    pa.used = reinterpret_cast<uint64_t*>(scr + SL.used);
+    pa.list_base = reinterpret_cast<const int32_t*>(scr + SL.list_base);
+    pa.page_ids = reinterpret_cast<const int32_t*>(scr + SL.page_ids);
+    const int dt = ash.dtype == MKV_BF16 ? 1 : 0;
+
+    // 1. decide every segment's kept count, 2. place the segments into pages (ordinals), then read the page
+    // counts back: the pages a request needs depend on its data
+    if ((st = upload_words(reinterpret_cast<int32_t*>(scr + CL.tab), tab, 0, stream))) { undo(); return st; }
+    if ((st = run(K_CMP_DECIDE, stream, [&] { return launch_cmp_decide(a, dt, stream); }))) { undo(); return st; }
+    if ((st = run(K_POOL_PLACE, stream, [&] { return launch_pool_place(pa, streams, stream); }))) { undo(); return st; }
+    std::vector<int32_t> need(streams);
+    std::vector<uint64_t> used(streams);
+    hipError_t e = hipMemcpyAsync(need.data(), pa.pages, 4ull * streams, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipMemcpyAsync(used.data(), pa.used, 8ull * streams, hipMemcpyDeviceToHost, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) { undo(); return fail(MKV_E_DEVICE, "page count read-back failed: %s", hipGetErrorString(e)); }
+    int64_t total = 0;
+    for (int i = 0; i < streams; ++i) total += need[i];
+    if (total > (int64_t)p->free_pages.size()) {
+        undo();
+        return fail(MKV_E_ARG, "the pool has %zu free pages, the new requests need %lld", p->free_pages.size(),
+                    (long long)total);
+    }
+    // 3. hand out pages in stream order, 4. turn ordinals into payload offsets, 5. pack
+    std::vector<int32_t> lists(streams + total);
+    int64_t k = streams;
+    for (int i = 0; i < streams; ++i) {
+        lists[i] = (int32_t)(k - streams);
+        mkv_pool::Req& q = p->req[got[i / (2 * Hkv)]];
+        for (int j = 0; j < need[i]; ++j) {
+            const int32_t pg = p->free_pages.back();
+            p->free_pages.pop_back();
+            q.pages.push_back(pg);
+            lists[k++] = pg;
+        }
+        q.payload += used[i];
+    }
+    static_assert(sizeof(int32_t) == 4, "");
+    e = hipMemcpyAsync(scr + SL.list_base, lists.data(), 4ull * streams, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess && total > 0)
+        e = hipMemcpyAsync(scr + SL.page_ids, lists.data() + streams, 4ull * total, hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);   // the host lists go out of scope below
+    if (e != hipSuccess) { undo(); return fail(MKV_E_DEVICE, "page list upload failed: %s", hipGetErrorString(e)); }
+    if ((st = run(K_POOL_FIX, stream, [&] { return launch_pool_fix(pa, streams, stream); }))) { undo(); return st; }
+    if ((st = run(K_CMP_PACK, stream, [&] { return launch_cmp_pack(a, dt, stream); }))) { undo(); return st; }
+    if (basis) {
+        const size_t per = (size_t)Hkv * 2 * MKV_HEAD_DIM * MKV_HEAD_DIM * sizeof(float);
+        for (int r = 0; r < B; ++r) {
+            e = hipMemcpyAsync(p->base + p->lay.basis + per * got[r], reinterpret_cast<const uint8_t*>(basis) + per * r,
+                               per, hipMemcpyDeviceToDevice, stream);
+            if (e != hipSuccess) { undo(); return fail(MKV_E_DEVICE, "basis copy failed: %s", hipGetErrorString(e)); }
+        }
+    }
+    for (int r = 0; r < B; ++r) ids[r] = got[r];
+    return MKV_OK;
+}
+
+mkv_status mkv_pool_remove(mkv_pool* p, int32_t n, const int32_t* ids) {
+    if (!p) return fail(MKV_E_ARG, "pool is NULL");
+    if (n < 0 || (n > 0 && !ids)) return fail(MKV_E_ARG, "ids must list n >= 0 request ids");
+    for (int32_t i = 0; i < n; ++i) {
+        if (ids[i] < 0 || ids[i] >= p->d.max_requests || p->req[ids[i]].n < 0)
+            return fail(MKV_E_ARG, "request id %d is not in the pool", ids[i]);
+        for (int32_t j = 0; j < i; ++j)
+            if (ids[j] == ids[i]) return fail(MKV_E_ARG, "request id %d is listed twice", ids[i]);
+    }
+    for (int32_t i = 0; i < n; ++i) pool_release(p, ids[i]);
+    return MKV_OK;
+}
+
+mkv_status mkv_pool_view(const mkv_pool* p, int32_t n, const int32_t* ids, mkv_store** out) {
+    if (!p || !out) return fail(MKV_E_ARG, "pool and out must be non-NULL");
+    if (n < 1 || !ids) return fail(MKV_E_ARG, "a view lists n >= 1 request ids");
+    Shape sh;
+    sh.B = n;
+    sh.Hkv = p->d.n_kv_heads;
+    sh.dtype = p->d.dtype;
+    sh.cu.assign(1, 0);
+    uint64_t payload = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        if (ids[i] < 0 || ids[i] >= p->d.max_requests || p->req[ids[i]].n < 0)
+            return fail(MKV_E_ARG, "request id %d is not in the pool", ids[i]);
+        const mkv_pool::Req& q = p->req[ids[i]];
+        sh.cu.push_back(sh.cu.back() + q.n);
+        sh.cap.push_back(q.n);
+        sh.scap.push_back(q.scap);
+        sh.segbase.push_back(q.ubase);
+        sh.bslot.push_back(ids[i]);
+        payload += q.payload;
+    }
+    sh.total = sh.cu.back();
+    sh.total_cap = sh.total;
+    if (sh.total * (int64_t)sh.Hkv >= (int64_t)INT32_MAX)
+        return fail(MKV_E_UNSUPPORTED, "total tokens x KV heads must stay below 2^31 (got %lld)", (long long)(sh.total * sh.Hkv));
+    sh.S = p->d.segment_slots * sh.Hkv;
+    sh.growable = false;
+    mkv_store* h = new (std::nothrow) mkv_store;
+    if (!h) return fail(MKV_E_ARG, "out of host memory");
+    h->sh = sh;
+    h->policy = p->policy;
+    h->has_basis = p->d.has_basis ? 1 : 0;
+    h->lay.codes = p->lay.codes;
+    h->lay.seg_off = p->lay.seg_off;
+    h->lay.basis = p->lay.basis;
+    h->lay.payload = p->lay.payload;
+    h->lay.capacity = (uint64_t)p->d.n_pages * p->d.page_bytes;
+    h->lay.open_pack = h->lay.open_rows = h->lay.open_bytes = 0;
+    h->lay.bytes = p->lay.bytes;
+    h->base = p->base;
+    h->cu_cap = sh.cu;
+    h->pool_view = true;
+    h->view_payload = payload;
+    *out = h;
+    return MKV_OK;
+}
+
+mkv_status mkv_pool_stats(const mkv_pool* p, mkv_pool_info* info) {
+    if (!p || !info) return fail(MKV_E_ARG, "pool and info must be non-NULL");
+    std::memset(info, 0, sizeof *info);
+    info->desc = p->d;
+    info->live_requests = p->live;
+    info->free_pages = (int64_t)p->free_pages.size();
+    for (const auto& fr : p->free_ranges) {
+        info->free_segment_slots += fr.second;
+        info->largest_free_run = std::max<int64_t>(info->largest_free_run, fr.second);
+    }
+    info->codes = p->base + p->lay.codes;
+    info->seg_off = p->base + p->lay.seg_off;
+    info->basis = p->d.has_basis ? p->base + p->lay.basis : nullptr;
+    info->payload = p->base + p->lay.payload;
+    info->pool_bytes = p->lay.bytes;
+    return MKV_OK;
+}
+
+mkv_status mkv_pool_request(const mkv_pool* p, int32_t id, int64_t* n_tokens, int64_t* pages, uint64_t* payload_bytes) {
+    if (!p) return fail(MKV_E_ARG, "pool is NULL");
+    if (id < 0 || id >= p->d.max_requests || p->req[id].n < 0) return fail(MKV_E_ARG, "request id %d is not in the pool", id);
+    const mkv_pool::Req& q = p->req[id];
+    if (n_tokens) *n_tokens = q.n;
+    if (pages) *pages = (int64_t)q.pages.size();
+    if (payload_bytes) *payload_bytes = q.payload;
+    return MKV_OK;
+}
+
 // ---- decode ------------------------------------------------------------------------------------------------
 namespace {
 
 struct DecPlan {
     int32_t G = 0, Hq = 0, spw = 0, sgx = 0, max_T = 0;
-    std::vector<int32_t> tab;    // n | segbase | tokbase | T | kblk | ablk
+    std::vector<int32_t> tab;    // n | segbase | scap | tokbase | T | kblk | ablk | basis slot
     int64_t n_sblk = 0, n_kblk = 0, n_ablk = 0;
     uint64_t o_tab, o_state, o_hist, o_qp, o_qbar, o_keys, o_L, o_sel, o_part, bytes;
 };
@@ -526,7 +955,7 @@ mkv_status plan_decode(const mkv_store* s, int32_t n_q_heads, const int32_t* T, 
     int64_t s_cur = 0;   // segments in use (the capacity may hold more)
     for (int r = 0; r < B; ++r) s_cur += (int64_t)sh.Hkv * cdiv(sh.cu[r + 1] - sh.cu[r], MKV_SEG_LEN);
     P->spw = (int32_t)(std::max<int64_t>(4, std::min<int64_t>(16, s_cur / 16384)) & ~3ll);
-    P->tab.assign(7 * B + 2, 0);
+    P->tab.assign(8 * B + 2, 0);
     int32_t* tn = P->tab.data();
     int32_t* tseg = tn + B;
     int32_t* tscap = tseg + B;
@@ -534,6 +963,7 @@ mkv_status plan_decode(const mkv_store* s, int32_t n_q_heads, const int32_t* T, 
     int32_t* tT = ttok + B;
     int32_t* tkb = tT + B;
     int32_t* tab_ = tkb + B + 1;
+    int32_t* tbs = tab_ + B + 1;
     int64_t sgx = 0, kb = 0, ab = 0, kpad = 0;
     for (int r = 0; r < B; ++r) {
         if (T[r] < 1) return fail(MKV_E_ARG, "T[%d] = %d must be >= 1", r, T[r]);
@@ -545,6 +975,7 @@ mkv_status plan_decode(const mkv_store* s, int32_t n_q_heads, const int32_t* T, 
         ttok[r] = (int32_t)kpad;          // keys of request r start at Hkv * (earlier contexts padded to 64)
         kpad += cdiv(n, 64) * 64;
         tT[r] = (int32_t)te;
+        tbs[r] = sh.bslot[r];
         tkb[r] = (int32_t)kb;
         tab_[r] = (int32_t)ab;
         sgx = std::max<int64_t>(sgx, cdiv(cdiv(n, MKV_SEG_LEN), P->spw));
@@ -625,6 +1056,7 @@ mkv_status mkv_decode_attn(const mkv_store* s, const void* q, int32_t n_q_heads,
     a.t_T = tb + 4 * sh.B;
     a.t_kblk = tb + 5 * sh.B;
     a.t_ablk = tb + 6 * sh.B + 1;
+    a.t_bslot = tb + 7 * sh.B + 2;
     a.spw = P.spw;
     a.sgx = P.sgx;
     a.qp = reinterpret_cast<float*>(w + P.o_qp);

@@ -545,8 +545,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         } else {
             const int code = a.codes[gs];
             const int c = a.keep[code];
-            uint8_t* dst = a.payload + wg_off;
-            if (tid == 0) a.seg_off[gs] = wg_off;
+            uint8_t* dst = a.payload + (a.preplaced ? a.seg_off[gs] : wg_off);
+            if (!a.preplaced && tid == 0) a.seg_off[gs] = wg_off;
             wg_off += (uint64_t)ns * c * (2 + (c < MKV_D ? 1 : 0));
             if (a.open_rows && ns < MKV_SEG && lrow < ns) {
                 // growable store: the stream's unfinished last segment keeps its original rows for appends
@@ -759,8 +759,8 @@ __global__ __launch_bounds__(256) void k_cmp_f32(CmpArgs a) {
         } else {
             const int code = a.codes[gs];
             const int c = a.keep[code];
-            uint8_t* dst = a.payload + wg_off;
-            if (tid == 0) a.seg_off[gs] = wg_off;
+            uint8_t* dst = a.payload + (a.preplaced ? a.seg_off[gs] : wg_off);
+            if (!a.preplaced && tid == 0) a.seg_off[gs] = wg_off;
             wg_off += (uint64_t)ns * c * (4 + (c < MKV_D ? 1 : 0));
             if (c == MKV_D) {
                 const int nq = ns * 32;   // 16-byte pieces of ns rows of 512 bytes
@@ -839,6 +839,75 @@ __global__ __launch_bounds__(1024) void k_cmp_scan(uint64_t* a, int64_t n, uint6
 
 hipError_t launch_cmp_scan(uint64_t* wg_total, int64_t count, uint64_t* total, hipStream_t s) {
     hipLaunchKernelGGL(k_cmp_scan, dim3(1), dim3(1024), 0, s, wg_total, count, total);
+    return hipGetLastError();
+}
+
+// =====================================================================================================
+// paged pools: segment placement into fixed-size pages
+// =====================================================================================================
+// One wave per (request, KV head, tensor) stream of the requests being added.  The stream's segments go into
+// its pages in segment order, each segment whole (it never straddles two pages, so the decode kernels' per-
+// segment reads stay contiguous): a segment that does not fit in the rest of the current page opens the next
+// page.  Until the host has picked the pages, seg_off holds (page ordinal << 32) | byte offset in the page.
+// The walk runs over the segment sizes of 64 segments at a time, held one per lane and read back in order.
+__global__ __launch_bounds__(64) void k_pool_place(PoolArgs p) {
+    const int st = blockIdx.x;                       // (r * Hkv + h) * 2 + X
+    const int X = st & 1, rh = st >> 1, r = rh / p.Hkv, h = rh - r * p.Hkv;
+    const int n = p.tab[p.B + r];
+    const int nseg = (n + MKV_SEG - 1) / MKV_SEG;
+    const int64_t g0 = X * p.S + (int64_t)p.Hkv * p.tab[2 * p.B + r] + (int64_t)h * p.tab[3 * p.B + r];
+    const int lane = threadIdx.x;
+    int ord = -1;                                    // current page ordinal (-1: none yet)
+    uint32_t cur = 0;                                // bytes used in the current page
+    uint64_t used = 0;
+    for (int s0 = 0; s0 < nseg; s0 += 64) {
+        const int s = s0 + lane;
+        uint32_t bytes = 0;
+        if (s < nseg) {
+            const int c = p.keep[p.codes[g0 + s]];
+            const int ns = min(MKV_SEG, n - s * MKV_SEG);
+            bytes = (uint32_t)(ns * c * (p.bv + (c < MKV_D ? 1 : 0)));
+        }
+        uint64_t mine = 0;
+        const int m = min(64, nseg - s0);
+        for (int j = 0; j < m; ++j) {
+            const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)bytes, j);
+            if (ord < 0 || (uint64_t)cur + b > p.page_bytes) { ++ord; cur = 0; }
+            if (lane == j) mine = ((uint64_t)ord << 32) | cur;
+            cur += b;
+            used += b;
+        }
+        if (s < nseg) p.seg_off[g0 + s] = mine;
+    }
+    if (lane == 0) {
+        p.pages[st] = ord + 1;
+        p.used[st] = used;
+    }
+}
+
+// Replaces each placed segment's (page ordinal, offset) by its payload offset in the page the host assigned.
+__global__ __launch_bounds__(256) void k_pool_fix(PoolArgs p) {
+    const int st = blockIdx.x;
+    const int X = st & 1, rh = st >> 1, r = rh / p.Hkv, h = rh - r * p.Hkv;
+    const int n = p.tab[p.B + r];
+    const int nseg = (n + MKV_SEG - 1) / MKV_SEG;
+    const int64_t g0 = X * p.S + (int64_t)p.Hkv * p.tab[2 * p.B + r] + (int64_t)h * p.tab[3 * p.B + r];
+    const int first = p.list_base[st];
+    for (int s = threadIdx.x; s < nseg; s += 256) {
+        const uint64_t v = p.seg_off[g0 + s];
+        p.seg_off[g0 + s] = (uint64_t)p.page_ids[first + (int)(v >> 32)] * p.page_bytes + (uint32_t)v;
+    }
+}
+
+hipError_t launch_pool_place(const PoolArgs& p, int n_streams, hipStream_t s) {
+    if (n_streams == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_pool_place, dim3(n_streams), dim3(64), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_pool_fix(const PoolArgs& p, int n_streams, hipStream_t s) {
+    if (n_streams == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_pool_fix, dim3(n_streams), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

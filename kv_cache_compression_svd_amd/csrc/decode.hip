@@ -71,7 +71,11 @@ __global__ __launch_bounds__(256) void k_dec_prep(DecArgs a, Upload tab) {
         for (int i = tid; i < tab.n; i += 256) tab.dst[i] = tab.w[i];
     const int stream = blockIdx.x >> 2, qd = blockIdx.x & 3, r = stream / a.Hkv, g = stream - r * a.Hkv;
     const int G = a.G, Hq = a.G * a.Hkv;
-    const float* Bk = a.basis ? a.basis + ((((size_t)r * a.Hkv + g) * 2) << 14) : nullptr;
+    // the basis slot comes from the table words this launch carries when they include it (workgroup 0 writes
+    // those words to memory during this kernel), else from memory, written by an earlier upload
+    const int bi = (int)(a.t_bslot - tab.dst) + r;
+    const int bslot = bi < tab.n ? tab.w[bi] : a.t_bslot[r];
+    const float* Bk = a.basis ? a.basis + ((((size_t)bslot * a.Hkv + g) * 2) << 14) : nullptr;
     f32x4 v[4];
     if (Bk) {   // rows 0..127, columns [32 qd, 32 qd + 32): 1024 16-byte pieces, 4 per thread
 #pragma unroll
@@ -903,7 +907,7 @@ __global__ __launch_bounds__(256) void k_combine(DecArgs a) {
     const int first = a.t_ablk[r] + g * nach;
     const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int Hq = a.G * a.Hkv;
-    const float* Bv = a.basis ? a.basis + ((((size_t)r * a.Hkv + g) * 2 + 1) << 14) : nullptr;
+    const float* Bv = a.basis ? a.basis + ((((size_t)a.t_bslot[r] * a.Hkv + g) * 2 + 1) << 14) : nullptr;
     f32x4 bvr[16];
     if (Bv) {   // issue the basis loads first: their latency overlaps the merge
         const f32x4* src = reinterpret_cast<const f32x4*>(Bv);

@@ -42,6 +42,22 @@ struct CmpArgs {
     double frac;
     uint16_t* open_rows;        // growable stores: original rows of each stream's open segment (else null)
     int64_t open_elems;         // elements per stream in open_rows
+    int32_t preplaced;          // pack: seg_off already holds every segment's payload offset (paged pools)
+};
+
+// Paged pools: placement of the segments of the requests being added (tab as in CmpArgs).
+struct PoolArgs {
+    const int32_t* tab;
+    int32_t B, Hkv, bv;
+    int64_t S;
+    int32_t keep[4];
+    const uint8_t* codes;
+    uint64_t* seg_off;
+    uint64_t page_bytes;
+    int32_t* pages;             // [2*B*Hkv] pages each stream needs (place)
+    uint64_t* used;             // [2*B*Hkv] payload bytes of each stream (place)
+    const int32_t* list_base;   // [2*B*Hkv] first entry of each stream in page_ids (fix)
+    const int32_t* page_ids;    // page of each (stream, ordinal) (fix)
 };
 
 // One token appended to each listed request of a growable bf16 store.
@@ -66,6 +82,8 @@ hipError_t launch_cmp_append(const CmpArgs& a, const AppendArgs& x, int n_reques
 hipError_t launch_cmp_decide(const CmpArgs& a, int dtype, hipStream_t s);
 hipError_t launch_cmp_scan(uint64_t* wg_total, int64_t count, uint64_t* total, hipStream_t s);
 hipError_t launch_cmp_pack(const CmpArgs& a, int dtype, hipStream_t s);
+hipError_t launch_pool_place(const PoolArgs& p, int n_streams, hipStream_t s);
+hipError_t launch_pool_fix(const PoolArgs& p, int n_streams, hipStream_t s);
 
 // ---- decode -------------------------------------------------------------------------------------------
 struct DecArgs {
@@ -91,6 +109,7 @@ struct DecArgs {
     const int32_t* t_T;
     const int32_t* t_kblk;
     const int32_t* t_ablk;
+    const int32_t* t_bslot;     // basis slot of each request (its index unless the store is a pool view)
     int32_t spw;                // segments per score workgroup (a multiple of 4)
     int32_t sgx;                // score workgroups per stream in the grid (the most any request needs)
     float* qp;                  // [B][Hq][128]

@@ -78,10 +78,22 @@ def _parse_segment(payload: np.ndarray, off: int, ns: int, c: int, dtype: str):
     return idx, v
 
 
-def _stream_from(payload, codes, seg_off, pay_base, keep, r, h, X, S, Hkv, cu, dtype, cu_cap=None) -> Stream:
-    """Stream (r, h, X) of a store: cu gives the tokens in use, cu_cap the capacities the segment slots follow."""
+def slot_layout(info):
+    """(S_r, seg_base) of a store's segment numbering, as the library reports them."""
+    B = int(info.batch)
+    S_r = np.array([info.seg_slots[i] for i in range(B)], dtype=np.int64)
+    seg_base = np.array([info.seg_base[i] for i in range(B)], dtype=np.int64)
+    return S_r, seg_base
+
+
+def _stream_from(payload, codes, seg_off, pay_base, keep, r, h, X, S, Hkv, cu, dtype, layout=None) -> Stream:
+    """Stream (r, h, X) of a store: cu gives the tokens in use, layout = (S_r, seg_base) the segment slots
+    (None: slots follow cu)."""
     n, S_use, _ = seg_counts(cu)
-    _, S_r, seg_base = seg_counts(cu if cu_cap is None else cu_cap)
+    if layout is None:
+        _, S_r, seg_base = seg_counts(cu)
+    else:
+        S_r, seg_base = layout
     nr = int(n[r])
     mask = np.zeros((nr, D), dtype=bool)
     vals = np.zeros((nr, D))
@@ -117,13 +129,13 @@ def read_store(store, dtype: str) -> dict:
     payload = buf[o_pay:]          # packed segments, then (growable stores) the open-segment areas
     B = int(info.batch)
     cu = np.array([info.cu_seqlens[i] for i in range(B + 1)], dtype=np.int64)
-    cu_cap = np.array([info.cu_capacity[i] for i in range(B + 1)], dtype=np.int64)
+    layout = slot_layout(info)
     n, _, _ = seg_counts(cu)
     out = {}
     for r in range(len(n)):
         for h in range(Hkv):
             for X in (0, 1):
-                out[(r, h, X)] = _stream_from(payload, codes, seg_off, 0, keep, r, h, X, S, Hkv, cu, dtype, cu_cap)
+                out[(r, h, X)] = _stream_from(payload, codes, seg_off, 0, keep, r, h, X, S, Hkv, cu, dtype, layout)
     return {"streams": out, "codes": codes, "seg_off": seg_off, "total": total, "S": S}
 
 
@@ -144,12 +156,12 @@ class StoreReader:
         self.total = int(store.buf[0:8].cpu().numpy().view(np.uint64)[0])
         B = int(info.batch)
         self.cu = np.array([info.cu_seqlens[i] for i in range(B + 1)], dtype=np.int64)
-        self.cu_cap = np.array([info.cu_capacity[i] for i in range(B + 1)], dtype=np.int64)
+        self.layout = slot_layout(info)
 
     def segment_bytes(self, bv: int) -> np.ndarray:
         """Payload bytes of every segment slot implied by its code (K slots, then V slots; 0 for unused slots)."""
         n, S_use, _ = seg_counts(self.cu)
-        _, S_r, seg_base = seg_counts(self.cu_cap)
+        S_r, seg_base = self.layout
         ns = np.zeros(2 * self.S, dtype=np.int64)
         for X in (0, 1):
             for r in range(len(n)):
@@ -164,7 +176,7 @@ class StoreReader:
 
     def stream(self, r: int, h: int, X: int) -> Stream:
         n, S_use, _ = seg_counts(self.cu)
-        _, S_r, seg_base = seg_counts(self.cu_cap)
+        S_r, seg_base = self.layout
         if S_use[r] == 0:
             return Stream(0, D, np.zeros(0, np.int64), np.zeros(0, np.int64), np.zeros((0, D), bool), np.zeros((0, D)))
         g0 = segment_id(X, r, h, 0, self.S, self.Hkv, seg_base, S_r)
@@ -178,7 +190,7 @@ class StoreReader:
         hi = int(max(int(o) + int(sz) for o, sz in zip(offs, self._sizes[g0:g1 + 1])))
         payload = self.store.buf[self.o_pay + lo:self.o_pay + hi].cpu().numpy()
         return _stream_from(payload, self.codes, self.seg_off, lo, self.keep, r, h, X, self.S, self.Hkv,
-                            self.cu, self.dtype, self.cu_cap)
+                            self.cu, self.dtype, self.layout)
 
 
 def pack_oracle_store(streams: dict, cu, Hkv: int, dtype: str, keep: tuple):

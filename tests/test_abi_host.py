@@ -178,3 +178,68 @@ def test_growable_sizes_and_argument_checks():
     assert L.mkv_append(h, ctypes.c_void_p(256), ctypes.c_void_p(512), None, ctypes.c_void_p(1 << 20), 4096, None) == mkv.MKV_E_ARG
     assert "growable" in mkv.mkv_last_error()
     L.mkv_store_destroy(h)
+
+
+def _pool_desc(heads=2, dtype=mkv.MKV_BF16, max_req=4, slots=10, pages=8, page_bytes=16384, has_basis=1):
+    d = mkv.PoolDesc()
+    d.n_kv_heads, d.dtype, d.has_basis, d.max_requests = heads, dtype, has_basis, max_req
+    d.segment_slots, d.n_pages, d.page_bytes = slots, pages, page_bytes
+    return d
+
+
+def test_pool_layout_and_host_checks():
+    L = mkv.lib()
+    d = _pool_desc()
+    nb = ctypes.c_size_t()
+    assert L.mkv_pool_bytes(ctypes.byref(d), ctypes.byref(nb)) == mkv.MKV_OK
+    align = lambda x: (x + 255) // 256 * 256   # noqa: E731
+    S = 2 * 10
+    seg_off = align(256 + 2 * S)
+    basis = align(seg_off + 16 * S)
+    payload = align(basis + 4 * 2 * 2 * 128 * 128 * 4)
+    assert nb.value == payload + 8 * 16384 + 256
+    for field, value in (("page_bytes", 8192), ("page_bytes", 16384 + 128), ("n_pages", 0), ("max_requests", 0),
+                         ("n_kv_heads", 0), ("segment_slots", -1)):
+        bad = _pool_desc()
+        setattr(bad, field, value)
+        assert L.mkv_pool_bytes(ctypes.byref(bad), ctypes.byref(nb)) == mkv.MKV_E_ARG, field
+    assert L.mkv_pool_bytes(ctypes.byref(_pool_desc(dtype=mkv.MKV_FP32)), ctypes.byref(nb)) == mkv.MKV_E_ARG  # < 32 KiB
+    # create only records pointers: a fake aligned address is never touched by the host-side calls below
+    p = mkv.mkv_default_policy()
+    h = ctypes.c_void_p()
+    assert L.mkv_pool_create(ctypes.byref(d), ctypes.byref(p), ctypes.c_void_p(1 << 20), nb.value - 1, ctypes.byref(h)) == mkv.MKV_E_ARG
+    assert L.mkv_pool_create(ctypes.byref(d), ctypes.byref(p), ctypes.c_void_p((1 << 20) + 64), 1 << 30, ctypes.byref(h)) == mkv.MKV_E_ARG
+    L.mkv_pool_bytes(ctypes.byref(d), ctypes.byref(nb))
+    assert L.mkv_pool_create(ctypes.byref(d), ctypes.byref(p), ctypes.c_void_p(1 << 20), nb.value, ctypes.byref(h)) == mkv.MKV_OK
+    info = mkv.PoolInfo()
+    assert L.mkv_pool_stats(h, ctypes.byref(info)) == mkv.MKV_OK
+    assert (info.free_pages, info.free_segment_slots, info.largest_free_run, info.live_requests) == (8, 10, 10, 0)
+    assert info.payload == (1 << 20) + payload and info.pool_bytes == nb.value
+    ids = (ctypes.c_int32 * 2)(0, 1)
+    out = ctypes.c_void_p()
+    assert L.mkv_pool_view(h, 1, ids, ctypes.byref(out)) == mkv.MKV_E_ARG and "not in the pool" in mkv.mkv_last_error()
+    assert L.mkv_pool_remove(h, 1, ids) == mkv.MKV_E_ARG
+    assert L.mkv_pool_request(h, 0, None, None, None) == mkv.MKV_E_ARG
+    # adds whose shape or basis does not match the pool fail before anything is enqueued
+    kd, cu = _desc(batch=1, heads=3, cu=(0, 100))
+    kd.K, kd.V = ctypes.c_void_p(256), ctypes.c_void_p(512)
+    got = (ctypes.c_int32 * 1)()
+    fake = ctypes.c_void_p(1 << 24)
+    assert L.mkv_pool_add(h, ctypes.byref(kd), fake, fake, 1 << 30, None, got) == mkv.MKV_E_ARG
+    assert "n_kv_heads" in mkv.mkv_last_error()
+    kd, cu = _desc(batch=1, heads=2, cu=(0, 100))
+    kd.K, kd.V = ctypes.c_void_p(256), ctypes.c_void_p(512)
+    assert L.mkv_pool_add(h, ctypes.byref(kd), None, fake, 1 << 30, None, got) == mkv.MKV_E_ARG
+    assert "basis" in mkv.mkv_last_error()
+    sb = ctypes.c_size_t()
+    assert L.mkv_pool_add_scratch_bytes(h, ctypes.byref(kd), ctypes.byref(sb)) == mkv.MKV_OK
+    assert L.mkv_pool_add(h, ctypes.byref(kd), fake, fake, sb.value - 1, None, got) == mkv.MKV_E_ARG
+    # more requests than free ids
+    kd, cu = _desc(batch=5, heads=2, cu=(0, 1, 2, 3, 4, 5))
+    kd.K, kd.V = ctypes.c_void_p(256), ctypes.c_void_p(512)
+    got5 = (ctypes.c_int32 * 5)()
+    assert L.mkv_pool_add(h, ctypes.byref(kd), fake, fake, 1 << 30, None, got5) == mkv.MKV_E_ARG
+    assert "ids" in mkv.mkv_last_error()
+    assert L.mkv_pool_stats(h, ctypes.byref(info)) == mkv.MKV_OK
+    assert (info.free_pages, info.free_segment_slots, info.live_requests) == (8, 10, 0)
+    assert L.mkv_pool_destroy(h) == mkv.MKV_OK
