@@ -48,6 +48,8 @@ def parse():
     ap.add_argument("--workers", type=int, default=min(16, os.cpu_count() or 1))
     ap.add_argument("--no-layers", dest="layers", action="store_false",
                     help="skip the layer-batched extra (32 layers x 32768 tokens in one call)")
+    ap.add_argument("--no-pool", dest="pool", action="store_false",
+                    help="skip the paged-pool extra (the same requests added to a pool, decoded through a view)")
     return ap.parse_args()
 
 
@@ -270,6 +272,43 @@ def main():
                       "appended_tokens_per_s": w.batch / (a_ms * 1e-3)}
         del gst
 
+    # paged pool (an extra): the same requests added into a pool of 256 KiB pages, then decoded through a view
+    pool_res = None
+    if args.pool:
+        page = 256 * 1024
+        n_pages = int(payload * 1.05) // page + 2 * w.batch * w.n_kv_heads + 64
+        pool = mkv.Pool(w.n_kv_heads, mkv.MKV_BF16 if w.dtype == "bf16" else mkv.MKV_FP32, w.batch,
+                        int(np.sum((np.diff(inp.cu_seqlens) + 63) // 64)), n_pages, page, policy=policy)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ids = pool.add(K, V, inp.cu_seqlens, basis)
+        torch.cuda.synchronize()
+        add_ms = (time.perf_counter() - t0) * 1e3
+        view = pool.view(ids)
+        pout = torch.empty_like(out)
+        psel = torch.empty_like(sel)
+        pws = torch.empty(mkv.mkv_decode_workspace_bytes(view, w.n_q_heads, T), dtype=torch.uint8, device=dev)
+
+        def pstep():
+            mkv.mkv_decode_attn(view, q, T, out=pout, sel=psel, ws=pws)
+
+        for _ in range(args.warmup):
+            pstep()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            pstep()
+        torch.cuda.synchronize()
+        p_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        step()
+        torch.cuda.synchronize()
+        st = pool.stats()
+        pool_res = {"page_bytes": page, "pages_used": n_pages - int(st.free_pages), "add_ms": add_ms,
+                    "ms_per_step_view": p_ms, "context_tokens_per_s_view": total_tokens / (p_ms * 1e-3),
+                    "view_equals_store": bool(torch.equal(pout, out) and torch.equal(psel, sel)),
+                    "page_fill": payload / ((n_pages - int(st.free_pages)) * page)}
+        del view, pool
+
     sel_np = sel.cpu().numpy()
     # V payload actually gathered: rows of the selected tokens
     n = np.diff(inp.cu_seqlens)
@@ -330,6 +369,7 @@ def main():
         "gram": gram_res,
         "layer_batched": layer_res,
         "append": append_res,
+        "pool": pool_res,
         "input_generation_s": t_gen,
     }
     if not args.no_cpu_baseline:
