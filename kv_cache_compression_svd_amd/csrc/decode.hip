@@ -894,25 +894,27 @@ __global__ __launch_bounds__(256) void k_attend(DecArgs a) {
     }
 }
 
-// One workgroup per stream: log-sum-exp merge of the attention chunks' partials, then out = o'·B_Vᵀ.  Wave w
+// Four workgroups per stream, one per quarter of the output channels: each merges the attention chunks'
+// partials (log-sum-exp) for all 128 channels, then writes its quarter of out = o'·B_Vᵀ.  Wave w
 // merges query heads w, w+4, ...; lane l owns channels 2l, 2l+1 and chunk weights are broadcast from the lane
 // that computed them, so every chunk's loads are independent and issue together.
 template <int G>
 __global__ __launch_bounds__(256) void k_combine(DecArgs a) {
+    constexpr int QR = MKV_D / 4;                  // output channels of this workgroup
     __shared__ float o[G][MKV_D];
-    __shared__ float bsh[MKV_D * (MKV_D + 1)];
-    const int stream = blockIdx.x, r = stream / a.Hkv, g = stream - r * a.Hkv;
+    __shared__ float bsh[QR * (MKV_D + 1)];
+    const int stream = blockIdx.x >> 2, qd = blockIdx.x & 3, r = stream / a.Hkv, g = stream - r * a.Hkv;
     const int n = a.t_n[r], T = (n > 0) ? a.t_T[r] : 0;
     const int nach = (T + a.achunk - 1) / a.achunk;
     const int first = a.t_ablk[r] + g * nach;
     const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int Hq = a.G * a.Hkv;
     const float* Bv = a.basis ? a.basis + ((((size_t)a.t_bslot[r] * a.Hkv + g) * 2 + 1) << 14) : nullptr;
-    f32x4 bvr[16];
-    if (Bv) {   // issue the basis loads first: their latency overlaps the merge
-        const f32x4* src = reinterpret_cast<const f32x4*>(Bv);
+    f32x4 bvr[4];
+    if (Bv) {   // rows [QR qd, QR qd + QR) of B_V; issued first so that their latency overlaps the merge
+        const f32x4* src = reinterpret_cast<const f32x4*>(Bv + (size_t)QR * qd * MKV_D);
 #pragma unroll
-        for (int j = 0; j < 16; ++j) bvr[j] = src[tid + 256 * j];
+        for (int j = 0; j < 4; ++j) bvr[j] = src[tid + 256 * j];
     }
     constexpr int PW = MKV_D + 2;
     for (int h = wid; h < G; h += 4) {
@@ -959,24 +961,24 @@ __global__ __launch_bounds__(256) void k_combine(DecArgs a) {
     }
     if (Bv) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
+        for (int j = 0; j < 4; ++j) {
             const int e = 4 * (tid + 256 * j), row = e >> 7, col = e & 127;
             float* d = &bsh[row * (MKV_D + 1) + col];
             d[0] = bvr[j].x; d[1] = bvr[j].y; d[2] = bvr[j].z; d[3] = bvr[j].w;
         }
     }
     __syncthreads();
-    for (int i = tid; i < G * MKV_D; i += 256) {
-        const int h = i >> 7, row = i & 127;
+    for (int i = tid; i < G * QR; i += 256) {
+        const int h = i / QR, row = i - h * QR;
         float v;
         if (Bv) {
             v = 0.f;
 #pragma unroll 8
             for (int k = 0; k < MKV_D; ++k) v = fmaf(o[h][k], bsh[row * (MKV_D + 1) + k], v);
         } else {
-            v = o[h][row];
+            v = o[h][QR * qd + row];
         }
-        a.out[((size_t)r * Hq + g * G + h) * MKV_D + row] = v;
+        a.out[((size_t)r * Hq + g * G + h) * MKV_D + QR * qd + row] = v;
     }
 }
 
@@ -999,7 +1001,7 @@ hipError_t launch_attend(const DecArgs& a, int n_blocks, hipStream_t s) {
 
 hipError_t launch_combine(const DecArgs& a, int n_streams, hipStream_t s) {
     if (n_streams == 0) return hipSuccess;
-    const dim3 grid(n_streams), block(256);
+    const dim3 grid(4 * n_streams), block(256);   // four workgroups per stream, one per quarter of the channels
     switch (a.G) {
         case 1: hipLaunchKernelGGL(k_combine<1>, grid, block, 0, s, a); break;
         case 2: hipLaunchKernelGGL(k_combine<2>, grid, block, 0, s, a); break;
