@@ -113,6 +113,8 @@ def main():
     lw = W.Workload("llama_32_layers", 32, 32, 8, (32768,) * 32, "bf16", (2048,) * 32, "per_request", 50,
                     "the 32 layers of one 32768-token request, one store")
     linp = W.generate(lw, basis="svd", workers=args.workers) if args.layers else None
+    # the oracle's CPU baseline runs before the GPU is touched (its process pool forks this process)
+    cpu_base = None if args.no_cpu_baseline else cpu_baseline(inp, args.cpu_seconds, args.workers)
 
     import torch
     import kv_cache_compression_svd_amd as mkv
@@ -191,6 +193,28 @@ def main():
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
     score_kern = mkv.mkv_profile_stop()
+
+    # per-call latency (an extra): events on the stream around each call, back to back and with the 256 MB
+    # MALL flushed before every call (a 512 MB fill outside the events)
+    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def per_call(flush):
+        evs = []
+        for i in range(args.steps):
+            if flush:
+                flush_buf.fill_(i & 0xFF)
+            e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e_a.record(stream)
+            step()
+            e_b.record(stream)
+            evs.append((e_a, e_b))
+        torch.cuda.synchronize()
+        t_ms = np.array([x.elapsed_time(y) for x, y in evs])
+        return {"p10_ms": float(np.percentile(t_ms, 10)), "median_ms": float(np.median(t_ms)),
+                "p90_ms": float(np.percentile(t_ms, 90)), "calls": int(t_ms.size)}
+
+    call_latency = {"back_to_back": per_call(False), "mall_flushed": per_call(True)}
+    del flush_buf
 
     # uncompressed baseline on the same inputs (an extra): bf16 only
     dense_base = None
@@ -357,6 +381,7 @@ def main():
         "step_alg_GBps": step_alg / (ms * 1e-3) / 1e9,
         "step_frac_of_hbm_peak": step_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "ms_per_step_unprofiled": clean_ms,
+        "call_latency": call_latency,
         "kernels_avg_ms": {k: v[0] / max(v[1], 1) for k, v in kern.items()},
         "store": {"payload_bytes": payload, "dense_kv_bytes": dense, "compression_ratio": dense / payload,
                   "k_payload_bytes": k_payload, "v_selected_bytes": v_sel_bytes},
@@ -372,8 +397,8 @@ def main():
         "pool": pool_res,
         "input_generation_s": t_gen,
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    if cpu_base is not None:
+        result["cpu_baseline"] = cpu_base
     print(json.dumps(result), flush=True)
 
 
@@ -412,28 +437,61 @@ def layer_batched(mkv, torch, dev, linp, args):
             "context_tokens_per_s_one_layer": n / (ms_one * 1e-3)}
 
 
-def cpu_baseline(inp, seconds: float):
-    """The oracle's decode step on one (request 0, KV head 0) unit, repeated for about ``seconds``; its store is
-    built by the oracle first (untimed).  Context tokens/s of a full layer = n_0 / (n_kv_heads * t_unit)."""
+def _oracle_unit_rate(inp, unit, seconds: float, blas_threads=None):
+    """(context tokens of the unit, decode repetitions, seconds) of the oracle's decode step on one (request,
+    KV head) unit, repeated for about ``seconds``; its store is built by the oracle first (untimed)."""
     import oracle
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=blas_threads):
+        streams = oracle.compress_all(inp, units=[unit])
+        reps, t = 0, 0.0
+        while t < seconds or reps < 1:
+            t0 = time.perf_counter()
+            oracle.decode_all(inp, streams, units=[unit])
+            t += time.perf_counter() - t0
+            reps += 1
+    r = unit[0]
+    return int(inp.cu_seqlens[r + 1] - inp.cu_seqlens[r]), reps, t
+
+
+_POOL_INP = None
+
+
+def _pool_worker(args):
+    unit, seconds = args
+    return _oracle_unit_rate(_POOL_INP, unit, seconds, blas_threads=1)
+
+
+def cpu_baseline(inp, seconds: float, procs: int):
+    """The float64 oracle's decode step timed on the host two ways: (i) one process, BLAS threads = all cores,
+    on the (request 0, KV head 0) unit; (ii) a process pool (one BLAS thread each) over ``procs`` independent
+    (request, KV head) units, all running at once.  Each unit's store is built by the oracle first, untimed.
+    Context tokens/s of a layer = (context-token-heads decoded per second) / n_kv_heads; the reported value is
+    the faster of the two."""
+    import multiprocessing as mp
     from threadpoolctl import threadpool_info
+    global _POOL_INP
     w = inp.workload
-    units = [(0, 0)]
-    streams = oracle.compress_all(inp, units=units)
-    reps, t = 0, 0.0
-    while t < seconds or reps < 1:
-        t0 = time.perf_counter()
-        oracle.decode_all(inp, streams, units=units)
-        t += time.perf_counter() - t0
-        reps += 1
-    n0 = int(inp.cu_seqlens[1] - inp.cu_seqlens[0])
+    n0, reps, t = _oracle_unit_rate(inp, (0, 0), seconds)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": n0 * reps / (w.n_kv_heads * t), "unit": "context tokens/s", "cores": threads,
+    single = n0 * reps / (w.n_kv_heads * t)
+    units = [(r, h) for r in range(w.batch) for h in range(w.n_kv_heads)][:max(1, procs)]
+    _POOL_INP = inp
+    with mp.get_context("fork").Pool(len(units)) as pool:
+        got = pool.map(_pool_worker, [(u, seconds) for u in units])
+    _POOL_INP = None
+    pooled = sum(n * k / tt for n, k, tt in got) / w.n_kv_heads
+    best = max(single, pooled)
+    return {"value": best, "unit": "context tokens/s", "cores": len(units) if pooled >= single else threads,
             "kind": "oracle",
-            "sample": f"float64 numpy oracle decode of request 0 / KV head 0 ({n0} tokens, T={int(inp.T[0])}) "
-                      f"repeated {reps}x in {t:.1f}s; its store compressed by the oracle beforehand, untimed; "
-                      f"a layer has {w.n_kv_heads} KV heads, so tokens/s = n0*reps/({w.n_kv_heads}*t); "
-                      f"BLAS threads {threads}, host cpu_count {os.cpu_count()}"}
+            "single_process": {"value": single, "blas_threads": threads, "reps": reps, "seconds": t},
+            "process_pool": {"value": pooled, "processes": len(units), "blas_threads_each": 1,
+                             "units": [list(u) for u in units]},
+            "sample": f"float64 numpy oracle decode: (i) request 0 / KV head 0 ({n0} tokens, T={int(inp.T[0])}) "
+                      f"repeated {reps}x in {t:.1f}s with {threads} BLAS threads; (ii) {len(units)} (request, KV "
+                      f"head) units at once in a process pool, one BLAS thread each, ~{seconds:.0f}s each; stores "
+                      f"compressed by the oracle beforehand, untimed; tokens/s = context-token-heads per second / "
+                      f"{w.n_kv_heads} KV heads; host cpu_count {os.cpu_count()}"}
 
 
 if __name__ == "__main__":

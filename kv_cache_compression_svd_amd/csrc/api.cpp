@@ -935,7 +935,7 @@ mkv_status mkv_pool_request(const mkv_pool* p, int32_t id, int64_t* n_tokens, in
 namespace {
 
 struct DecPlan {
-    int32_t G = 0, Hq = 0, spw = 0, sgx = 0, max_T = 0;
+    int32_t G = 0, Hq = 0, spw = 0, sgx = 0, max_T = 0, hcopies = 1, etiles = 1;
     std::vector<int32_t> tab;    // n | segbase | scap | tokbase | T | kblk | ablk | basis slot
     int64_t n_sblk = 0, n_kblk = 0, n_ablk = 0;
     uint64_t o_tab, o_state, o_hist, o_qp, o_qbar, o_keys, o_L, o_sel, o_part, bytes;
@@ -982,6 +982,7 @@ mkv_status plan_decode(const mkv_store* s, int32_t n_q_heads, const int32_t* T, 
         kb += (int64_t)sh.Hkv * cdiv(n, kKeysPerBlock);
         ab += (int64_t)sh.Hkv * cdiv(te, kAttnChunk);
         P->max_T = std::max<int32_t>(P->max_T, (int32_t)te);
+        P->etiles = std::max<int32_t>(P->etiles, (int32_t)cdiv(n, kEmitTileTokens));
     }
     tkb[B] = (int32_t)kb;
     tab_[B] = (int32_t)ab;
@@ -989,13 +990,18 @@ mkv_status plan_decode(const mkv_store* s, int32_t n_q_heads, const int32_t* T, 
     P->n_sblk = (int64_t)P->sgx * B * sh.Hkv;
     P->n_kblk = kb;
     P->n_ablk = ab;
-    if (P->n_sblk > INT32_MAX || kb > INT32_MAX || ab > INT32_MAX) return fail(MKV_E_UNSUPPORTED, "too many workgroups");
+    if (P->n_sblk > INT32_MAX || kb > INT32_MAX || ab > INT32_MAX || (int64_t)B * sh.Hkv * P->etiles > INT32_MAX)
+        return fail(MKV_E_UNSUPPORTED, "too many workgroups");
     const uint64_t streams = (uint64_t)B * sh.Hkv;
     const uint64_t th = (uint64_t)kpad * sh.Hkv;
     uint64_t o = 0;
     P->o_tab = o; o = align_up(o + 4 * P->tab.size());
     P->o_state = o; o = align_up(o + 4 * streams * kStateWords);
-    P->o_hist = o; o = align_up(o + 4 * streams * kHistBins);
+    // histogram copies: the score kernel's atomics on a stream's bins are spread over several copies when
+    // there are few streams (one copy at 64 streams or more)
+    P->hcopies = 1;
+    while (P->hcopies < kMaxHistCopies && (int64_t)streams * P->hcopies * 2 <= 64) P->hcopies *= 2;
+    P->o_hist = o; o = align_up(o + 4 * streams * (uint64_t)P->hcopies * kHistBins);
     P->o_qp = o; o = align_up(o + 4ull * B * n_q_heads * MKV_HEAD_DIM);
     P->o_qbar = o; o = align_up(o + 4 * streams * MKV_HEAD_DIM);
     P->o_keys = o; o = align_up(o + 4 * th);
@@ -1063,6 +1069,8 @@ mkv_status mkv_decode_attn(const mkv_store* s, const void* q, int32_t n_q_heads,
     a.qbar = reinterpret_cast<float*>(w + P.o_qbar);
     a.keys = reinterpret_cast<uint32_t*>(w + P.o_keys);
     a.hist = reinterpret_cast<uint32_t*>(w + P.o_hist);
+    a.hcopies = P.hcopies;
+    a.etiles = P.etiles;
     a.state = reinterpret_cast<uint32_t*>(w + P.o_state);
     a.L = reinterpret_cast<uint2*>(w + P.o_L);
     a.part = reinterpret_cast<float*>(w + P.o_part);

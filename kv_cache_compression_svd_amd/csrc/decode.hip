@@ -90,8 +90,15 @@ __global__ __launch_bounds__(256) void k_dec_prep(DecArgs a, Upload tab) {
         qs[h][c] = a.dtype == 1 ? bf16_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qi])
                                 : reinterpret_cast<const float*>(a.q)[qi];
     }
-    reinterpret_cast<u32x4*>(a.hist + (size_t)stream * kHistBins + qd * (kHistBins / 4))[tid] = u32x4{0u, 0u, 0u, 0u};
-    if (qd == 0 && tid < kStateWords) a.state[stream * kStateWords + tid] = 0u;
+    {   // a quarter of every histogram copy of the stream
+        u32x4* hq = reinterpret_cast<u32x4*>(a.hist + (size_t)stream * a.hcopies * kHistBins);
+        for (int j = tid; j < a.hcopies * (kHistBins / 16); j += 256) {
+            const int c = j / (kHistBins / 16), i = j - c * (kHistBins / 16);
+            hq[c * (kHistBins / 4) + qd * (kHistBins / 16) + i] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    if (qd == 0)
+        for (int i = tid; i < kCoarseOff + 64 * a.hcopies; i += 256) a.state[stream * kStateWords + i] = 0u;
     if (Bk) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -323,8 +330,9 @@ __global__ __launch_bounds__(256) void k_score(DecArgs a) {
         }
     }
     __syncthreads();
-    // flush the non-empty fine and coarse bins
-    uint32_t* gh = a.hist + (size_t)stream * kHistBins;
+    // flush the non-empty fine and coarse bins into one of the stream's histogram copies
+    const int copy = (int)(blockIdx.x & (uint32_t)(a.hcopies - 1));
+    uint32_t* gh = a.hist + ((size_t)stream * a.hcopies + copy) * kHistBins;
 #pragma unroll 4
     for (int j = tid; j < kHistBins; j += 256) {
         const uint32_t c = sh[j];
@@ -332,7 +340,7 @@ __global__ __launch_bounds__(256) void k_score(DecArgs a) {
     }
     if (tid < 64) {
         const uint32_t c = shc[tid];
-        if (c) atomic_add_dev(&a.state[stream * kStateWords + kCoarseOff + tid], c);
+        if (c) atomic_add_dev(&a.state[stream * kStateWords + kCoarseOff + 64 * copy + tid], c);
     }
 }
 
@@ -377,13 +385,24 @@ __device__ __forceinline__ uint32_t wave_incl(uint32_t v) {
 __device__ __forceinline__ void find_threshold(const DecArgs& a, int stream, uint32_t T, uint32_t* res) {
     const int lane = threadIdx.x & 63;
     const uint32_t* st = a.state + stream * kStateWords;
-    const uint32_t cv = st[kCoarseOff + 63 - lane];
+    // the copies are summed from loads issued together (copies past hcopies re-read the last one, unused)
+    uint32_t cv = 0;
+#pragma unroll
+    for (int c = 0; c < kMaxHistCopies; ++c) {
+        const uint32_t v = st[kCoarseOff + 64 * min(c, a.hcopies - 1) + 63 - lane];
+        cv += c < a.hcopies ? v : 0u;
+    }
     const uint32_t ci = wave_incl(cv), ce = ci - cv;
     const uint64_t cb_bal = __ballot(ce < T && ci >= T);
     const int cl = max(__ffsll((unsigned long long)cb_bal) - 1, 0);
     const int cb = 63 - cl;
     const uint32_t above = __shfl(ce, cl, MKV_WAVE);
-    const uint32_t fv = a.hist[(size_t)stream * kHistBins + cb * 64 + 63 - lane];
+    uint32_t fv = 0;
+#pragma unroll
+    for (int c = 0; c < kMaxHistCopies; ++c) {
+        const uint32_t v = a.hist[((size_t)stream * a.hcopies + min(c, a.hcopies - 1)) * kHistBins + cb * 64 + 63 - lane];
+        fv += c < a.hcopies ? v : 0u;
+    }
     const uint32_t fi = wave_incl(fv) + above, fe = fi - fv;
     if (fe < T && fi >= T) {
         res[0] = (uint32_t)(cb * 64 + 63 - lane);
@@ -455,46 +474,46 @@ __device__ __forceinline__ void find_bin1024(const uint32_t* h, uint32_t need, u
     __syncthreads();
 }
 
-constexpr int kTileBits = 1 << 17;          // tokens per bitmap tile of the emit kernel (16 KB of LDS)
-constexpr int kTileWords = kTileBits / 32;
+// Tokens per bitmap tile of the emit kernel: one 32-bit word per thread of a 1024-thread workgroup.
+constexpr int kTileWords = 1024;
+constexpr int kTileBits = kTileWords * 32;
+static_assert(kTileBits == kEmitTileTokens, "the host sizes the emit grid with kEmitTileTokens");
 
-// Tokens of one bitmap tile in ascending order: thread t owns words [4t, 4t+4); returns the tile's count.
+// Tokens of one bitmap tile in ascending order (thread t owns word t), written from position carry on; returns
+// the tile's count.
 __device__ __forceinline__ uint32_t emit_tile(const uint32_t* bm, int tile0, uint32_t carry, int32_t* srow,
                                               int32_t* urow, uint32_t* tmp) {
     const int tid = threadIdx.x;
-    uint32_t w[4], c = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) { w[j] = bm[4 * tid + j]; c += __popc(w[j]); }
+    uint32_t x = bm[tid];
     uint32_t tot;
-    uint32_t pos = carry + block_exscan(c, tmp, &tot);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        uint32_t x = w[j];
-        while (x) {
-            const int bit = __ffs(x) - 1;
-            x &= x - 1;
-            const int32_t idx = tile0 + (4 * tid + j) * 32 + bit;
-            srow[pos] = idx;
-            if (urow) urow[pos] = idx;
-            ++pos;
-        }
+    uint32_t pos = carry + block_exscan((uint32_t)__popc(x), tmp, &tot);
+    while (x) {
+        const int bit = __ffs(x) - 1;
+        x &= x - 1;
+        const int32_t idx = tile0 + tid * 32 + bit;
+        srow[pos] = idx;
+        if (urow) urow[pos] = idx;
+        ++pos;
     }
     return tot;
 }
 
-// One workgroup per stream: the exact T-th key among the candidates (two 10-bit radix levels), the cut among
-// keys equal to it (lowest token indices first), then the selected tokens in ascending order through a bitmap.
+// One workgroup per (stream, tile of kTileBits tokens): the exact T-th key among the stream's candidates (two
+// 10-bit radix levels, recomputed by every tile of the stream), the cut among keys equal to it (lowest token
+// indices first), the count of selected tokens before the tile, then the tile's selected tokens in ascending
+// order through an LDS bitmap.  Tile 0 also pads the caller's selection row with -1.
 __global__ __launch_bounds__(1024) void k_sel_emit(DecArgs a) {
     __shared__ uint32_t bm[kTileWords];
     __shared__ uint32_t h[1024];
     __shared__ uint32_t tmp[20];
     __shared__ uint32_t res[4];
-    __shared__ uint32_t s_eq;
-    const int stream = blockIdx.x, r = stream / a.Hkv, g = stream - r * a.Hkv;
+    const int stream = blockIdx.x / a.etiles, tile = blockIdx.x - stream * a.etiles;
+    const int r = stream / a.Hkv, g = stream - r * a.Hkv;
     const int n = a.t_n[r], T = a.t_T[r];
     const int tid = threadIdx.x;
+    const int t0 = tile * kTileBits;
     int32_t* urow = a.sel ? a.sel + (size_t)stream * a.sel_stride : nullptr;
-    if (n > 0 && T > 0) {
+    if (n > 0 && T > 0 && t0 < n) {
         const uint32_t* st = a.state + stream * kStateWords;
         const uint32_t p1 = st[ST_P1], ngt = st[ST_NGT], ncand = st[ST_NCAND], need = st[ST_NEED];
         const uint2* L = a.L + key_base(a, r, g, n);
@@ -504,7 +523,6 @@ __global__ __launch_bounds__(1024) void k_sel_emit(DecArgs a) {
         int cut = n;   // ties equal to K* are taken up to this token index
         if (!all) {
             h[tid] = 0u;
-            if (tid == 0) s_eq = 0u;
             __syncthreads();
             for (uint32_t i = tid; i < ncand; i += 1024) atomicAdd(&h[(cand[i].y >> 10) & 1023u], 1u);
             __syncthreads();
@@ -526,30 +544,24 @@ __global__ __launch_bounds__(1024) void k_sel_emit(DecArgs a) {
                 // the need_eq-th smallest token index among the keys equal to K*: scan tie bitmaps tile by tile
                 uint32_t seen = 0;
                 cut = -1;
-                for (int t0 = 0; t0 < n && cut < 0; t0 += kTileBits) {
-                    for (int i = tid; i < kTileWords; i += 1024) bm[i] = 0u;
+                for (int u0 = 0; u0 < n && cut < 0; u0 += kTileBits) {
+                    bm[tid] = 0u;
                     __syncthreads();
                     for (uint32_t i = tid; i < ncand; i += 1024) {
                         const uint2 e = cand[i];
-                        if (e.y == kstar && (int)e.x >= t0 && (int)e.x < t0 + kTileBits)
-                            atomicOr(&bm[(e.x - t0) >> 5], 1u << ((e.x - t0) & 31));
+                        if (e.y == kstar && (int)e.x >= u0 && (int)e.x < u0 + kTileBits)
+                            atomicOr(&bm[(e.x - u0) >> 5], 1u << ((e.x - u0) & 31));
                     }
                     __syncthreads();
-                    uint32_t w[4], c = 0;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) { w[j] = bm[4 * tid + j]; c += __popc(w[j]); }
+                    uint32_t x = bm[tid];
                     uint32_t tot;
-                    const uint32_t before = seen + block_exscan(c, tmp, &tot);
-                    if (before < need_eq && before + c >= need_eq) {
+                    const uint32_t before = seen + block_exscan((uint32_t)__popc(x), tmp, &tot);
+                    if (before < need_eq && before + (uint32_t)__popc(x) >= need_eq) {
                         uint32_t run = before;
-                        for (int j = 0; j < 4 && cut < 0; ++j) {
-                            uint32_t x = w[j];
-                            while (x) {
-                                const int bit = __ffs(x) - 1;
-                                x &= x - 1;
-                                if (++run == need_eq) { res[0] = (uint32_t)(t0 + (4 * tid + j) * 32 + bit); break; }
-                            }
-                            if (run == need_eq) break;
+                        while (x) {
+                            const int bit = __ffs(x) - 1;
+                            x &= x - 1;
+                            if (++run == need_eq) { res[0] = (uint32_t)(u0 + tid * 32 + bit); break; }
                         }
                     }
                     seen += tot;
@@ -559,27 +571,33 @@ __global__ __launch_bounds__(1024) void k_sel_emit(DecArgs a) {
                 }
             }
         }
-        int32_t* srow = a.sel_int + (size_t)stream * a.sel_int_stride;
-        uint32_t carry = 0;
-        for (int t0 = 0; t0 < n; t0 += kTileBits) {
-            for (int i = tid; i < kTileWords; i += 1024) bm[i] = 0u;
-            __syncthreads();
-            for (uint32_t i = tid; i < ngt; i += 1024) {
-                const uint32_t x = L[i].x;
-                if ((int)x >= t0 && (int)x < t0 + kTileBits) atomicOr(&bm[(x - t0) >> 5], 1u << ((x - t0) & 31));
-            }
+        auto taken = [&](const uint2 e) { return all || e.y > kstar || (e.y == kstar && (int)e.x <= cut); };
+        // selected tokens before this tile: they come first in the stream's ascending row
+        uint32_t before = 0;
+        if (tile > 0) {
+            uint32_t c = 0;
+            for (uint32_t i = tid; i < ngt; i += 1024) c += (int)L[i].x < t0 ? 1u : 0u;
             for (uint32_t i = tid; i < ncand; i += 1024) {
                 const uint2 e = cand[i];
-                const bool take = all || e.y > kstar || (e.y == kstar && (int)e.x <= cut);
-                if (take && (int)e.x >= t0 && (int)e.x < t0 + kTileBits)
-                    atomicOr(&bm[(e.x - t0) >> 5], 1u << ((e.x - t0) & 31));
+                c += ((int)e.x < t0 && taken(e)) ? 1u : 0u;
             }
-            __syncthreads();
-            carry += emit_tile(bm, t0, carry, srow, urow, tmp);
-            __syncthreads();
+            block_exscan(c, tmp, &before);
         }
+        bm[tid] = 0u;
+        __syncthreads();
+        for (uint32_t i = tid; i < ngt; i += 1024) {
+            const uint32_t x = L[i].x;
+            if ((int)x >= t0 && (int)x < t0 + kTileBits) atomicOr(&bm[(x - t0) >> 5], 1u << ((x - t0) & 31));
+        }
+        for (uint32_t i = tid; i < ncand; i += 1024) {
+            const uint2 e = cand[i];
+            if (taken(e) && (int)e.x >= t0 && (int)e.x < t0 + kTileBits)
+                atomicOr(&bm[(e.x - t0) >> 5], 1u << ((e.x - t0) & 31));
+        }
+        __syncthreads();
+        emit_tile(bm, t0, before, a.sel_int + (size_t)stream * a.sel_int_stride, urow, tmp);
     }
-    if (urow) {
+    if (urow && tile == 0) {
         const int start = (n > 0) ? min(T, n) : 0;
         for (int j = start + tid; j < a.sel_stride; j += 1024) urow[j] = -1;
     }
@@ -592,7 +610,7 @@ hipError_t launch_sel_collect(const DecArgs& a, int n_blocks, hipStream_t s) {
 }
 hipError_t launch_sel_emit(const DecArgs& a, int n_streams, hipStream_t s) {
     if (n_streams == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_sel_emit, dim3(n_streams), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(k_sel_emit, dim3(n_streams * a.etiles), dim3(1024), 0, s, a);
     return hipGetLastError();
 }
 

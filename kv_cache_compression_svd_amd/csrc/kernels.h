@@ -7,10 +7,12 @@ namespace mkv {
 
 constexpr int kUploadWords = 448;       // int32 words a table upload carries in its kernel arguments
 constexpr int kHistBins = 4096;         // first radix level of the top-T select: key bits [31:20]
-constexpr int kStateWords = 128;        // per (request, KV head) selection state and coarse histogram
-constexpr int kCoarseOff = 64;          // coarse histogram (top 6 key bits) inside the state words
+constexpr int kMaxHistCopies = 8;      // copies of each stream's histograms (spreads the score kernel's atomics)
+constexpr int kCoarseOff = 64;          // coarse histograms (top 6 key bits, 64 bins per copy) inside the state words
+constexpr int kStateWords = kCoarseOff + 64 * kMaxHistCopies;   // per (request, KV head) selection state
 constexpr int kKeysPerBlock = 4096;     // keys per workgroup in the selection passes
 constexpr int kAttnChunk = 256;         // selected tokens per attention workgroup
+constexpr int kEmitTileTokens = 32768;  // tokens per workgroup of the selection's emit kernel
 constexpr int kDenseChunk = 512;        // tokens per workgroup of the uncompressed baseline
 constexpr int kGramChunk = 16384;       // tokens per workgroup of the Gram matrices
 
@@ -115,8 +117,10 @@ struct DecArgs {
     float* qp;                  // [B][Hq][128]
     float* qbar;                // [B][Hkv][128]
     uint32_t* keys;             // [Hkv * sum of contexts padded to 64 tokens]
-    uint32_t* hist;             // [B*Hkv][4096]
-    uint32_t* state;            // [B*Hkv][16]
+    uint32_t* hist;             // [B*Hkv][hcopies][4096]
+    uint32_t* state;            // [B*Hkv][kStateWords]
+    int32_t hcopies;            // histogram copies per stream (a power of two <= kMaxHistCopies)
+    int32_t etiles;             // emit workgroups per stream: tiles of 32768 tokens of the longest context
     uint2* L;                   // same indexing as keys: taken tokens, then candidates, as (token index, key)
     float* part;                // [n_ablk][G][130]
     int32_t achunk;             // tokens per attention partial (the combine kernel's chunk)

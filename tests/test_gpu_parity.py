@@ -249,8 +249,27 @@ def test_repeat_runs_are_bit_identical(mkv):
     assert torch.equal(o1, o2) and torch.equal(q1, q2)
 
 
+def test_equal_scores_across_emit_tiles(mkv):
+    """Every score equal on a stream of several 32768-token emit tiles: the selection is the lowest T indices,
+    so the cut among equal keys falls inside a later tile and every tile must count the tokens before it."""
+    import torch
+    wl = _custom([100_000, 40_000], [70_000, 33_000], Hq=4, Hkv=1, seed=12)
+    inp = W.generate(wl, basis="none")
+    inp.K[:] = 0
+    ref = oracle.compress_all(inp)
+    store, q = _compress_gpu(mkv, inp)
+    out, sel = mkv.mkv_decode_attn(store, q, inp.T)
+    torch.cuda.synchronize()
+    sel = sel.cpu().numpy()
+    assert np.array_equal(sel[0, 0, :70_000], np.arange(70_000))
+    assert np.array_equal(sel[1, 0, :33_000], np.arange(33_000)) and np.all(sel[1, 0, 33_000:] == -1)
+    res = oracle.decode_all(inp, ref)
+    for r in range(2):
+        check_out(out.cpu().numpy()[r].astype(np.float64), res[(r, 0)]["out"])
+
+
 def test_long_stream_spans_several_bitmap_tiles(mkv):
-    """A 300K-token stream spans three 131072-token bitmap tiles of the selection's emit step."""
+    """A 300K-token stream spans ten 32768-token bitmap tiles of the selection's emit step."""
     wl = _custom([300_000, 5_000], [5_000, 150], Hq=4, Hkv=1, seed=9)
     inp = W.generate(wl, basis="sperm")
     ref = oracle.compress_all(inp)
