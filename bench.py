@@ -195,14 +195,15 @@ def main():
     score_kern = mkv.mkv_profile_stop()
 
     # per-call latency (an extra): events on the stream around each call, back to back and with the 256 MB
-    # MALL flushed before every call (a 512 MB fill outside the events)
-    flush_buf = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # MALL flushed before every call by reading a 512 MB buffer outside the events (a read leaves clean lines;
+    # a fill would leave dirty ones whose write-back would be charged to the next call)
+    flush_buf = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
 
     def per_call(flush):
         evs = []
         for i in range(args.steps):
             if flush:
-                flush_buf.fill_(i & 0xFF)
+                flush_buf.sum()
             e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e_a.record(stream)
             step()

@@ -950,11 +950,12 @@ mkv_status plan_decode(const mkv_store* s, int32_t n_q_heads, const int32_t* T, 
     if (P->G != 1 && P->G != 2 && P->G != 4 && P->G != 8) return fail(MKV_E_UNSUPPORTED, "query heads per KV head must be 1, 2, 4 or 8 (got %d)", P->G);
     P->Hq = n_q_heads;
     const int B = sh.B;
-    // segments per score workgroup, a multiple of 4 (one segment per wave at a time): about 16K workgroups for
-    // long contexts
+    // segments per score workgroup, a multiple of 4 (one segment per wave at a time): 8 once there are 64K
+    // segments or more (measured best from 8 x 128K down to the 16-request ragged mix), else 4 for more
+    // workgroups on small stores
     int64_t s_cur = 0;   // segments in use (the capacity may hold more)
     for (int r = 0; r < B; ++r) s_cur += (int64_t)sh.Hkv * cdiv(sh.cu[r + 1] - sh.cu[r], MKV_SEG_LEN);
-    P->spw = (int32_t)(std::max<int64_t>(4, std::min<int64_t>(16, s_cur / 16384)) & ~3ll);
+    P->spw = s_cur >= 65536 ? 8 : 4;
     P->tab.assign(8 * B + 2, 0);
     int32_t* tn = P->tab.data();
     int32_t* tseg = tn + B;
