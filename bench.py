@@ -203,7 +203,7 @@ def main():
         evs = []
         for i in range(args.steps):
             if flush:
-                flush_buf.sum()
+                flush_buf.view(torch.float32).sum()
             e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e_a.record(stream)
             step()
