@@ -201,8 +201,15 @@ mkv_status mkv_decode_attn(const mkv_store* store, const void* q, int32_t n_q_he
  * and decode over a view equals decode over a store of the same requests.
  * Pool buffer layout (offsets from pool_buf): header, codes uint8 [2][S], seg_off uint64 [2][S] (S =
  * n_kv_heads * segment_slots), bases float32 [max_requests][n_kv_heads][2][128][128] when has_basis, then
- * n_pages pages of page_bytes; a request with id i and segment-slot run starting at u numbers its segments
- * X*S + n_kv_heads*u + h*S_r + s with S_r = ceil(n_r/64), and its bases sit at basis slot i.
+ * n_pages pages of page_bytes, then (appendable pools) per request id, KV head and tensor an open-segment area
+ * holding the unfinished last segment packed (addressed like the pages, through seg_off) and the same area's
+ * original rows.  A request with id i and segment-slot run starting at u numbers its segments
+ * X*S + n_kv_heads*u + h*S_r + s with S_r = ceil(cap_r/64) (cap_r: its token capacity, n_r unless it was added
+ * with one), and its bases sit at basis slot i.
+ * Appends (appendable bf16 pools): mkv_pool_append adds one token to each listed request exactly as
+ * mkv_append does for growable stores; a segment that an append completes is sealed into a page at a position
+ * the host reserves for it with the uncompressed segment size (64*128*2 bytes), taken from the request's
+ * current append page (all its streams' sealed segments share it) or from a new page.
  * Ordering: the pool's host bookkeeping is not thread-safe; pool calls and decode calls on its views must be
  * ordered by the caller (one stream, or synchronisation), since removing a request lets the next add overwrite
  * its pages. */
@@ -215,6 +222,7 @@ typedef struct {
                                     n tokens takes a contiguous run of ceil(n/64) */
     int64_t n_pages;             /* >= 1 */
     int64_t page_bytes;          /* multiple of 256, >= 64*128*dtype bytes (one uncompressed segment), <= 2^31 */
+    int32_t appendable;          /* 1: open-segment areas for mkv_pool_append (bf16 only) */
 } mkv_pool_desc;
 
 typedef struct mkv_pool mkv_pool;   /* opaque host handle */
@@ -242,13 +250,23 @@ mkv_status mkv_pool_create(const mkv_pool_desc* desc, const mkv_seg_policy* poli
 mkv_status mkv_pool_add_scratch_bytes(const mkv_pool* pool, const mkv_kv_desc* kv, size_t* scratch_bytes);
 /* Compresses the requests of kv (shape checks as mkv_compress; n_kv_heads and dtype must match the pool) into
  * the pool and writes their ids to ids [host] [kv->batch].  basis: as for mkv_compress, required when the pool
- * has bases and NULL otherwise; the pool keeps a copy.  SYNCHRONISES `stream` (twice): the pages a request
+ * has bases and NULL otherwise; the pool keeps a copy.  capacity: [host] [kv->batch] token capacities >= the
+ * contexts for later appends (appendable pools only), or NULL.  SYNCHRONISES `stream` (twice): the pages a request
  * needs depend on its kept channel counts, so they are read back after the decide pass and handed out on the
  * host.  Fails with MKV_E_ARG, leaving the pool as it was, when ids, segment slots (a contiguous run per
  * request) or pages run short; the page check comes after the decide pass has run on the device, every other
  * check before anything is enqueued.  scratch [dev] >= mkv_pool_add_scratch_bytes, 256-byte aligned. */
-mkv_status mkv_pool_add(mkv_pool* pool, const mkv_kv_desc* kv, const float* basis, void* scratch,
-                        size_t scratch_bytes, mkv_stream_t stream, int32_t* ids);
+mkv_status mkv_pool_add(mkv_pool* pool, const mkv_kv_desc* kv, const float* basis, const int64_t* capacity,
+                        void* scratch, size_t scratch_bytes, mkv_stream_t stream, int32_t* ids);
+/* Appends one token to each of the n listed live requests (ids [host] [n], distinct): K_new[i][h] and
+ * V_new[i][h] ([dev] [n][n_kv_heads][128] bf16, unrotated like the K/V given to mkv_pool_add) become token n_r of
+ * request ids[i].  Every check (appendable pool, live ids, capacity, free pages for the segments the append
+ * seals) runs on the host before anything is enqueued; on failure nothing changes.  Views made earlier keep
+ * the old token counts: make a new view to decode the extended requests.  ws [dev] >=
+ * mkv_pool_append_workspace_bytes(pool, n), 256-byte aligned. */
+mkv_status mkv_pool_append_workspace_bytes(const mkv_pool* pool, int32_t n, size_t* ws_bytes);
+mkv_status mkv_pool_append(mkv_pool* pool, int32_t n, const int32_t* ids, const void* K_new, const void* V_new,
+                           void* ws, size_t ws_bytes, mkv_stream_t stream);
 /* Returns the listed requests' pages, slots and ids to the pool.  Host-only: the caller makes sure no enqueued
  * work still reads them (a later add on the same stream is ordered after earlier decodes on it).  Views that
  * list a removed request must not be used again.  Unknown or repeated ids: MKV_E_ARG, nothing removed. */
@@ -259,8 +277,9 @@ mkv_status mkv_pool_remove(mkv_pool* pool, int32_t n, const int32_t* ids);
 mkv_status mkv_pool_view(const mkv_pool* pool, int32_t n, const int32_t* ids, mkv_store** out);
 /* Occupancy and device regions of the pool. */
 mkv_status mkv_pool_stats(const mkv_pool* pool, mkv_pool_info* info);
-/* Tokens, pages and packed payload bytes of one live request (each output pointer may be NULL). */
-mkv_status mkv_pool_request(const mkv_pool* pool, int32_t id, int64_t* n_tokens, int64_t* pages,
+/* Tokens, token capacity, pages and packed payload bytes of one live request (each output pointer may be NULL;
+ * sealed appended segments count with their reserved size). */
+mkv_status mkv_pool_request(const mkv_pool* pool, int32_t id, int64_t* n_tokens, int64_t* capacity, int64_t* pages,
                             uint64_t* payload_bytes);
 /* Frees the host handle only. NULL is accepted. */
 mkv_status mkv_pool_destroy(mkv_pool* pool);

@@ -64,7 +64,7 @@ class StoreInfo(ctypes.Structure):
 
 class PoolDesc(ctypes.Structure):
     _fields_ = [("n_kv_heads", c_int32), ("dtype", c_int32), ("has_basis", c_int32), ("max_requests", c_int32),
-                ("segment_slots", c_int64), ("n_pages", c_int64), ("page_bytes", c_int64)]
+                ("segment_slots", c_int64), ("n_pages", c_int64), ("page_bytes", c_int64), ("appendable", c_int32)]
 
 
 class PoolInfo(ctypes.Structure):
@@ -100,11 +100,15 @@ SIGNATURES = {
     "mkv_pool_bytes": (c_int32, [POINTER(PoolDesc), POINTER(c_size_t)]),
     "mkv_pool_create": (c_int32, [POINTER(PoolDesc), POINTER(SegPolicy), c_void_p, c_size_t, POINTER(c_void_p)]),
     "mkv_pool_add_scratch_bytes": (c_int32, [c_void_p, POINTER(KVDesc), POINTER(c_size_t)]),
-    "mkv_pool_add": (c_int32, [c_void_p, POINTER(KVDesc), c_void_p, c_void_p, c_size_t, c_void_p, POINTER(c_int32)]),
+    "mkv_pool_add": (c_int32, [c_void_p, POINTER(KVDesc), c_void_p, POINTER(c_int64), c_void_p, c_size_t, c_void_p,
+                               POINTER(c_int32)]),
+    "mkv_pool_append_workspace_bytes": (c_int32, [c_void_p, c_int32, POINTER(c_size_t)]),
+    "mkv_pool_append": (c_int32, [c_void_p, c_int32, POINTER(c_int32), c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "mkv_pool_remove": (c_int32, [c_void_p, c_int32, POINTER(c_int32)]),
     "mkv_pool_view": (c_int32, [c_void_p, c_int32, POINTER(c_int32), POINTER(c_void_p)]),
     "mkv_pool_stats": (c_int32, [c_void_p, POINTER(PoolInfo)]),
-    "mkv_pool_request": (c_int32, [c_void_p, c_int32, POINTER(c_int64), POINTER(c_int64), POINTER(c_uint64)]),
+    "mkv_pool_request": (c_int32, [c_void_p, c_int32, POINTER(c_int64), POINTER(c_int64), POINTER(c_int64),
+                                   POINTER(c_uint64)]),
     "mkv_pool_destroy": (c_int32, [c_void_p]),
     "mkv_last_error": (c_char_p, []),
     "mkv_profile_start": (c_int32, [c_int32, c_uint32]),
@@ -320,12 +324,14 @@ class Pool:
     """A paged pool of compressed requests in one device buffer (a uint8 tensor) with its host handle."""
 
     def __init__(self, n_kv_heads: int, dtype: int, max_requests: int, segment_slots: int, n_pages: int,
-                 page_bytes: int, has_basis: bool = True, policy: SegPolicy | None = None, device="cuda", buf=None):
+                 page_bytes: int, has_basis: bool = True, policy: SegPolicy | None = None, device="cuda", buf=None,
+                 appendable: bool = False):
         torch = _torch()
         self.policy = policy or mkv_default_policy()
         d = PoolDesc()
         d.n_kv_heads, d.dtype, d.has_basis, d.max_requests = int(n_kv_heads), int(dtype), int(bool(has_basis)), int(max_requests)
         d.segment_slots, d.n_pages, d.page_bytes = int(segment_slots), int(n_pages), int(page_bytes)
+        d.appendable = int(bool(appendable))
         self.desc = d
         nb = c_size_t()
         _check(lib().mkv_pool_bytes(byref(d), byref(nb)))
@@ -336,9 +342,10 @@ class Pool:
         self.n_kv_heads, self.dtype = int(n_kv_heads), int(dtype)
         self._keep = []
 
-    def add(self, K, V, cu_seqlens, basis=None, stream=None, scratch=None):
+    def add(self, K, V, cu_seqlens, basis=None, stream=None, scratch=None, capacity=None):
         """Compresses the requests of (K, V, cu_seqlens) into the pool; returns their ids (numpy int32).
-        Synchronises the stream."""
+        ``capacity``: per-request token capacities for later appends (appendable pools).  Synchronises the
+        stream."""
         import numpy as np
         torch = _torch()
         d, cu = _kv_desc(K, V, cu_seqlens)
@@ -350,9 +357,33 @@ class Pool:
             _check(lib().mkv_pool_add_scratch_bytes(self.handle, byref(d), byref(v)))
             scratch = torch.empty(max(v.value, 1), dtype=torch.uint8, device=self.buf.device)
         ids = np.zeros(d.batch, dtype=np.int32)
-        _check(lib().mkv_pool_add(self.handle, byref(d), _ptr(basis), _ptr(scratch), c_size_t(scratch.numel()),
-                                  _stream_ptr(stream), ids.ctypes.data_as(POINTER(c_int32))))
+        cap = None
+        if capacity is not None:
+            cap = np.ascontiguousarray(np.asarray(capacity, dtype=np.int64))
+            if cap.shape != (d.batch,):
+                raise ValueError("capacity must hold one token count per request")
+        _check(lib().mkv_pool_add(self.handle, byref(d), _ptr(basis),
+                                  None if cap is None else cap.ctypes.data_as(POINTER(c_int64)), _ptr(scratch),
+                                  c_size_t(scratch.numel()), _stream_ptr(stream), ids.ctypes.data_as(POINTER(c_int32))))
         return ids
+
+    def append(self, ids, K_new, V_new, ws=None, stream=None):
+        """One token for each listed request: K_new, V_new are [len(ids)][n_kv_heads][128] bf16 CUDA tensors."""
+        import numpy as np
+        torch = _torch()
+        a = np.ascontiguousarray(np.atleast_1d(np.asarray(ids, dtype=np.int32)))
+        for t in (K_new, V_new):
+            if tuple(t.shape) != (len(a), self.n_kv_heads, HEAD_DIM) or not t.is_contiguous() or not t.is_cuda \
+                    or _dtype_code(t) != self.dtype:
+                raise ValueError("K_new and V_new must be contiguous CUDA tensors [len(ids)][n_kv_heads][128] of "
+                                 "the pool's dtype")
+        if ws is None:
+            v = c_size_t()
+            _check(lib().mkv_pool_append_workspace_bytes(self.handle, len(a), byref(v)))
+            ws = torch.empty(max(v.value, 1), dtype=torch.uint8, device=self.buf.device)
+        _check(lib().mkv_pool_append(self.handle, len(a), a.ctypes.data_as(POINTER(c_int32)), _ptr(K_new),
+                                     _ptr(V_new), _ptr(ws), c_size_t(ws.numel()), _stream_ptr(stream)))
+        self._keep = [ws]   # the enqueued kernel reads it
 
     def remove(self, ids):
         import numpy as np
@@ -377,9 +408,14 @@ class Pool:
 
     def request(self, rid: int):
         """(tokens, pages, payload bytes) of a live request."""
-        n, pg, pb = c_int64(), c_int64(), c_uint64()
-        _check(lib().mkv_pool_request(self.handle, int(rid), byref(n), byref(pg), byref(pb)))
+        n, cap, pg, pb = c_int64(), c_int64(), c_int64(), c_uint64()
+        _check(lib().mkv_pool_request(self.handle, int(rid), byref(n), byref(cap), byref(pg), byref(pb)))
         return int(n.value), int(pg.value), int(pb.value)
+
+    def capacity(self, rid: int) -> int:
+        cap = c_int64()
+        _check(lib().mkv_pool_request(self.handle, int(rid), None, byref(cap), None, None))
+        return int(cap.value)
 
     def close(self):
         if self.handle is not None and self.handle.value:

@@ -230,7 +230,7 @@ struct ScratchLayout {
 ScratchLayout scratch_layout(const Shape& sh) {
     ScratchLayout L;
     L.tab = 0;
-    L.thr = align_up(sizeof(int32_t) * (5ull * sh.B + 1));
+    L.thr = align_up(sizeof(int32_t) * (6ull * sh.B + 1));
     L.wg = align_up(L.thr + 2ull * sh.total * sh.Hkv * 4 * sizeof(uint16_t));
     L.bytes = L.wg + 2ull * std::max<int64_t>(cmp_plan(sh).nblk, 1) * sizeof(uint64_t);
     return L;
@@ -334,7 +334,7 @@ static mkv_status compress(const mkv_kv_desc* kv, const float* basis, const mkv_
     uint8_t* base = static_cast<uint8_t*>(store_buf);
     uint8_t* scr = static_cast<uint8_t*>(scratch);
     const int64_t spw = cmp_plan(sh).spw;
-    std::vector<int32_t> tab(5 * sh.B + 1);
+    std::vector<int32_t> tab(6 * sh.B + 1);
     int64_t nblk = 0;
     for (int r = 0; r < sh.B; ++r) {
         const int64_t n = sh.cu[r + 1] - sh.cu[r];
@@ -343,6 +343,7 @@ static mkv_status compress(const mkv_kv_desc* kv, const float* basis, const mkv_
         tab[2 * sh.B + r] = sh.segbase[r];
         tab[3 * sh.B + r] = sh.scap[r];
         tab[4 * sh.B + r] = (int32_t)nblk;
+        tab[5 * sh.B + 1 + r] = r;   // open slot
         nblk += (int64_t)sh.Hkv * cdiv(cdiv(n, MKV_SEG_LEN), spw);
     }
     tab[5 * sh.B] = (int32_t)nblk;
@@ -403,7 +404,7 @@ mkv_status mkv_compress_growable(const mkv_kv_desc* kv, const float* basis, cons
 
 mkv_status mkv_append_workspace_bytes(const mkv_store* s, size_t* ws_bytes) {
     if (!s || !ws_bytes) return fail(MKV_E_ARG, "store and ws_bytes must be non-NULL");
-    *ws_bytes = align_up(16ull * s->sh.B);
+    *ws_bytes = align_up(20ull * s->sh.B);
     return MKV_OK;
 }
 
@@ -415,18 +416,19 @@ mkv_status mkv_append(mkv_store* s, const void* K_new, const void* V_new, const 
     if (!sh.growable) return fail(MKV_E_ARG, "the store was not built growable (mkv_compress_growable)");
     if (!K_new || !V_new) return fail(MKV_E_ARG, "K_new and V_new must be non-NULL");
     if (!ws || !aligned(ws)) return fail(MKV_E_ARG, "ws must be non-NULL and 256-byte aligned");
-    if (ws_bytes < align_up(16ull * sh.B)) return fail(MKV_E_ARG, "ws_bytes %zu too small", ws_bytes);
+    if (ws_bytes < align_up(20ull * sh.B)) return fail(MKV_E_ARG, "ws_bytes %zu too small", ws_bytes);
     std::vector<int32_t> tab;
     for (int r = 0; r < sh.B; ++r) {
         if (active && !active[r]) continue;
         const int64_t n = sh.cu[r + 1] - sh.cu[r];
         if (n + 1 > sh.cap[r]) return fail(MKV_E_ARG, "request %d is at its capacity (%lld tokens)", r, (long long)sh.cap[r]);
-        tab.push_back(r);
+        tab.push_back(r);                     // row of K_new / V_new
         tab.push_back((int32_t)n);
         tab.push_back(sh.Hkv * sh.segbase[r]);
         tab.push_back(sh.scap[r]);
+        tab.push_back(r);                     // open slot
     }
-    const int n_req = (int)(tab.size() / 4);
+    const int n_req = (int)(tab.size() / 5);
     if (n_req == 0) return MKV_OK;
     int32_t* tdev = static_cast<int32_t*>(ws);
     mkv_status st;
@@ -451,11 +453,12 @@ mkv_status mkv_append(mkv_store* s, const void* K_new, const void* V_new, const 
     x.open_bytes = L.open_bytes;
     x.open_rows = reinterpret_cast<uint16_t*>(s->base + L.open_rows);
     x.total = reinterpret_cast<unsigned long long*>(s->base);
+    x.seal_off = nullptr;
     if ((st = run(K_APPEND, stream, [&] { return launch_cmp_append(a, x, n_req, stream); }))) return st;
     // the listed requests now hold one more token
     std::vector<int64_t> n(sh.B);
     for (int r = 0; r < sh.B; ++r) n[r] = sh.cu[r + 1] - sh.cu[r];
-    for (int i = 0; i < n_req; ++i) n[tab[4 * i]] += 1;
+    for (int i = 0; i < n_req; ++i) n[tab[5 * i]] += 1;
     for (int r = 0; r < sh.B; ++r) sh.cu[r + 1] = sh.cu[r] + n[r];
     sh.total = sh.cu[sh.B];
     return MKV_OK;
@@ -523,7 +526,7 @@ mkv_status mkv_store_destroy(mkv_store* s) {
 namespace {
 
 struct PoolLayout {
-    uint64_t codes, seg_off, basis, payload, bytes;
+    uint64_t codes, seg_off, basis, payload, open_pack, open_rows, open_bytes, bytes;
 };
 
 int64_t pool_max_segment_bytes(mkv_dtype dt) { return (int64_t)MKV_SEG_LEN * MKV_HEAD_DIM * dtype_bytes(dt); }
@@ -540,6 +543,7 @@ mkv_status check_pool_desc(const mkv_pool_desc* d) {
     if (d->page_bytes % kAlign != 0 || d->page_bytes < pool_max_segment_bytes(d->dtype) || d->page_bytes > (1ll << 31))
         return fail(MKV_E_ARG, "page_bytes (%lld) must be a multiple of 256 in [%lld, 2^31]", (long long)d->page_bytes,
                     (long long)pool_max_segment_bytes(d->dtype));
+    if (d->appendable && d->dtype != MKV_BF16) return fail(MKV_E_UNSUPPORTED, "appendable pools take bf16 K/V only");
     return MKV_OK;
 }
 
@@ -551,7 +555,13 @@ PoolLayout pool_layout(const mkv_pool_desc& d) {
     L.basis = align_up(L.seg_off + 16 * S);
     L.payload = align_up(L.basis + (d.has_basis ? (uint64_t)d.max_requests * d.n_kv_heads * 2 * MKV_HEAD_DIM *
                                                      MKV_HEAD_DIM * sizeof(float) : 0));
-    L.bytes = L.payload + (uint64_t)d.n_pages * d.page_bytes + kAlign;   // slack: fixed-shape row loads may read past
+    // appendable pools: per request id and stream, an open-segment area (packed, addressed like the payload)
+    // and the open segment's original rows
+    L.open_bytes = d.appendable ? (uint64_t)pool_max_segment_bytes(d.dtype) : 0;
+    const uint64_t streams = 2ull * d.max_requests * d.n_kv_heads;
+    L.open_pack = L.payload + (uint64_t)d.n_pages * d.page_bytes;
+    L.open_rows = L.open_pack + streams * L.open_bytes;
+    L.bytes = L.open_rows + streams * L.open_bytes + kAlign;   // slack: fixed-shape row loads may read past
     return L;
 }
 
@@ -590,9 +600,12 @@ struct mkv_pool {
     std::map<int64_t, int64_t> free_ranges;    // free segment-slot ranges (units of n_kv_heads slots): start -> length
     struct Req {
         int64_t n = -1;                        // tokens; -1: the id is free
-        int32_t ubase = 0, scap = 0;           // first slot unit and slots per stream
+        int64_t cap = 0;                       // token capacity (appendable pools; else n)
+        int32_t ubase = 0, scap = 0;           // first slot unit and slots per stream (from the capacity)
         std::vector<int32_t> pages;
-        uint64_t payload = 0;
+        uint64_t payload = 0;                  // packed bytes (appended segments: their reserved bytes)
+        int32_t apage = -1;                    // page taking this request's appended segments
+        uint64_t aused = 0;                    // bytes reserved in it
     };
     std::vector<Req> req;
     std::vector<int32_t> free_ids;             // stack
@@ -698,8 +711,8 @@ mkv_status mkv_pool_add_scratch_bytes(const mkv_pool* p, const mkv_kv_desc* kv, 
     return MKV_OK;
 }
 
-mkv_status mkv_pool_add(mkv_pool* p, const mkv_kv_desc* kv, const float* basis, void* scratch, size_t scratch_bytes,
-                        mkv_stream_t stream_, int32_t* ids) {
+mkv_status mkv_pool_add(mkv_pool* p, const mkv_kv_desc* kv, const float* basis, const int64_t* capacity,
+                        void* scratch, size_t scratch_bytes, mkv_stream_t stream_, int32_t* ids) {
     hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
     Shape ash;
     mkv_status st = pool_add_shape(p, kv, true, &ash);
@@ -712,13 +725,19 @@ mkv_status mkv_pool_add(mkv_pool* p, const mkv_kv_desc* kv, const float* basis, 
     if (scratch_bytes < SL.bytes) return fail(MKV_E_ARG, "scratch_bytes %zu < required %llu", scratch_bytes, (unsigned long long)SL.bytes);
     const int B = ash.B, Hkv = ash.Hkv;
     if ((int)p->free_ids.size() < B) return fail(MKV_E_ARG, "the pool has %zu free request ids, %d requested", p->free_ids.size(), B);
+    if (capacity && !p->d.appendable) return fail(MKV_E_ARG, "capacities need an appendable pool");
+    for (int r = 0; capacity && r < B; ++r)
+        if (capacity[r] < ash.cu[r + 1] - ash.cu[r] || capacity[r] > INT32_MAX)
+            return fail(MKV_E_ARG, "capacity[%d] = %lld must lie in [its context %lld, 2^31)", r, (long long)capacity[r],
+                        (long long)(ash.cu[r + 1] - ash.cu[r]));
 
     // request ids and segment-slot ranges (host bookkeeping; undone if anything below fails)
     std::vector<int32_t> got;
     auto undo = [&] { for (auto it = got.rbegin(); it != got.rend(); ++it) pool_release(p, *it); };
     for (int r = 0; r < B; ++r) {
         const int64_t n = ash.cu[r + 1] - ash.cu[r];
-        const int32_t scap = (int32_t)cdiv(n, MKV_SEG_LEN);
+        const int64_t cap = capacity ? capacity[r] : n;
+        const int32_t scap = (int32_t)cdiv(cap, MKV_SEG_LEN);
         const int64_t ub = pool_take_range(p, scap);
         if (ub < 0) {
             undo();
@@ -730,6 +749,7 @@ mkv_status mkv_pool_add(mkv_pool* p, const mkv_kv_desc* kv, const float* basis, 
         ++p->live;
         mkv_pool::Req& q = p->req[id];
         q.n = n;
+        q.cap = cap;
         q.ubase = (int32_t)ub;
         q.scap = scap;
         got.push_back(id);
@@ -738,7 +758,7 @@ mkv_status mkv_pool_add(mkv_pool* p, const mkv_kv_desc* kv, const float* basis, 
     uint8_t* scr = static_cast<uint8_t*>(scratch);
     const ScratchLayout CL = scratch_layout(ash);
     const int64_t spw = cmp_plan(ash).spw;
-    std::vector<int32_t> tab(5 * B + 1);
+    std::vector<int32_t> tab(6 * B + 1);
     int64_t nblk = 0;
     for (int r = 0; r < B; ++r) {
         const int64_t n = ash.cu[r + 1] - ash.cu[r];
@@ -747,6 +767,7 @@ mkv_status mkv_pool_add(mkv_pool* p, const mkv_kv_desc* kv, const float* basis, 
         tab[2 * B + r] = p->req[got[r]].ubase;
         tab[3 * B + r] = p->req[got[r]].scap;
         tab[4 * B + r] = (int32_t)nblk;
+        tab[5 * B + 1 + r] = got[r];   // open slot: the request's id
         nblk += (int64_t)Hkv * cdiv(cdiv(n, MKV_SEG_LEN), spw);
     }
     tab[5 * B] = (int32_t)nblk;
@@ -775,6 +796,10 @@ mkv_status mkv_pool_add(mkv_pool* p, const mkv_kv_desc* kv, const float* basis, 
     a.n_keep = p->policy.n_keep;
     a.frac = p->policy.energy_frac;
     a.preplaced = 1;
+    if (p->d.appendable) {
+        a.open_rows = reinterpret_cast<uint16_t*>(p->base + p->lay.open_rows);
+        a.open_elems = (int64_t)(p->lay.open_bytes / 2);
+    }
     PoolArgs pa;
     std::memset(&pa, 0, sizeof pa);
     pa.tab = a.tab;
@@ -844,6 +869,98 @@ mkv_status mkv_pool_add(mkv_pool* p, const mkv_kv_desc* kv, const float* basis, 
     return MKV_OK;
 }
 
+mkv_status mkv_pool_append_workspace_bytes(const mkv_pool* p, int32_t n, size_t* ws_bytes) {
+    if (!p || !ws_bytes || n < 0) return fail(MKV_E_ARG, "pool and ws_bytes must be non-NULL, n >= 0");
+    *ws_bytes = align_up(20ull * n) + align_up(16ull * n * p->d.n_kv_heads);
+    return MKV_OK;
+}
+
+mkv_status mkv_pool_append(mkv_pool* p, int32_t n, const int32_t* ids, const void* K_new, const void* V_new, void* ws,
+                           size_t ws_bytes, mkv_stream_t stream_) {
+    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
+    if (!p) return fail(MKV_E_ARG, "pool is NULL");
+    if (!p->d.appendable) return fail(MKV_E_ARG, "the pool was not created appendable");
+    if (n < 0 || (n > 0 && (!ids || !K_new || !V_new))) return fail(MKV_E_ARG, "ids, K_new and V_new must be non-NULL");
+    if (n == 0) return MKV_OK;
+    size_t need = 0;
+    mkv_pool_append_workspace_bytes(p, n, &need);
+    if (!ws || !aligned(ws) || ws_bytes < need) return fail(MKV_E_ARG, "ws must be 256-byte aligned with >= %zu bytes", need);
+    const int Hkv = p->d.n_kv_heads;
+    const uint64_t seal = (uint64_t)pool_max_segment_bytes(p->d.dtype);   // reserved per sealed segment
+    int64_t new_pages = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        if (ids[i] < 0 || ids[i] >= p->d.max_requests || p->req[ids[i]].n < 0)
+            return fail(MKV_E_ARG, "request id %d is not in the pool", ids[i]);
+        for (int32_t j = 0; j < i; ++j)
+            if (ids[j] == ids[i]) return fail(MKV_E_ARG, "request id %d is listed twice", ids[i]);
+        const mkv_pool::Req& q = p->req[ids[i]];
+        if (q.n + 1 > q.cap) return fail(MKV_E_ARG, "request %d is at its capacity (%lld tokens)", ids[i], (long long)q.cap);
+        if ((q.n + 1) % MKV_SEG_LEN == 0) {   // this append seals the request's 2 * n_kv_heads open segments
+            uint64_t used = q.apage < 0 ? (uint64_t)p->d.page_bytes : q.aused;
+            for (int k = 0; k < 2 * Hkv; ++k) {
+                if (used + seal > (uint64_t)p->d.page_bytes) { ++new_pages; used = 0; }
+                used += seal;
+            }
+        }
+    }
+    if (new_pages > (int64_t)p->free_pages.size())
+        return fail(MKV_E_ARG, "the pool has %zu free pages, sealing the listed requests' segments needs %lld",
+                    p->free_pages.size(), (long long)new_pages);
+    // host-side placement of the sealed segments (worst-case size each), then one kernel
+    std::vector<int32_t> words(5 * (size_t)n);
+    std::vector<uint64_t> seals(2 * (size_t)Hkv * n, 0);
+    for (int32_t i = 0; i < n; ++i) {
+        mkv_pool::Req& q = p->req[ids[i]];
+        words[5 * i] = i;
+        words[5 * i + 1] = (int32_t)q.n;
+        words[5 * i + 2] = Hkv * q.ubase;
+        words[5 * i + 3] = q.scap;
+        words[5 * i + 4] = ids[i];
+        if ((q.n + 1) % MKV_SEG_LEN != 0) continue;
+        for (int k = 0; k < 2 * Hkv; ++k) {
+            if (q.apage < 0 || q.aused + seal > (uint64_t)p->d.page_bytes) {
+                q.apage = p->free_pages.back();
+                p->free_pages.pop_back();
+                q.pages.push_back(q.apage);
+                q.aused = 0;
+            }
+            seals[2 * (size_t)Hkv * i + k] = (uint64_t)q.apage * p->d.page_bytes + q.aused;
+            q.aused += seal;
+            q.payload += seal;
+        }
+    }
+    std::vector<int32_t> up(words);
+    const size_t o_seal = align_up(20ull * n) / 4;
+    up.resize(o_seal + 4 * (size_t)Hkv * n, 0);
+    std::memcpy(up.data() + o_seal, seals.data(), seals.size() * sizeof(uint64_t));
+    int32_t* wdev = static_cast<int32_t*>(ws);
+    mkv_status st;
+    if ((st = upload_words(wdev, up, 0, stream))) return st;
+    CmpArgs a;
+    std::memset(&a, 0, sizeof a);
+    for (int k = 0; k < 4; ++k) a.keep[k] = k < p->policy.n_keep ? p->policy.keep[k] : 0;
+    a.n_keep = p->policy.n_keep;
+    a.frac = p->policy.energy_frac;
+    AppendArgs x;
+    x.Kn = static_cast<const uint16_t*>(K_new);
+    x.Vn = static_cast<const uint16_t*>(V_new);
+    x.basis = p->d.has_basis ? reinterpret_cast<const float*>(p->base + p->lay.basis) : nullptr;
+    x.tab = wdev;
+    x.seal_off = reinterpret_cast<const uint64_t*>(wdev + o_seal);
+    x.Hkv = Hkv;
+    x.S = p->d.segment_slots * Hkv;
+    x.codes = p->base + p->lay.codes;
+    x.seg_off = reinterpret_cast<uint64_t*>(p->base + p->lay.seg_off);
+    x.payload = p->base + p->lay.payload;
+    x.open_pack = p->lay.open_pack - p->lay.payload;
+    x.open_bytes = p->lay.open_bytes;
+    x.open_rows = reinterpret_cast<uint16_t*>(p->base + p->lay.open_rows);
+    x.total = nullptr;
+    if ((st = run(K_APPEND, stream, [&] { return launch_cmp_append(a, x, n, stream); }))) return st;
+    for (int32_t i = 0; i < n; ++i) p->req[ids[i]].n += 1;
+    return MKV_OK;
+}
+
 mkv_status mkv_pool_remove(mkv_pool* p, int32_t n, const int32_t* ids) {
     if (!p) return fail(MKV_E_ARG, "pool is NULL");
     if (n < 0 || (n > 0 && !ids)) return fail(MKV_E_ARG, "ids must list n >= 0 request ids");
@@ -871,14 +988,15 @@ mkv_status mkv_pool_view(const mkv_pool* p, int32_t n, const int32_t* ids, mkv_s
             return fail(MKV_E_ARG, "request id %d is not in the pool", ids[i]);
         const mkv_pool::Req& q = p->req[ids[i]];
         sh.cu.push_back(sh.cu.back() + q.n);
-        sh.cap.push_back(q.n);
+        sh.cap.push_back(q.cap);
         sh.scap.push_back(q.scap);
         sh.segbase.push_back(q.ubase);
         sh.bslot.push_back(ids[i]);
         payload += q.payload;
     }
     sh.total = sh.cu.back();
-    sh.total_cap = sh.total;
+    sh.total_cap = 0;
+    for (int64_t c : sh.cap) sh.total_cap += c;
     if (sh.total * (int64_t)sh.Hkv >= (int64_t)INT32_MAX)
         return fail(MKV_E_UNSUPPORTED, "total tokens x KV heads must stay below 2^31 (got %lld)", (long long)(sh.total * sh.Hkv));
     sh.S = p->d.segment_slots * sh.Hkv;
@@ -896,7 +1014,8 @@ mkv_status mkv_pool_view(const mkv_pool* p, int32_t n, const int32_t* ids, mkv_s
     h->lay.open_pack = h->lay.open_rows = h->lay.open_bytes = 0;
     h->lay.bytes = p->lay.bytes;
     h->base = p->base;
-    h->cu_cap = sh.cu;
+    h->cu_cap.assign(1, 0);
+    for (int32_t i = 0; i < n; ++i) h->cu_cap.push_back(h->cu_cap.back() + sh.cap[i]);
     h->pool_view = true;
     h->view_payload = payload;
     *out = h;
@@ -921,11 +1040,13 @@ mkv_status mkv_pool_stats(const mkv_pool* p, mkv_pool_info* info) {
     return MKV_OK;
 }
 
-mkv_status mkv_pool_request(const mkv_pool* p, int32_t id, int64_t* n_tokens, int64_t* pages, uint64_t* payload_bytes) {
+mkv_status mkv_pool_request(const mkv_pool* p, int32_t id, int64_t* n_tokens, int64_t* capacity, int64_t* pages,
+                            uint64_t* payload_bytes) {
     if (!p) return fail(MKV_E_ARG, "pool is NULL");
     if (id < 0 || id >= p->d.max_requests || p->req[id].n < 0) return fail(MKV_E_ARG, "request id %d is not in the pool", id);
     const mkv_pool::Req& q = p->req[id];
     if (n_tokens) *n_tokens = q.n;
+    if (capacity) *capacity = q.cap;
     if (pages) *pages = (int64_t)q.pages.size();
     if (payload_bytes) *payload_bytes = q.payload;
     return MKV_OK;

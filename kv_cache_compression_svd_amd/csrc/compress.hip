@@ -550,7 +550,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
             wg_off += (uint64_t)ns * c * (2 + (c < MKV_D ? 1 : 0));
             if (a.open_rows && ns < MKV_SEG && lrow < ns) {
                 // growable store: the stream's unfinished last segment keeps its original rows for appends
-                uint16_t* orow = a.open_rows + (((int64_t)t.r * a.Hkv + t.h) * 2 + t.X) * a.open_elems;
+                const int os = a.tab[5 * a.B + 1 + t.r];
+                uint16_t* orow = a.open_rows + (((int64_t)os * a.Hkv + t.h) * 2 + t.X) * a.open_elems;
                 u32x4* d = reinterpret_cast<u32x4*>(orow + lrow * MKV_D + lq * 16);
                 const u32x4* q = reinterpret_cast<const u32x4*>(&X[lrow * XS + lq * 16]);
                 d[0] = q[0];
@@ -585,7 +586,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 // store) and the new row form the tile; the tile is rotated, decided and packed by the same code as the
 // compressor, so the segment ends up exactly as compressing the extended context would leave it.  An open
 // segment lives in its stream's open area; the append that completes it (64 tokens) seals it into the payload
-// at a position taken from the payload counter.
+// at a position taken from the payload counter, or (pools) at the position the host reserved for it.
 __global__ __launch_bounds__(512) void k_cmp_append(CmpArgs a, AppendArgs x) {
     __shared__ __attribute__((aligned(16))) uint16_t xs[64 * XS];
     __shared__ __attribute__((aligned(16))) uint16_t xh[64 * XS];
@@ -595,13 +596,13 @@ __global__ __launch_bounds__(512) void k_cmp_append(CmpArgs a, AppendArgs x) {
     __shared__ unsigned long long s_pos;
     const int tid = threadIdx.x, lane = tid & 63, wid = uni(tid >> 6);
     const int ai = blockIdx.x / (2 * x.Hkv), rem = blockIdx.x - ai * 2 * x.Hkv, h = rem >> 1, X = rem & 1;
-    const int r = x.tab[4 * ai], n_old = x.tab[4 * ai + 1];
+    const int kr = x.tab[5 * ai], n_old = x.tab[5 * ai + 1], os = x.tab[5 * ai + 4];
     const int p = n_old & (MKV_SEG - 1), ns = p + 1;
-    const int64_t g = (int64_t)X * x.S + x.tab[4 * ai + 2] + (int64_t)h * x.tab[4 * ai + 3] + (n_old >> 6);
-    const int64_t st = ((int64_t)r * x.Hkv + h) * 2 + X;
+    const int64_t g = (int64_t)X * x.S + x.tab[5 * ai + 2] + (int64_t)h * x.tab[5 * ai + 3] + (n_old >> 6);
+    const int64_t st = ((int64_t)os * x.Hkv + h) * 2 + X;
     uint16_t* rows = x.open_rows + st * (int64_t)(x.open_bytes / 2);
-    const uint16_t* nr = (X ? x.Vn : x.Kn) + ((int64_t)r * x.Hkv + h) * MKV_D;
-    const float* Bm = x.basis ? x.basis + ((((size_t)r * x.Hkv + h) * 2 + X) << 14) : nullptr;
+    const uint16_t* nr = (X ? x.Vn : x.Kn) + ((int64_t)kr * x.Hkv + h) * MKV_D;
+    const float* Bm = x.basis ? x.basis + ((((size_t)os * x.Hkv + h) * 2 + X) << 14) : nullptr;
     bf16x8 bh[4], bmid[4], blo[4];
     if (Bm) basis_frags(Bm, wid, lane, bh, bmid, blo);
 
@@ -647,7 +648,8 @@ __global__ __launch_bounds__(512) void k_cmp_append(CmpArgs a, AppendArgs x) {
     const int c = a.keep[code];
     if (tid == 0) {
         const uint64_t bytes = (uint64_t)ns * c * (2 + (c < MKV_D ? 1 : 0));
-        s_pos = ns == MKV_SEG ? atomicAdd(x.total, (unsigned long long)bytes) : x.open_pack + st * x.open_bytes;
+        s_pos = ns < MKV_SEG ? x.open_pack + st * x.open_bytes
+              : x.seal_off ? x.seal_off[blockIdx.x] : atomicAdd(x.total, (unsigned long long)bytes);
         x.codes[g] = (uint8_t)code;
     }
     if (c < MKV_D && valid) vector_pack8(w, thr[code], c, v, pl, ns, stg);

@@ -30,7 +30,7 @@ struct CmpArgs {
     const void* K;
     const void* V;
     const float* basis;         // [B][Hkv][2][128][128] or null (inputs already rotated)
-    const int32_t* tab;         // tok_base[B] | n[B] | seg_base[B] | slots per stream[B] | cblk_base[B+1]
+    const int32_t* tab;         // tok_base[B] | n[B] | seg_base[B] | slots per stream[B] | cblk_base[B+1] | open slot[B]
     int32_t B, Hkv, spw, nblk;  // spw: segments per workgroup; nblk: workgroups per tensor
     int64_t S;                  // segments per tensor
     int64_t total_tokens;
@@ -42,7 +42,8 @@ struct CmpArgs {
     int32_t keep[4];
     int32_t n_keep;
     double frac;
-    uint16_t* open_rows;        // growable stores: original rows of each stream's open segment (else null)
+    uint16_t* open_rows;        // growable stores: original rows of each stream's open segment (else null), by
+                                // open slot (the request's index, or its id in a pool)
     int64_t open_elems;         // elements per stream in open_rows
     int32_t preplaced;          // pack: seg_off already holds every segment's payload offset (paged pools)
 };
@@ -62,12 +63,15 @@ struct PoolArgs {
     const int32_t* page_ids;    // page of each (stream, ordinal) (fix)
 };
 
-// One token appended to each listed request of a growable bf16 store.
+// One token appended to each listed request of a growable bf16 store or pool.
 struct AppendArgs {
-    const uint16_t* Kn;         // [B][Hkv][128]
+    const uint16_t* Kn;         // [rows][Hkv][128]
     const uint16_t* Vn;
-    const float* basis;         // the store's copy, or null
-    const int32_t* tab;         // per listed request: r | its tokens before the append | Hkv * seg_base | slots per stream
+    const float* basis;         // the store's copy, or null; indexed by open slot
+    const int32_t* tab;         // per listed request: row of Kn/Vn | its tokens before the append | Hkv * seg_base |
+                                // slots per stream | open slot (open areas and basis)
+    const uint64_t* seal_off;   // [listed][2*Hkv] payload offset of a segment the append completes (pools), or null:
+                                // taken from the payload counter
     int32_t Hkv;
     int64_t S;                  // segment slots per tensor
     uint8_t* codes;

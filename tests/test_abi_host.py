@@ -219,27 +219,73 @@ def test_pool_layout_and_host_checks():
     out = ctypes.c_void_p()
     assert L.mkv_pool_view(h, 1, ids, ctypes.byref(out)) == mkv.MKV_E_ARG and "not in the pool" in mkv.mkv_last_error()
     assert L.mkv_pool_remove(h, 1, ids) == mkv.MKV_E_ARG
-    assert L.mkv_pool_request(h, 0, None, None, None) == mkv.MKV_E_ARG
+    assert L.mkv_pool_request(h, 0, None, None, None, None) == mkv.MKV_E_ARG
     # adds whose shape or basis does not match the pool fail before anything is enqueued
     kd, cu = _desc(batch=1, heads=3, cu=(0, 100))
     kd.K, kd.V = ctypes.c_void_p(256), ctypes.c_void_p(512)
     got = (ctypes.c_int32 * 1)()
     fake = ctypes.c_void_p(1 << 24)
-    assert L.mkv_pool_add(h, ctypes.byref(kd), fake, fake, 1 << 30, None, got) == mkv.MKV_E_ARG
+    assert L.mkv_pool_add(h, ctypes.byref(kd), fake, None, fake, 1 << 30, None, got) == mkv.MKV_E_ARG
     assert "n_kv_heads" in mkv.mkv_last_error()
     kd, cu = _desc(batch=1, heads=2, cu=(0, 100))
     kd.K, kd.V = ctypes.c_void_p(256), ctypes.c_void_p(512)
-    assert L.mkv_pool_add(h, ctypes.byref(kd), None, fake, 1 << 30, None, got) == mkv.MKV_E_ARG
+    assert L.mkv_pool_add(h, ctypes.byref(kd), None, None, fake, 1 << 30, None, got) == mkv.MKV_E_ARG
     assert "basis" in mkv.mkv_last_error()
+    cap = (ctypes.c_int64 * 1)(200)
+    assert L.mkv_pool_add(h, ctypes.byref(kd), fake, cap, fake, 1 << 30, None, got) == mkv.MKV_E_ARG
+    assert "appendable" in mkv.mkv_last_error()
+    ws = ctypes.c_size_t()
+    assert L.mkv_pool_append_workspace_bytes(h, 2, ctypes.byref(ws)) == mkv.MKV_OK
+    assert L.mkv_pool_append(h, 1, got, fake, fake, fake, ws.value, None) == mkv.MKV_E_ARG
+    assert "appendable" in mkv.mkv_last_error()
     sb = ctypes.c_size_t()
     assert L.mkv_pool_add_scratch_bytes(h, ctypes.byref(kd), ctypes.byref(sb)) == mkv.MKV_OK
-    assert L.mkv_pool_add(h, ctypes.byref(kd), fake, fake, sb.value - 1, None, got) == mkv.MKV_E_ARG
+    assert L.mkv_pool_add(h, ctypes.byref(kd), fake, None, fake, sb.value - 1, None, got) == mkv.MKV_E_ARG
     # more requests than free ids
     kd, cu = _desc(batch=5, heads=2, cu=(0, 1, 2, 3, 4, 5))
     kd.K, kd.V = ctypes.c_void_p(256), ctypes.c_void_p(512)
     got5 = (ctypes.c_int32 * 5)()
-    assert L.mkv_pool_add(h, ctypes.byref(kd), fake, fake, 1 << 30, None, got5) == mkv.MKV_E_ARG
+    assert L.mkv_pool_add(h, ctypes.byref(kd), fake, None, fake, 1 << 30, None, got5) == mkv.MKV_E_ARG
     assert "ids" in mkv.mkv_last_error()
     assert L.mkv_pool_stats(h, ctypes.byref(info)) == mkv.MKV_OK
     assert (info.free_pages, info.free_segment_slots, info.live_requests) == (8, 10, 0)
     assert L.mkv_pool_destroy(h) == mkv.MKV_OK
+
+
+def test_appendable_pool_layout_and_refusals():
+    L = mkv.lib()
+    align = lambda x: (x + 255) // 256 * 256   # noqa: E731
+    plain, grow = _pool_desc(has_basis=0), _pool_desc(has_basis=0)
+    grow.appendable = 1
+    nb0, nb1 = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.mkv_pool_bytes(ctypes.byref(plain), ctypes.byref(nb0)) == mkv.MKV_OK
+    assert L.mkv_pool_bytes(ctypes.byref(grow), ctypes.byref(nb1)) == mkv.MKV_OK
+    # per request id, KV head and tensor: a packed open segment and its original rows, 64 x 128 bf16 each
+    assert nb1.value - nb0.value == 2 * (4 * 2 * 2) * 64 * 128 * 2
+    bad = _pool_desc(dtype=mkv.MKV_FP32, page_bytes=32768)
+    bad.appendable = 1
+    assert L.mkv_pool_bytes(ctypes.byref(bad), ctypes.byref(nb0)) == mkv.MKV_E_UNSUPPORTED
+    p = mkv.mkv_default_policy()
+    h = ctypes.c_void_p()
+    assert L.mkv_pool_create(ctypes.byref(grow), ctypes.byref(p), ctypes.c_void_p(1 << 20), nb1.value, ctypes.byref(h)) == mkv.MKV_OK
+    fake = ctypes.c_void_p(1 << 24)
+    ws = ctypes.c_size_t()
+    assert L.mkv_pool_append_workspace_bytes(h, 3, ctypes.byref(ws)) == mkv.MKV_OK
+    assert ws.value == align(20 * 3) + align(16 * 3 * 2)
+    ids = (ctypes.c_int32 * 1)(0)
+    assert L.mkv_pool_append(h, 1, ids, fake, fake, fake, ws.value, None) == mkv.MKV_E_ARG   # id 0 not live
+    assert "not in the pool" in mkv.mkv_last_error()
+    assert L.mkv_pool_append(h, 0, None, None, None, None, 0, None) == mkv.MKV_OK            # nothing to do
+    kd, cu = _desc(batch=1, heads=2, cu=(0, 100))
+    kd.K, kd.V = ctypes.c_void_p(256), ctypes.c_void_p(512)
+    cap = (ctypes.c_int64 * 1)(99)                                                          # below the context
+    got = (ctypes.c_int32 * 1)()
+    assert L.mkv_pool_add(h, ctypes.byref(kd), None, cap, fake, 1 << 30, None, got) == mkv.MKV_E_ARG
+    assert "capacity" in mkv.mkv_last_error()
+    cap[0] = 64 * 11                                                                        # 11 slots > 10
+    assert L.mkv_pool_add(h, ctypes.byref(kd), None, cap, fake, 1 << 30, None, got) == mkv.MKV_E_ARG
+    assert "slots" in mkv.mkv_last_error()
+    info = mkv.PoolInfo()
+    L.mkv_pool_stats(h, ctypes.byref(info))
+    assert (info.free_pages, info.free_segment_slots, info.live_requests) == (8, 10, 0)
+    L.mkv_pool_destroy(h)

@@ -55,9 +55,9 @@ class Reqs:
                 self.T[idx])
 
 
-def _pool(mkv, n_pages, page_bytes, slots, max_req=16, dtype="bf16", has_basis=True):
+def _pool(mkv, n_pages, page_bytes, slots, max_req=16, dtype="bf16", has_basis=True, appendable=False):
     code = mkv.MKV_BF16 if dtype == "bf16" else mkv.MKV_FP32
-    return mkv.Pool(4, code, max_req, slots, n_pages, page_bytes, has_basis=has_basis)
+    return mkv.Pool(4, code, max_req, slots, n_pages, page_bytes, has_basis=has_basis, appendable=appendable)
 
 
 def _same_as_plain(mkv, pool, ids, R, order, dtype="bf16"):
@@ -102,8 +102,11 @@ def _check_placement(pool, views, dtype="bf16"):
                         c = keep[int(codes[g])]
                         nb = min(SEG, n - s * SEG) * c * (bv + (c < 128))
                         o = int(offs[g])
-                        assert o // pb == (o + nb - 1) // pb, "segment straddles two pages"
-                        assert o + nb <= int(info.desc.n_pages) * pb
+                        if o >= int(info.desc.n_pages) * pb:   # an open segment, in its stream's open area
+                            assert o + nb <= int(info.pool_bytes)
+                        else:
+                            assert o // pb == (o + nb - 1) // pb, "segment straddles two pages"
+                            assert o + nb <= int(info.desc.n_pages) * pb
                         spans.append((o, o + nb))
     spans = sorted(set(spans))
     for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
@@ -222,3 +225,105 @@ def test_pool_against_the_oracle(mkv_lib):
             nd = check_decode_unit(sel[vr, h], out[vr, h * G:(h + 1) * G], qg, inp.basis[r, h, 0], inp.basis[r, h, 1],
                                    got[(vr, h, 0)], got[(vr, h, 1)], min(int(T[vr]), n))
             assert nd >= 0
+
+
+def _grow_in_pool(mkv, R, n0, steps, pool, active_of=None):
+    """Adds the first n0[r] tokens of each request of R with their full contexts as capacities, then appends
+    `steps` tokens (request r takes part in step k when active_of(k)[r]); returns the ids and token counts."""
+    import torch
+    cu = R.cu
+    B = len(n0)
+    take = torch.as_tensor(np.concatenate([np.arange(cu[r], cu[r] + n0[r]) for r in range(B)]), device="cuda")
+    cu0 = np.concatenate([[0], np.cumsum(n0)]).astype(np.int64)
+    cap = np.diff(cu)
+    ids = pool.add(R.K[take].contiguous(), R.V[take].contiguous(), cu0, R.basis, capacity=cap)
+    n = np.array(n0)
+    for k in range(steps):
+        act = np.ones(B, dtype=bool) if active_of is None else np.asarray(active_of(k), dtype=bool)
+        act &= n < cap
+        rs = np.nonzero(act)[0]
+        if rs.size == 0:
+            continue
+        rows = torch.as_tensor(cu[:-1][rs] + n[rs], device="cuda")
+        pool.append(ids[rs], R.K[rows].contiguous(), R.V[rows].contiguous())
+        n[rs] += 1
+    torch.cuda.synchronize()
+    for r in range(B):
+        assert pool.request(int(ids[r]))[0] == n[r] and pool.capacity(int(ids[r])) == cap[r]
+    return ids, n
+
+
+def _same_as_plain_prefix(mkv, pool, ids, R, n, dtype="bf16"):
+    """A view of the grown requests against compressing their first n[r] tokens at once: segments and decode."""
+    import torch
+    cu = R.cu
+    B = len(n)
+    view = pool.view(ids)
+    assert np.array_equal(np.diff(view.cu), n)
+    take = torch.as_tensor(np.concatenate([np.arange(cu[r], cu[r] + n[r]) for r in range(B)]), device="cuda")
+    ref = mkv.mkv_compress(R.K[take].contiguous(), R.V[take].contiguous(), np.concatenate([[0], np.cumsum(n)]),
+                           R.basis)
+    g, f = read_store(view, dtype)["streams"], read_store(ref, dtype)["streams"]
+    for key in f:
+        assert np.array_equal(g[key].c, f[key].c), key
+        assert np.array_equal(g[key].mask, f[key].mask), key
+        assert np.array_equal(g[key].vals, f[key].vals), key
+    o1, s1 = mkv.mkv_decode_attn(view, R.q, R.T)
+    o2, s2 = mkv.mkv_decode_attn(ref, R.q, R.T)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2) and torch.equal(o1, o2)
+    return view
+
+
+@pytest.mark.parametrize("n0,steps", [([64, 100, 0], 70), ([1, 63, 128], 66)])
+def test_pool_appends_equal_compressing_the_extended_context(mkv_lib, n0, steps):
+    mkv = mkv_lib
+    R = Reqs([a + steps for a in n0], seed=76)
+    pool = _pool(mkv, n_pages=200, page_bytes=40960, slots=64, appendable=True)
+    ids, n = _grow_in_pool(mkv, R, n0, steps, pool)
+    view = _same_as_plain_prefix(mkv, pool, ids, R, n)
+    _check_placement(pool, [view])
+
+
+def test_pool_appends_to_a_subset_then_removal(mkv_lib):
+    mkv = mkv_lib
+    R = Reqs([150, 90, 70], seed=77)
+    pool = _pool(mkv, n_pages=300, page_bytes=16384, slots=32, max_req=4, appendable=True)
+    free0 = pool.stats().free_pages
+    ids, n = _grow_in_pool(mkv, R, [60, 20, 63], 80, pool, active_of=lambda k: [k % 2 == 0, True, k < 3])
+    _same_as_plain_prefix(mkv, pool, ids, R, n)
+    # the request at its capacity refuses one more token, and nothing changes
+    full = [r for r in range(3) if n[r] == np.diff(R.cu)[r]]
+    assert full
+    import torch
+    before = pool.stats().free_pages
+    with pytest.raises(mkv.MkvError) as ei:
+        rows = torch.as_tensor([R.cu[full[0]]], device="cuda")
+        pool.append(ids[full[:1]], R.K[rows].contiguous(), R.V[rows].contiguous())
+    assert ei.value.status == mkv.MKV_E_ARG and "capacity" in str(ei.value)
+    assert pool.stats().free_pages == before and pool.request(int(ids[full[0]]))[0] == n[full[0]]
+    pool.remove(ids)
+    st = pool.stats()
+    assert st.free_pages == free0 and st.live_requests == 0 and st.free_segment_slots == 32
+
+
+def test_pool_append_refused_without_pages(mkv_lib):
+    """An append that would seal segments with no page left fails before anything is enqueued."""
+    mkv = mkv_lib
+    import torch
+    R2 = Reqs([200], seed=78)
+    cu0 = np.array([0, 127], dtype=np.int64)
+    # the pages the first 127 tokens take, measured in a roomy pool; the tight pool has exactly those, so none is
+    # spare for the 8 segments (4 KV heads x 2 tensors) that the 128th token seals
+    probe = _pool(mkv, n_pages=64, page_bytes=16384, slots=8, appendable=True)
+    p127 = probe.request(int(probe.add(R2.K[:127].contiguous(), R2.V[:127].contiguous(), cu0, R2.basis,
+                                       capacity=[200])[0]))[1]
+    pool = _pool(mkv, n_pages=p127, page_bytes=16384, slots=8, appendable=True)
+    ids = pool.add(R2.K[:127].contiguous(), R2.V[:127].contiguous(), cu0, R2.basis, capacity=[200])
+    assert pool.stats().free_pages == 0
+    rows = torch.as_tensor([127], device="cuda")
+    with pytest.raises(mkv.MkvError) as ei:
+        pool.append(ids, R2.K[rows].contiguous(), R2.V[rows].contiguous())
+    assert ei.value.status == mkv.MKV_E_ARG and "pages" in str(ei.value)
+    assert pool.request(int(ids[0]))[0] == 127
+    _same_as_plain_prefix(mkv, pool, ids, R2, np.array([127]))
