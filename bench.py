@@ -302,11 +302,14 @@ def main():
     if args.pool:
         page = 256 * 1024
         n_pages = int(payload * 1.05) // page + 2 * w.batch * w.n_kv_heads + 64
+        grow = 256 if w.dtype == "bf16" else 0   # appendable (bf16): room for 256 more tokens per request
+        n_pages += 2 * w.batch * (grow // 64 + 1) * (2 * w.n_kv_heads * 64 * 128 * 2) // page
         pool = mkv.Pool(w.n_kv_heads, mkv.MKV_BF16 if w.dtype == "bf16" else mkv.MKV_FP32, w.batch,
-                        int(np.sum((np.diff(inp.cu_seqlens) + 63) // 64)), n_pages, page, policy=policy)
+                        int(np.sum((np.diff(inp.cu_seqlens) + grow + 63) // 64)), n_pages, page, policy=policy,
+                        appendable=grow > 0)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        ids = pool.add(K, V, inp.cu_seqlens, basis)
+        ids = pool.add(K, V, inp.cu_seqlens, basis, capacity=(np.diff(inp.cu_seqlens) + grow) if grow else None)
         torch.cuda.synchronize()
         add_ms = (time.perf_counter() - t0) * 1e3
         view = pool.view(ids)
@@ -332,6 +335,19 @@ def main():
                     "ms_per_step_view": p_ms, "context_tokens_per_s_view": total_tokens / (p_ms * 1e-3),
                     "view_equals_store": bool(torch.equal(pout, out) and torch.equal(psel, sel)),
                     "page_fill": payload / ((n_pages - int(st.free_pages)) * page)}
+        if grow:   # one token for every pooled request per call
+            newK = K[:w.batch].reshape(w.batch, w.n_kv_heads, 128).contiguous()
+            newV = V[:w.batch].reshape(w.batch, w.n_kv_heads, 128).contiguous()
+            pws = torch.empty(64 * 1024, dtype=torch.uint8, device=dev)
+            for _ in range(4):
+                pool.append(ids, newK, newV, ws=pws)
+            torch.cuda.synchronize()
+            n_app = 64
+            t0 = time.perf_counter()
+            for _ in range(n_app):
+                pool.append(ids, newK, newV, ws=pws)
+            torch.cuda.synchronize()
+            pool_res["ms_per_append_call"] = (time.perf_counter() - t0) * 1e3 / n_app
         del view, pool
 
     sel_np = sel.cpu().numpy()
