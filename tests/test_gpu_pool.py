@@ -327,3 +327,93 @@ def test_pool_append_refused_without_pages(mkv_lib):
     assert ei.value.status == mkv.MKV_E_ARG and "pages" in str(ei.value)
     assert pool.request(int(ids[0]))[0] == 127
     _same_as_plain_prefix(mkv, pool, ids, R2, np.array([127]))
+
+
+def test_random_pool_lifecycle(mkv_lib):
+    """A seeded sequence of adds (some with capacities), appends to random subsets and removals on a small,
+    fragmenting pool: after every few operations each live request still holds exactly what compressing its
+    current tokens gives, no two live segments overlap, and the pool's counts add up."""
+    mkv = mkv_lib
+    import torch
+    rng = np.random.default_rng(2024)
+    ctx = [int(x) for x in rng.integers(1, 260, size=12)]
+    R = Reqs([c + 130 for c in ctx], seed=79)          # each request's full token supply
+    n_pages, slots = 400, 96
+    pool = _pool(mkv, n_pages=n_pages, page_bytes=20480, slots=slots, max_req=6, appendable=True)
+    live = {}                                           # id -> (request index in R, tokens held)
+    unused = list(range(12))
+    done = {"add": 0, "append": 0, "seal": 0, "remove": 0}
+
+    def check():
+        if not live:
+            return
+        ids = list(live)
+        view = pool.view(ids)
+        n = np.array([live[i][1] for i in ids])
+        rows = [np.arange(R.cu[live[i][0]], R.cu[live[i][0]] + live[i][1]) for i in ids]
+        take = torch.as_tensor(np.concatenate(rows), device="cuda")
+        ii = torch.as_tensor([live[i][0] for i in ids], device="cuda")
+        ref = mkv.mkv_compress(R.K[take].contiguous(), R.V[take].contiguous(), np.concatenate([[0], np.cumsum(n)]),
+                               R.basis[ii].contiguous())
+        g, f = read_store(view, "bf16")["streams"], read_store(ref, "bf16")["streams"]
+        for key in f:
+            assert np.array_equal(g[key].c, f[key].c) and np.array_equal(g[key].mask, f[key].mask), key
+            assert np.array_equal(g[key].vals, f[key].vals), key
+        q = R.q[ii].contiguous()
+        T = np.full(len(ids), 40)
+        o1, s1 = mkv.mkv_decode_attn(view, q, T)
+        o2, s2 = mkv.mkv_decode_attn(ref, q, T)
+        torch.cuda.synchronize()
+        assert torch.equal(s1, s2) and torch.equal(o1, o2)
+        _check_placement(pool, [view])
+        st = pool.stats()
+        assert st.live_requests == len(live)
+        assert st.free_pages + sum(pool.request(i)[1] for i in ids) == n_pages
+        assert st.free_segment_slots + sum((pool.capacity(i) + 63) // 64 for i in ids) == slots
+
+    for step in range(40):
+        op = rng.choice(["add", "append", "append", "remove"]) if live else "add"
+        if op == "add" and unused and len(live) < 6:
+            k = min(int(rng.integers(1, 3)), len(unused), 6 - len(live))
+            picks = [unused.pop(int(rng.integers(len(unused)))) for _ in range(k)]
+            K, V, cu, basis, _, _ = R.pick(picks)
+            cap = [ctx[p] + int(rng.integers(0, 131)) for p in picks]
+            n0 = [min(ctx[p], c) for p, c in zip(picks, cap)]
+            take = torch.as_tensor(np.concatenate([np.arange(R.cu[p], R.cu[p] + a) for p, a in zip(picks, n0)]),
+                                   device="cuda")
+            try:
+                ids = pool.add(R.K[take].contiguous(), R.V[take].contiguous(), np.concatenate([[0], np.cumsum(n0)]),
+                               basis, capacity=cap)
+            except mkv.MkvError as e:   # out of slots or pages: the pool must be unchanged
+                assert e.status == mkv.MKV_E_ARG
+                unused += picks
+                continue
+            for i, p, a in zip(ids, picks, n0):
+                live[int(i)] = (p, a)
+            done["add"] += len(picks)
+        elif op == "append":
+            ids = [i for i in live if live[i][1] < pool.capacity(i) and rng.random() < 0.7]
+            for _ in range(int(rng.integers(1, 40))):
+                ids = [i for i in ids if live[i][1] < pool.capacity(i)]
+                if not ids:
+                    break
+                rows = torch.as_tensor([R.cu[live[i][0]] + live[i][1] for i in ids], device="cuda")
+                try:
+                    pool.append(ids, R.K[rows].contiguous(), R.V[rows].contiguous())
+                except mkv.MkvError as e:   # out of pages for a sealed segment
+                    assert e.status == mkv.MKV_E_ARG and "pages" in str(e)
+                    break
+                for i in ids:
+                    live[i] = (live[i][0], live[i][1] + 1)
+                    done["append"] += 1
+                    done["seal"] += live[i][1] % 64 == 0
+        elif op == "remove" and live:
+            gone = [i for i in live if rng.random() < 0.4] or [next(iter(live))]
+            pool.remove(gone)
+            for i in gone:
+                unused.append(live.pop(i)[0])
+            done["remove"] += len(gone)
+        if step % 5 == 4:
+            check()
+    check()
+    assert min(done.values()) > 0, done
