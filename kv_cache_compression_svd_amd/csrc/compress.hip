@@ -242,10 +242,17 @@ __device__ __forceinline__ uint32_t min8u(uint32_t v) {
     v = min(v, (uint32_t)dpp_i<0x141>((int)v));
     return v;
 }
+// 64-bit values move between lanes as two 32-bit DPP moves (no LDS round trip)
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+    const uint64_t u = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)dpp_i<CTRL>((int)(uint32_t)u), hi = (uint32_t)dpp_i<CTRL>((int)(uint32_t)(u >> 32));
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
 __device__ __forceinline__ double sum8d(double v) {
-    v += __shfl_xor(v, 1, MKV_WAVE);
-    v += __shfl_xor(v, 2, MKV_WAVE);
-    v += __shfl_xor(v, 4, MKV_WAVE);
+    v += dpp_d<0xB1>(v);
+    v += dpp_d<0x4E>(v);
+    v += dpp_d<0x141>(v);
     return v;
 }
 // exclusive prefix over the 8 lanes of a vector (lane order = channel order)
@@ -258,16 +265,56 @@ __device__ __forceinline__ int excl8(int v, int p) {
     }
     return x - v;
 }
-// count of this lane's 16 magnitudes >= cand (0 <= cand <= 0x8000)
-__device__ __forceinline__ int count_ge16(const uint32_t* w, uint32_t cand) {
-    const u16x2 cc = {(unsigned short)cand, (unsigned short)cand};
-    u16x2 acc = {0, 0};
+// This lane's 16 magnitudes (mw: 15-bit patterns, two per word) as 7-bit search keys, four per word with the top
+// bit of every byte set: key = min((m - base) >> sh, 127), and 0 for m < base.
+__device__ __forceinline__ void swar_keys(const uint32_t* mw, uint32_t base, int sh, uint32_t (&kw)[4]) {
+    typedef __attribute__((ext_vector_type(2))) unsigned short u16v2;
+    const u16v2 b2 = {(unsigned short)base, (unsigned short)base};
+    const u16v2 cap = {127, 127};
+    const u16v2 sh2 = {(unsigned short)sh, (unsigned short)sh};
+    uint32_t u[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const u16x2 m = __builtin_bit_cast(u16x2, w[j] & 0x7FFF7FFFu);
-        acc += (m - cc) >> (unsigned short)15;   // 1 where m < cand
+        u16v2 x = __builtin_bit_cast(u16v2, mw[j]);
+        x = __builtin_elementwise_sub_sat(x, b2);
+        x = x >> sh2;
+        x = __builtin_elementwise_min(x, cap);
+        u[j] = __builtin_bit_cast(uint32_t, x);
     }
-    return 16 - (int)(acc.x + acc.y);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kw[j] = __builtin_amdgcn_perm(u[2 * j + 1], u[2 * j], 0x06040200u) | 0x80808080u;
+}
+// Number of this lane's 16 keys >= t (0 <= t <= 127), given tt = t in every byte: per byte, (key | 0x80) - t
+// keeps its top bit iff key >= t, and no byte borrows from its neighbour.
+__device__ __forceinline__ int swar_count_ge(const uint32_t (&kw)[4], uint32_t tt) {
+    int n = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) n += __popc((kw[j] - tt) & 0x80808080u);
+    return n;
+}
+
+// Magnitude pattern of the c-th largest of the vector's 128 values, given lo_end with at least c values >= lo_end
+// and the largest value mx: the largest t with count(m >= t) >= c, found by halving the integer range
+// [lo_end, mx].  The range of L bits is cut into phases of up to 7 bits (the top phase takes what is left over):
+// each phase turns the magnitudes into 7-bit keys relative to the range's low end and searches the key bit by bit,
+// counting four keys per 32-bit word; values above the phase's range saturate at key 127 and still count.
+__device__ __forceinline__ uint32_t vector_threshold8(const uint32_t* mw, uint32_t lo_end, uint32_t mx, int c) {
+    uint32_t base = lo_end;
+    const uint32_t wdt = mx - lo_end;
+    int L = wdt ? 32 - __clz(wdt) : 0;
+    while (L > 0) {
+        const int sh = ((L - 1) / 7) * 7;
+        uint32_t kw[4];
+        swar_keys(mw, base, sh, kw);
+        uint32_t tt = 0;   // the key found so far, in every byte
+        for (int bit = L - sh - 1; bit >= 0; --bit) {
+            const uint32_t cand = tt | (0x01010101u << bit);
+            if (sum8i(swar_count_ge(kw, cand)) >= c) tt = cand;
+        }
+        base += (tt & 0x7Fu) << sh;
+        L = sh;
+    }
+    return base;
 }
 
 // Largest code k the vector admits (keep[k] channels hold >= frac of its energy); thr[k] <- the magnitude of its
@@ -283,12 +330,14 @@ __device__ __forceinline__ int vector_decide8(const uint32_t* w, const CmpArgs& 
                                               int* s_fail) {
     double e = 0.0;
     u16x2 mx2 = {0, 0}, mn2 = {0x7FFF, 0x7FFF};
+    uint32_t mw[8];   // magnitude patterns
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const double lo = bf16_to_f32(w[j] & 0xFFFFu), hi = bf16_to_f32(w[j] >> 16);
+        mw[j] = w[j] & 0x7FFF7FFFu;
+        const double lo = bf16_to_f32(mw[j] & 0xFFFFu), hi = bf16_to_f32(mw[j] >> 16);
         e += lo * lo;
         e += hi * hi;
-        const u16x2 m = __builtin_bit_cast(u16x2, w[j] & 0x7FFF7FFFu);
+        const u16x2 m = __builtin_bit_cast(u16x2, mw[j]);
         mx2 = __builtin_elementwise_max(mx2, m);
         mn2 = __builtin_elementwise_min(mn2, m);
     }
@@ -307,23 +356,17 @@ __device__ __forceinline__ int vector_decide8(const uint32_t* w, const CmpArgs& 
             __syncthreads();
             if (s_fail[k]) break;
         }
-        const uint32_t diff = lo_end ^ mx;
-        uint32_t t = mx;
-        if (diff) {
-            const int hb = 31 - __clz(diff);
-            t = mx & ~((2u << hb) - 1u);
-            for (int bit = hb; bit >= 0; --bit) {
-                const uint32_t cand = t | (1u << bit);
-                if (sum8i(count_ge16(w, cand)) >= c) t = cand;
-            }
-        }
+        const uint32_t t = vector_threshold8(mw, lo_end, mx, c);
+        // kept energy from the magnitudes (squares of bf16 values are exact in fp32), recomputed rather than kept
+        // from the total: holding the 16 float64 values across the search costs registers
         double part = 0.0;
         int gt = 0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const uint32_t lo = w[j] & 0xFFFFu, hi = w[j] >> 16;
-            if ((lo & 0x7FFFu) > t) { const double x = bf16_to_f32(lo); part += x * x; ++gt; }
-            if ((hi & 0x7FFFu) > t) { const double x = bf16_to_f32(hi); part += x * x; ++gt; }
+            const uint32_t lo = mw[j] & 0xFFFFu, hi = mw[j] >> 16;
+            const float xl = bf16_to_f32(lo), xh = bf16_to_f32(hi);
+            if (lo > t) { part += (double)(xl * xl); ++gt; }
+            if (hi > t) { part += (double)(xh * xh); ++gt; }
         }
         const double tv = bf16_to_f32(t);
         const double ec = sum8d(part) + (double)(c - sum8i(gt)) * (tv * tv);
