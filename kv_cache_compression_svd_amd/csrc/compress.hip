@@ -531,6 +531,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     if (tid < 8) s_fail[tid >> 2][tid & 3] = 0;
     uint64_t wg_bytes = 0;                                  // decide: payload bytes of this workgroup
     uint64_t wg_off = PACK ? a.wg_total[blockIdx.x] : 0;    // pack: offset of this workgroup's first segment
+    // pack: the segment code and this thread's vector's thresholds are loaded one segment ahead, so that their
+    // latency overlaps the previous segment
+    int code_n = 0;
+    u32x2 thr_n = {0u, 0u};
+    auto load_meta = [&](int s) {
+        code_n = a.codes[t.seg0 + s];
+        if ((tid >> 3) < min(MKV_SEG, t.n - s * MKV_SEG))
+            thr_n = *reinterpret_cast<const u32x2*>(a.thr + thr_index(a, t, t.tok0 + (int64_t)s * MKV_SEG + (tid >> 3)));
+    };
+    if (PACK && t.s0 < t.s1) load_meta(t.s0);
 
     for (int s = t.s0; s < t.s1; ++s) {
         const int cur = (s - t.s0) & 1;
@@ -541,7 +551,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         // the other parity's flags were last read in the previous segment, before this barrier
         if (tid < 4) s_fail[cur ^ 1][tid] = 0;
         const bool more = s + 1 < t.s1;
-        if (more) load_tile(s + 1);
+        const int code_c = code_n;
+        const u32x2 thr_c = thr_n;
+        if (more) {
+            load_tile(s + 1);
+            if (PACK) load_meta(s + 1);
+        }
         const uint16_t* X = xs[cur];
         if (Bm) {
 #pragma unroll
@@ -586,7 +601,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
                 wg_bytes += (uint64_t)ns * c * (2 + (c < MKV_D ? 1 : 0));
             }
         } else {
-            const int code = a.codes[gs];
+            const int code = code_c;
             const int c = a.keep[code];
             uint8_t* dst = a.payload + (a.preplaced ? a.seg_off[gs] : wg_off);
             if (!a.preplaced && tid == 0) a.seg_off[gs] = wg_off;
@@ -608,7 +623,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
                 }
             } else {
                 if (valid) {
-                    const uint32_t tt = a.thr[thr_index(a, t, tokS + v) + code];
+                    const uint32_t tt = ((code & 2) ? thr_c.y : thr_c.x) >> (16 * (code & 1)) & 0xFFFFu;
                     vector_pack8(w, tt, c, v, p, ns, stg);
                 }
                 __syncthreads();
