@@ -32,7 +32,7 @@ __device__ __forceinline__ uint32_t score_key(float s) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// ---- wave-level reductions (DPP within rows of 16 lanes, permute beyond) -------------------------------
+// ---- wave-level reductions (DPP within rows of 16 lanes, scalar reads or row broadcasts beyond) ---------
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
@@ -47,12 +47,43 @@ __device__ __forceinline__ float sum8(float v) {
 __device__ __forceinline__ float shfl_xor_f(float v, int m) {
     return __shfl_xor(v, m, MKV_WAVE);
 }
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+__device__ __forceinline__ float lane_f(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+// Whole-wave max and sum: DPP inside each row of 16 lanes (every lane of a row ends with the row's result), then
+// the four rows' results read into scalar registers and combined.  Every lane returns the same value.
 __device__ __forceinline__ float wave_max(float v) {
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, MKV_WAVE));
-    return v;
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x141>(v));
+    v = fmaxf(v, dpp_f<0x140>(v));   // row_mirror: lane i <-> 15-i inside each row
+    return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, MKV_WAVE);
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x141>(v);
+    v += dpp_f<0x140>(v);
+    return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+// Inclusive prefix sum over the 64 lanes of a wave: shifts inside each row of 16, then row 0's total is added to
+// row 1 and row 2's to row 3 (row_bcast:15), and rows 0-1's total to rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ uint32_t wave_incl_u32(uint32_t v) {
+    const int r = threadIdx.x & 15;
+    uint32_t y = dpp_u<0x111>(v);
+    if (r >= 1) v += y;
+    y = dpp_u<0x112>(v);
+    if (r >= 2) v += y;
+    y = dpp_u<0x114>(v);
+    if (r >= 4) v += y;
+    y = dpp_u<0x118>(v);
+    if (r >= 8) v += y;
+    v += dpp_u<0x142, 0xA>(v);
+    v += dpp_u<0x143, 0xC>(v);
     return v;
 }
 
@@ -82,11 +113,7 @@ __device__ __forceinline__ int find_slot(const int32_t* base, int n, int b) {
 // `tmp` must hold blockDim.x/64 + 1 words of LDS.  Returns the exclusive prefix; *total gets the sum.
 __device__ __forceinline__ uint32_t block_exscan(uint32_t v, uint32_t* tmp, uint32_t* total) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    uint32_t x = v;
-    for (int d = 1; d < 64; d <<= 1) {
-        uint32_t y = __shfl_up(x, d, MKV_WAVE);
-        if (lane >= d) x += y;
-    }
+    const uint32_t x = wave_incl_u32(v);
     if (lane == 63) tmp[wid] = x;
     __syncthreads();
     if (threadIdx.x == 0) {

@@ -255,14 +255,16 @@ __device__ __forceinline__ double sum8d(double v) {
     v += dpp_d<0x141>(v);
     return v;
 }
-// exclusive prefix over the 8 lanes of a vector (lane order = channel order)
+// exclusive prefix over the 8 lanes of a vector (lane order = channel order): DPP row shifts by 1, 2, 4, each
+// added only where the source lane belongs to the same vector
 __device__ __forceinline__ int excl8(int v, int p) {
     int x = v;
-#pragma unroll
-    for (int d = 1; d < 8; d <<= 1) {
-        const int y = __shfl_up(x, d, MKV_WAVE);
-        if (p >= d) x += y;
-    }
+    int y = dpp_i<0x111>(x);
+    if (p >= 1) x += y;
+    y = dpp_i<0x112>(x);
+    if (p >= 2) x += y;
+    y = dpp_i<0x114>(x);
+    if (p >= 4) x += y;
     return x - v;
 }
 // This lane's 16 magnitudes (mw: 15-bit patterns, two per word) as 7-bit search keys, four per word with the top
@@ -407,8 +409,12 @@ __device__ __forceinline__ void vector_pack8(const uint32_t* w, uint32_t t, int 
 
 // Segment code: minimum over the valid vectors of the tile (8 waves x 8 vectors).
 __device__ __forceinline__ int segment_code8(int best, bool valid, int* s_code) {
+    // best is the same on the 8 lanes of a vector: the two vectors of each row of 16 lanes meet by a row mirror,
+    // the four rows through scalar reads
     int v = valid ? best : 255;
-    for (int m = 32; m >= 1; m >>= 1) v = min(v, __shfl_xor(v, m, MKV_WAVE));
+    v = min(v, dpp_i<0x140>(v));
+    v = min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+            min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
     if ((threadIdx.x & 63) == 0) s_code[threadIdx.x >> 6] = v;
     __syncthreads();
     int code = s_code[0];

@@ -370,15 +370,6 @@ __device__ __forceinline__ KBlock kblock(const DecArgs& a) {
     return k;
 }
 
-// Inclusive prefix over the 64 lanes of a wave.
-__device__ __forceinline__ uint32_t wave_incl(uint32_t v) {
-    const int lane = threadIdx.x & 63;
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t y = __shfl_up(v, d, MKV_WAVE);
-        if (lane >= d) v += y;
-    }
-    return v;
-}
 
 // Bin of the T-th largest key (first wave of the block): the 64-bin coarse histogram (top 6 key bits) gives the
 // coarse bin, its 64 fine bins (top 12 bits) the bin p1.  res <- p1, keys above p1, keys in p1, keys to take in p1.
@@ -392,18 +383,18 @@ __device__ __forceinline__ void find_threshold(const DecArgs& a, int stream, uin
         const uint32_t v = st[kCoarseOff + 64 * min(c, a.hcopies - 1) + 63 - lane];
         cv += c < a.hcopies ? v : 0u;
     }
-    const uint32_t ci = wave_incl(cv), ce = ci - cv;
+    const uint32_t ci = wave_incl_u32(cv), ce = ci - cv;
     const uint64_t cb_bal = __ballot(ce < T && ci >= T);
     const int cl = max(__ffsll((unsigned long long)cb_bal) - 1, 0);
     const int cb = 63 - cl;
-    const uint32_t above = __shfl(ce, cl, MKV_WAVE);
+    const uint32_t above = (uint32_t)__builtin_amdgcn_readlane((int)ce, cl);   // cl is the same on every lane
     uint32_t fv = 0;
 #pragma unroll
     for (int c = 0; c < kMaxHistCopies; ++c) {
         const uint32_t v = a.hist[((size_t)stream * a.hcopies + min(c, a.hcopies - 1)) * kHistBins + cb * 64 + 63 - lane];
         fv += c < a.hcopies ? v : 0u;
     }
-    const uint32_t fi = wave_incl(fv) + above, fe = fi - fv;
+    const uint32_t fi = wave_incl_u32(fv) + above, fe = fi - fv;
     if (fe < T && fi >= T) {
         res[0] = (uint32_t)(cb * 64 + 63 - lane);
         res[1] = fe;
@@ -960,14 +951,14 @@ __global__ __launch_bounds__(256) void k_combine(DecArgs a) {
                         v[u] = *reinterpret_cast<const float2*>(a.part + ((size_t)(first + c0 + k + u) * G + h) * PW + 2 + 2 * lane);
 #pragma unroll
                     for (int u = 0; u < 8; ++u) {
-                        const float fk = __shfl(f, k + u, MKV_WAVE);
+                        const float fk = lane_f(f, k + u);
                         O0 = fmaf(fk, v[u].x, O0);
                         O1 = fmaf(fk, v[u].y, O1);
                     }
                 }
                 for (; k < cnt; ++k) {
                     const float2 v = *reinterpret_cast<const float2*>(a.part + ((size_t)(first + c0 + k) * G + h) * PW + 2 + 2 * lane);
-                    const float fk = __shfl(f, k, MKV_WAVE);
+                    const float fk = lane_f(f, k);
                     O0 = fmaf(fk, v.x, O0);
                     O1 = fmaf(fk, v.y, O1);
                 }
