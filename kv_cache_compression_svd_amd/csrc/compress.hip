@@ -60,20 +60,10 @@ __device__ __forceinline__ size_t thr_index(const CmpArgs& a, const Tile& t, int
     return ((((size_t)t.X * a.total_tokens + tok) * a.Hkv + t.h) << 2);
 }
 
-// ---- magnitude counting helpers -----------------------------------------------------------------------
-// Number of the 32 bf16 magnitudes (15-bit patterns, two per word) that are >= cand (0 <= cand <= 0x8000).
-__device__ __forceinline__ int count_ge_bf16(const uint32_t* w, uint32_t cand) {
-    const u16x2 cc = {(unsigned short)cand, (unsigned short)cand};
-    u16x2 acc = {0, 0};
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const u16x2 m = __builtin_bit_cast(u16x2, w[j] & 0x7FFF7FFFu);
-        const u16x2 d = m - cc;          // bit 15 set exactly when m < cand
-        acc += d >> (unsigned short)15;
-    }
-    return 32 - (int)(acc.x + acc.y);
-}
-
+// =====================================================================================================
+// fp32 path: 4 lanes per vector, each owning 32 channels
+// =====================================================================================================
+// Number of this lane's 32 float32 magnitudes that are >= cand.
 __device__ __forceinline__ int count_ge_f32(const uint32_t* w, uint32_t cand) {
     int c = 0;
 #pragma unroll
@@ -107,56 +97,30 @@ __device__ __forceinline__ uint32_t lowest_bits(uint32_t m, int k) {
     return r;
 }
 
-// Value of a magnitude pattern.
-__device__ __forceinline__ double mag_value(uint32_t t, bool bf16) {
-    return bf16 ? (double)bf16_to_f32(t) : (double)__uint_as_float(t);
-}
-
-// ---- per-vector decision: 4 lanes own 32 channels each of one vector ----------------------------------
-// Returns the largest code k (smallest count keep[k]) the vector admits; thr[k] gets keep[k]'s threshold.
-template <bool BF16>
-__device__ __forceinline__ int vector_decide(const uint32_t* w, const CmpArgs& a, uint32_t* thr) {
+// Largest code k (smallest count keep[k]) the vector admits; thr[k] gets the magnitude pattern of its keep[k]-th
+// largest value, found bit by bit over the 31-bit float32 magnitude.
+__device__ __forceinline__ int vector_decide_f32(const uint32_t* w, const CmpArgs& a, uint32_t* thr) {
     double e = 0.0;
-    if (BF16) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const double lo = bf16_to_f32(w[j] & 0xFFFFu), hi = bf16_to_f32(w[j] >> 16);
-            e += lo * lo;
-            e += hi * hi;
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 32; ++j) { const double x = __uint_as_float(w[j]); e += x * x; }
-    }
+    for (int j = 0; j < 32; ++j) { const double x = __uint_as_float(w[j]); e += x * x; }
     const double e_all = sum4d(e);
     const double bound = __dmul_rn(a.frac, e_all);
     int best = 0;
     for (int k = 1; k < a.n_keep; ++k) {
         const int c = a.keep[k];
         uint32_t t = 0;
-        const int top = BF16 ? 14 : 30;
-        for (int bit = top; bit >= 0; --bit) {
+        for (int bit = 30; bit >= 0; --bit) {
             const uint32_t cand = t | (1u << bit);
-            const int ge = sum4i(BF16 ? count_ge_bf16(w, cand) : count_ge_f32(w, cand));
-            if (ge >= c) t = cand;
+            if (sum4i(count_ge_f32(w, cand)) >= c) t = cand;
         }
         // energy of the c largest: everything strictly above t, plus (c - gt) copies of t
         double part = 0.0;
         int gt = 0;
-        if (BF16) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const uint32_t lo = w[j] & 0xFFFFu, hi = w[j] >> 16;
-                if ((lo & 0x7FFFu) > t) { const double x = bf16_to_f32(lo); part += x * x; ++gt; }
-                if ((hi & 0x7FFFu) > t) { const double x = bf16_to_f32(hi); part += x * x; ++gt; }
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < 32; ++j) {
-                if ((w[j] & 0x7FFFFFFFu) > t) { const double x = __uint_as_float(w[j]); part += x * x; ++gt; }
-            }
+        for (int j = 0; j < 32; ++j) {
+            if ((w[j] & 0x7FFFFFFFu) > t) { const double x = __uint_as_float(w[j]); part += x * x; ++gt; }
         }
-        const double tv = mag_value(t, BF16);
+        const double tv = (double)__uint_as_float(t);
         const double ec = sum4d(part) + (double)(c - sum4i(gt)) * (tv * tv);
         thr[k] = t;
         if (ec >= bound) best = k;
@@ -164,44 +128,27 @@ __device__ __forceinline__ int vector_decide(const uint32_t* w, const CmpArgs& a
     return best;
 }
 
-// ---- pack one vector's kept channels into the staging block -------------------------------------------
-template <bool BF16>
-__device__ __forceinline__ void vector_pack(const uint32_t* w, uint32_t t, int c, int v, int p, int ns,
-                                            uint8_t* stg) {
+// This lane's kept channels of one vector into the staging block (values [ns][c] then indices [ns][c]); among
+// values equal to the threshold the lower channels are kept.
+__device__ __forceinline__ void vector_pack_f32(const uint32_t* w, uint32_t t, int c, int v, int p, int ns,
+                                                uint8_t* stg) {
     uint32_t gtm = 0, eqm = 0;
-    if (BF16) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const uint32_t lo = w[j] & 0x7FFFu, hi = (w[j] >> 16) & 0x7FFFu;
-            gtm |= (lo > t ? 1u : 0u) << (2 * j);
-            gtm |= (hi > t ? 1u : 0u) << (2 * j + 1);
-            eqm |= (lo == t ? 1u : 0u) << (2 * j);
-            eqm |= (hi == t ? 1u : 0u) << (2 * j + 1);
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < 32; ++j) {
-            const uint32_t m = w[j] & 0x7FFFFFFFu;
-            gtm |= (m > t ? 1u : 0u) << j;
-            eqm |= (m == t ? 1u : 0u) << j;
-        }
+    for (int j = 0; j < 32; ++j) {
+        const uint32_t m = w[j] & 0x7FFFFFFFu;
+        gtm |= (m > t ? 1u : 0u) << j;
+        eqm |= (m == t ? 1u : 0u) << j;
     }
     const int need = c - sum4i(__popc(gtm));
     const int eqc = __popc(eqm);
     const int take = min(max(need - excl4(eqc, p), 0), eqc);
     const uint32_t keepm = gtm | lowest_bits(eqm, take);
     int pos = excl4(__popc(keepm), p);
-    const int bv = BF16 ? 2 : 4;
-    uint8_t* vals = stg + (size_t)v * c * bv;
-    uint8_t* idx = stg + (size_t)ns * c * bv + (size_t)v * c;
+    uint8_t* vals = stg + (size_t)v * c * 4;
+    uint8_t* idx = stg + (size_t)ns * c * 4 + (size_t)v * c;
     for (int j = 0; j < 32; ++j) {
         if (!((keepm >> j) & 1u)) continue;
-        if (BF16) {
-            const uint32_t u = (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xFFFFu);
-            reinterpret_cast<uint16_t*>(vals)[pos] = (uint16_t)u;
-        } else {
-            reinterpret_cast<uint32_t*>(vals)[pos] = w[j];
-        }
+        reinterpret_cast<uint32_t*>(vals)[pos] = w[j];
         idx[pos] = (uint8_t)(32 * p + j);
         ++pos;
     }
@@ -336,7 +283,7 @@ __device__ __forceinline__ int vector_decide8(const uint32_t* w, const CmpArgs& 
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         mw[j] = w[j] & 0x7FFF7FFFu;
-        const double lo = bf16_to_f32(mw[j] & 0xFFFFu), hi = bf16_to_f32(mw[j] >> 16);
+        const double lo = bf16_to_f32(w[j] & 0xFFFFu), hi = bf16_to_f32(w[j] >> 16);
         e += lo * lo;
         e += hi * hi;
         const u16x2 m = __builtin_bit_cast(u16x2, mw[j]);
@@ -359,16 +306,17 @@ __device__ __forceinline__ int vector_decide8(const uint32_t* w, const CmpArgs& 
             if (s_fail[k]) break;
         }
         const uint32_t t = vector_threshold8(mw, lo_end, mx, c);
-        // kept energy from the magnitudes (squares of bf16 values are exact in fp32), recomputed rather than kept
-        // from the total: holding the 16 float64 values across the search costs registers
+        // kept energy from the magnitudes, squared in float64 (exact for every bf16 value, subnormals and values
+        // beyond 2^64 included); recomputed from the magnitude words rather than kept from the total (the signed
+        // words): holding the 16 float64 values across the search costs registers
         double part = 0.0;
         int gt = 0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const uint32_t lo = mw[j] & 0xFFFFu, hi = mw[j] >> 16;
-            const float xl = bf16_to_f32(lo), xh = bf16_to_f32(hi);
-            if (lo > t) { part += (double)(xl * xl); ++gt; }
-            if (hi > t) { part += (double)(xh * xh); ++gt; }
+            const double xl = bf16_to_f32(lo), xh = bf16_to_f32(hi);
+            if (lo > t) { part += xl * xl; ++gt; }
+            if (hi > t) { part += xh * xh; ++gt; }
         }
         const double tv = bf16_to_f32(t);
         const double ec = sum8d(part) + (double)(c - sum8i(gt)) * (tv * tv);
@@ -806,7 +754,7 @@ __global__ __launch_bounds__(256) void k_cmp_f32(CmpArgs a) {
         __syncthreads();   // xs is reused as staging below
         if (!PACK) {
             uint32_t thr[4] = {0, 0, 0, 0};
-            const int best = vector_decide<false>(w, a, thr);
+            const int best = vector_decide_f32(w, a, thr);
             const int code = segment_code(best, valid, s_code);
             // an fp32 magnitude threshold takes two of the vector's four 16-bit scratch slots, so fp32 stores
             // support at most two kept counts below 128
@@ -838,7 +786,7 @@ __global__ __launch_bounds__(256) void k_cmp_f32(CmpArgs a) {
                 if (valid) {
                     const uint16_t* tp = a.thr + thr_index(a, t, tokS + v);
                     const uint32_t tt = (uint32_t)tp[2 * (code - 1)] | ((uint32_t)tp[2 * (code - 1) + 1] << 16);
-                    vector_pack<false>(w, tt, c, v, p, ns, stg);
+                    vector_pack_f32(w, tt, c, v, p, ns, stg);
                 }
                 __syncthreads();
                 const int nq = ns * c * 5 / 16;

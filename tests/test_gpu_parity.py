@@ -275,3 +275,92 @@ def test_long_stream_spans_several_bitmap_tiles(mkv):
     ref = oracle.compress_all(inp)
     store, q = _compress_gpu(mkv, inp)
     _decode_compare(mkv, inp, store, q, ref)
+
+
+# ---- constructed vectors for the per-vector threshold search ------------------------------------------------
+SEGMENT_KINDS = ["wide", "wide_sparse", "ties", "flat", "zero_mix", "threshold", "denormal", "near_two", "normal",
+                 "big_flat", "tiny_sparse"]
+
+
+def _crafted_segment(rng, kind: str, rows: int) -> np.ndarray:
+    """float64 [rows][128] vectors of one kind, exactly representable in bf16 except where rounding is intended."""
+    sign = rng.choice([-1.0, 1.0], size=(rows, 128))
+    if kind == "wide":          # magnitudes 2^-120 .. 2^100 with 7 random mantissa bits
+        x = sign * np.ldexp(1.0 + rng.integers(0, 128, (rows, 128)) / 128.0, rng.integers(-120, 101, (rows, 128)))
+    elif kind == "wide_sparse":  # at most 24 non-zeros spanning 2^-120 .. 2^100: every vector admits 32 channels
+        x = np.zeros((rows, 128))
+        for i in range(rows):
+            ch = rng.choice(128, int(rng.integers(1, 25)), replace=False)
+            x[i, ch] = sign[i, ch] * np.ldexp(1.0 + rng.integers(0, 128, ch.size) / 128.0,
+                                              rng.integers(-120, 101, ch.size))
+    elif kind == "ties":        # three magnitudes only: long runs of equal values at every threshold
+        x = sign * rng.choice([1.0, 0.5, 0.25], size=(rows, 128), p=[0.2, 0.5, 0.3])
+    elif kind == "flat":        # top-64 energy exactly half: only the full vector is admissible
+        x = sign.copy()
+    elif kind == "zero_mix":    # all-zero vectors (admit every count) between ordinary ones
+        x = rng.standard_normal((rows, 128))
+        x[::2] = 0.0
+    elif kind == "threshold":   # 32 channels of 3, 32 of 1, 64 of 0: E_32 = 288 = 0.9 * 320 exactly
+        x = np.zeros((rows, 128))
+        for i in range(rows):
+            perm = rng.permutation(128)
+            x[i, perm[:32]] = 3.0 * sign[i, perm[:32]]
+            x[i, perm[32:64]] = sign[i, perm[32:64]]
+    elif kind == "denormal":    # bf16 subnormals (below 2^-126) next to small normal values
+        x = sign * np.where(rng.random((rows, 128)) < 0.5, np.ldexp(rng.integers(1, 128, (rows, 128)), -133),
+                            np.ldexp(1.0 + rng.integers(0, 128, (rows, 128)) / 128.0, -120))
+    elif kind == "near_two":    # magnitudes across 2.0, where the top bit of the magnitude pattern flips
+        x = sign * rng.uniform(1.9, 2.1, (rows, 128))
+    elif kind == "big_flat":    # flat at 2^70: squares beyond the float32 range, only the full vector admissible
+        x = sign * 2.0 ** 70
+    elif kind == "tiny_sparse":  # at most 24 non-zeros near 2^-100: squares below the float32 range, admits 32
+        x = np.zeros((rows, 128))
+        for i in range(rows):
+            ch = rng.choice(128, int(rng.integers(1, 25)), replace=False)
+            x[i, ch] = sign[i, ch] * np.ldexp(1.0 + rng.integers(0, 128, ch.size) / 128.0, -100)
+    else:
+        x = rng.standard_normal((rows, 128)) * (np.arange(128) + 1.0) ** -0.5
+    return x
+
+
+def test_compress_constructed_vectors_bit_exact(mkv):
+    """Pre-rotated (basis NULL) bf16 stores of constructed vectors: wide dynamic range (threshold searches over
+    the full 15-bit magnitude range), long ties, flat, zero, exactly-at-threshold, subnormal and 2.0-straddling
+    vectors, and vectors whose squares leave the float32 range (the energy rule is float64); codes, channel
+    sets and values must equal the oracle's bit for bit."""
+    rng = np.random.default_rng(77)
+    ctx = (11 * 64 + 17, 200)
+    wl = W.Workload("crafted", 2, 4, 2, ctx, "bf16", (64, 64), "single", 77)
+    tot = sum(ctx)
+    K = np.zeros((tot, 2, 128), np.uint16)
+    V = np.zeros((tot, 2, 128), np.uint16)
+    cu = np.array([0, ctx[0], tot], np.int64)
+    kind_at = 0
+    for r in range(2):
+        for h in range(2):
+            for arr in (K, V):
+                for s0 in range(0, ctx[r], 64):
+                    rows = min(64, ctx[r] - s0)
+                    x = _crafted_segment(rng, SEGMENT_KINDS[kind_at % len(SEGMENT_KINDS)], rows)
+                    kind_at += 1
+                    arr[cu[r] + s0:cu[r] + s0 + rows, h, :] = W.f32_to_bf16_bits(x.astype(np.float32))
+    q = W.f32_to_bf16_bits(rng.standard_normal((2, 4, 128)).astype(np.float32))
+    inp = W.Inputs(wl, K, V, q, None, cu, np.array([64, 64], np.int32))
+    ref = oracle.compress_all(inp)
+    # the data reaches the cases it is meant for: a 32-channel segment whose vectors span more than 2^14
+    # magnitude patterns, segments at every count, and subnormal stored values
+    codes = np.concatenate([s.c for s in ref.values()])
+    assert set(np.unique(codes).tolist()) == {128, 64, 32}
+    wide32 = False
+    for (r, h, X), s in ref.items():
+        arr = K if X == 0 else V
+        m = arr[cu[r]:cu[r + 1], h, :] & 0x7FFF
+        for si, c in enumerate(s.c):
+            seg = m[64 * si:64 * si + 64].astype(np.int64)
+            wide32 |= bool(c == 32 and np.any(seg.max(1) - seg.min(1) >= (1 << 14)))
+    assert wide32
+    assert np.any(((K & 0x7F80) == 0) & ((K & 0x7F) != 0))
+    store, _ = _compress_gpu(mkv, inp)
+    got = read_store(store, inp.dtype)
+    _assert_streams_equal(got["streams"], ref)
+    assert got["total"] == _closed_form_bytes(ref, inp.dtype) == store.payload_bytes()
