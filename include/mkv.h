@@ -23,6 +23,8 @@
  *     call returns MKV_E_ARG or MKV_E_UNSUPPORTED and mkv_last_error() says why.  A failed launch returns
  *     MKV_E_DEVICE.  No C++ exception crosses this boundary.
  *   - Preconditions not checked: finite inputs (NaN/Inf give unspecified results) and an orthonormal basis.
+ *     The rotation and the decode arithmetic run in float32 (the segment energy rule in float64, exact for
+ *     every bf16 value): rotated values, scores and logits must stay inside the float32 range.
  */
 #ifndef MKV_H
 #define MKV_H
