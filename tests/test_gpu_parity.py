@@ -202,6 +202,24 @@ def test_edge_cases(mkv, label, wl, basis):
         _decode_compare(mkv, inp, store2, q, ref)
 
 
+def test_many_requests(mkv):
+    """130 requests of 0..300 tokens (some empty, most with a ragged last segment) and per-request budgets: the
+    per-request tables outgrow the words a kernel launch carries (448), so both calls upload them in several
+    launches.  Whole compression bit-exact (signed-permutation basis) and decode against the oracle."""
+    rng = np.random.default_rng(31)
+    ctx = [int(x) for x in rng.integers(0, 301, 130)]
+    ctx[5] = 0
+    T = [max(1, int(x)) for x in rng.integers(1, 80, 130)]
+    wl = _custom(ctx, T, Hq=4, Hkv=2, seed=31)
+    inp = W.generate(wl, basis="sperm")
+    ref = oracle.compress_all(inp)
+    store, q = _compress_gpu(mkv, inp)
+    got = read_store(store, inp.dtype)
+    _assert_streams_equal(got["streams"], ref)
+    assert got["total"] == _closed_form_bytes(ref, inp.dtype) == store.payload_bytes()
+    _decode_compare(mkv, inp, store, q, ref)
+
+
 @pytest.mark.parametrize("keep", [(128,), (128, 64), (128, 64, 32, 16)])
 def test_other_strategy_sets(mkv, keep):
     wl = _custom([400, 77], [64, 20])
