@@ -267,8 +267,8 @@ __device__ __forceinline__ uint32_t vector_threshold8(const uint32_t* mw, uint32
 }
 
 // Largest code k the vector admits (keep[k] channels hold >= frac of its energy); thr[k] <- the magnitude of its
-// keep[k]-th largest value.  Thresholds are searched bit by bit, only over the bits where the lower end of the
-// range and the vector's largest magnitude differ; smaller counts are searched above the previous threshold.
+// keep[k]-th largest value.  Thresholds come from vector_threshold8 over the range [smallest magnitude, largest]
+// for the first count; smaller counts are searched above the previous threshold.
 // Called by every thread of the workgroup (64 vectors of one segment): before searching level k >= 2 the
 // workgroup checks whether some valid vector already cannot reach it, either because it failed level k-1 or
 // because the top keep[k] energy is bounded by E_{k-1} - (keep[k-1] - keep[k]) * t_{k-1}^2 (each of the dropped
