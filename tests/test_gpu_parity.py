@@ -295,6 +295,19 @@ def test_long_stream_spans_several_bitmap_tiles(mkv):
     _decode_compare(mkv, inp, store, q, ref)
 
 
+@pytest.mark.parametrize("frac", ["all", "all_but_one", "half"])
+def test_large_budgets_across_bitmap_tiles(mkv, frac):
+    """Budgets of every token, all but one, and half of a 70000-token stream (three emit tiles): the selection
+    takes whole tiles, leaves a single token out, or cuts in the middle of the candidates."""
+    n = 70_000
+    T = {"all": n, "all_but_one": n - 1, "half": n // 2}[frac]
+    wl = _custom([n, 300], [T, 299], Hq=4, Hkv=1, seed=13)
+    inp = W.generate(wl, basis="sperm")
+    ref = oracle.compress_all(inp)
+    store, q = _compress_gpu(mkv, inp)
+    _decode_compare(mkv, inp, store, q, ref)
+
+
 # ---- constructed vectors for the per-vector threshold search ------------------------------------------------
 SEGMENT_KINDS = ["wide", "wide_sparse", "ties", "flat", "zero_mix", "threshold", "denormal", "near_two", "normal",
                  "big_flat", "tiny_sparse"]
