@@ -69,6 +69,18 @@ def test_compress_p1_prerotated_bit_exact(mkv, name, div):
     assert got["total"] == _closed_form_bytes(ref, inp.dtype) == st.payload_bytes()
 
 
+@pytest.mark.parametrize("name,div", [("llama_layer", 32), ("ragged16", 64)], ids=["llama_layer/32", "ragged16/64"])
+def test_decode_without_basis(mkv, name, div):
+    """A store compressed with basis = NULL: decode takes q as already rotated and returns o' unrotated; against
+    the oracle run without a basis."""
+    inp = W.generate(_wl(name, div), basis="svd")
+    pre = prerotated_inputs(inp, oracle.compress_all(inp))
+    ref = oracle.compress_all(pre)
+    store, q = _compress_gpu(mkv, pre)
+    _assert_streams_equal(read_store(store, pre.dtype)["streams"], ref)
+    _decode_compare(mkv, pre, store, q, ref)
+
+
 @pytest.mark.parametrize("name,div", CASES, ids=IDS)
 def test_compress_p2_signed_permutation_bit_exact(mkv, name, div):
     inp = W.generate(_wl(name, div), basis="sperm")
