@@ -366,17 +366,19 @@ def _crafted_segment(rng, kind: str, rows: int) -> np.ndarray:
     return x
 
 
-def test_compress_constructed_vectors_bit_exact(mkv):
-    """Pre-rotated (basis NULL) bf16 stores of constructed vectors: wide dynamic range (threshold searches over
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_compress_constructed_vectors_bit_exact(mkv, dtype):
+    """Pre-rotated (basis NULL) stores of constructed vectors: wide dynamic range (bf16: threshold searches over
     the full 15-bit magnitude range), long ties, flat, zero, exactly-at-threshold, subnormal and 2.0-straddling
     vectors, and vectors whose squares leave the float32 range (the energy rule is float64); codes, channel
     sets and values must equal the oracle's bit for bit."""
     rng = np.random.default_rng(77)
     ctx = (11 * 64 + 17, 200)
-    wl = W.Workload("crafted", 2, 4, 2, ctx, "bf16", (64, 64), "single", 77)
+    wl = W.Workload("crafted", 2, 4, 2, ctx, dtype, (64, 64), "single", 77)
     tot = sum(ctx)
-    K = np.zeros((tot, 2, 128), np.uint16)
-    V = np.zeros((tot, 2, 128), np.uint16)
+    store_t = np.uint16 if dtype == "bf16" else np.float32
+    K = np.zeros((tot, 2, 128), store_t)
+    V = np.zeros((tot, 2, 128), store_t)
     cu = np.array([0, ctx[0], tot], np.int64)
     kind_at = 0
     for r in range(2):
@@ -384,25 +386,30 @@ def test_compress_constructed_vectors_bit_exact(mkv):
             for arr in (K, V):
                 for s0 in range(0, ctx[r], 64):
                     rows = min(64, ctx[r] - s0)
-                    x = _crafted_segment(rng, SEGMENT_KINDS[kind_at % len(SEGMENT_KINDS)], rows)
+                    x = _crafted_segment(rng, SEGMENT_KINDS[kind_at % len(SEGMENT_KINDS)], rows).astype(np.float32)
                     kind_at += 1
-                    arr[cu[r] + s0:cu[r] + s0 + rows, h, :] = W.f32_to_bf16_bits(x.astype(np.float32))
-    q = W.f32_to_bf16_bits(rng.standard_normal((2, 4, 128)).astype(np.float32))
+                    arr[cu[r] + s0:cu[r] + s0 + rows, h, :] = W.f32_to_bf16_bits(x) if dtype == "bf16" else x
+    q = rng.standard_normal((2, 4, 128)).astype(np.float32)
+    q = W.f32_to_bf16_bits(q) if dtype == "bf16" else q
     inp = W.Inputs(wl, K, V, q, None, cu, np.array([64, 64], np.int32))
     ref = oracle.compress_all(inp)
-    # the data reaches the cases it is meant for: a 32-channel segment whose vectors span more than 2^14
-    # magnitude patterns, segments at every count, and subnormal stored values
+    # the data reaches the cases it is meant for: every count, subnormal stored values and, for bf16, a
+    # 32-channel segment whose vectors span more than 2^14 magnitude patterns
     codes = np.concatenate([s.c for s in ref.values()])
     assert set(np.unique(codes).tolist()) == {128, 64, 32}
-    wide32 = False
-    for (r, h, X), s in ref.items():
-        arr = K if X == 0 else V
-        m = arr[cu[r]:cu[r + 1], h, :] & 0x7FFF
-        for si, c in enumerate(s.c):
-            seg = m[64 * si:64 * si + 64].astype(np.int64)
-            wide32 |= bool(c == 32 and np.any(seg.max(1) - seg.min(1) >= (1 << 14)))
-    assert wide32
-    assert np.any(((K & 0x7F80) == 0) & ((K & 0x7F) != 0))
+    if dtype == "bf16":
+        wide32 = False
+        for (r, h, X), s in ref.items():
+            arr = K if X == 0 else V
+            m = arr[cu[r]:cu[r + 1], h, :] & 0x7FFF
+            for si, c in enumerate(s.c):
+                seg = m[64 * si:64 * si + 64].astype(np.int64)
+                wide32 |= bool(c == 32 and np.any(seg.max(1) - seg.min(1) >= (1 << 14)))
+        assert wide32
+        assert np.any(((K & 0x7F80) == 0) & ((K & 0x7F) != 0))
+    else:
+        u = K.view(np.uint32)
+        assert np.any(((u & 0x7F800000) == 0) & ((u & 0x7FFFFF) != 0))
     store, _ = _compress_gpu(mkv, inp)
     got = read_store(store, inp.dtype)
     _assert_streams_equal(got["streams"], ref)
