@@ -114,7 +114,9 @@ mkv_status mkv_compress(const mkv_kv_desc* kv, const float* basis, const mkv_seg
  * segment by the segment rule over its tokens so far (same rotation, selection and packing as mkv_compress),
  * and the append that completes a segment (64 tokens) seals it into the payload.  After any sequence of
  * appends, every segment holds exactly what mkv_compress would build from the extended contexts: the same
- * code, channels and values; only payload offsets differ.  bf16 only (MKV_E_UNSUPPORTED otherwise).
+ * code, channels and values; only payload offsets differ.  The payload has room for the capacities at all 128
+ * channels plus, per stream, the first compression's copy of its unfinished segment, which appends leave unused.
+ * bf16 only (MKV_E_UNSUPPORTED otherwise).
  * mkv_compress_growable is mkv_compress with capacities; the sizes come from mkv_compress_bytes_growable. */
 mkv_status mkv_compress_bytes_growable(const mkv_kv_desc* kv, const mkv_seg_policy* policy, const int64_t* capacity,
                                        size_t* store_bytes, size_t* scratch_bytes);

@@ -202,6 +202,12 @@ StoreLayout store_layout(const Shape& sh) {
     L.basis = align_up(L.seg_off + 16 * (uint64_t)sh.S);
     L.payload = align_up(L.basis + (uint64_t)sh.B * sh.Hkv * 2 * MKV_HEAD_DIM * MKV_HEAD_DIM * sizeof(float));
     L.capacity = 2ull * sh.Hkv * (uint64_t)sh.total_cap * MKV_HEAD_DIM * dtype_bytes(sh.dtype);
+    // growable stores: the first compression packs each stream's unfinished last segment into the payload like
+    // any other; the appends that extend it re-pack it into the stream's open area and seal it at the payload's
+    // end, so that first copy stays behind unused.  Room for one such segment (at most 63 rows, all channels)
+    // per stream keeps every seal inside the payload.
+    if (sh.growable)
+        L.capacity += 2ull * sh.B * sh.Hkv * (uint64_t)(MKV_SEG_LEN - 1) * MKV_HEAD_DIM * dtype_bytes(sh.dtype);
     // an open segment holds at most 64 rows, packed or raw: 64 * 128 values
     L.open_bytes = sh.growable ? (uint64_t)MKV_SEG_LEN * MKV_HEAD_DIM * dtype_bytes(sh.dtype) : 0;
     const uint64_t streams = 2ull * sh.B * sh.Hkv;

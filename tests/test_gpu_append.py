@@ -50,7 +50,9 @@ def _compare(mkv, inp, st, n, q, basis):
     B = inp.workload.batch
     take = np.concatenate([np.arange(cu[r], cu[r] + n[r]) for r in range(B)])
     ref = mkv.mkv_compress(K[take].contiguous(), V[take].contiguous(), np.concatenate([[0], np.cumsum(n)]), basis)
-    g, f = read_store(st, "bf16")["streams"], read_store(ref, "bf16")["streams"]
+    raw = read_store(st, "bf16")
+    assert raw["total"] <= int(st.view().payload_capacity)   # seals never run into the open-segment areas
+    g, f = raw["streams"], read_store(ref, "bf16")["streams"]
     for key in f:
         assert np.array_equal(g[key].c, f[key].c), key
         assert np.array_equal(g[key].mask, f[key].mask), key
@@ -119,3 +121,39 @@ def mkv_lib():
     import kv_cache_compression_svd_amd as m
     m.lib()
     return m
+
+
+def test_appends_of_constructed_vectors_match_the_oracle(mkv_lib):
+    """Appends (no basis, bf16) of the parity tests' constructed vectors (full-range magnitudes, ties, flat,
+    zero, exact-threshold, subnormal, out-of-float32-range squares): the grown store equals the oracle's
+    compression of the extended context bit for bit."""
+    mkv = mkv_lib
+    from test_gpu_parity import SEGMENT_KINDS, _crafted_segment
+    rng = np.random.default_rng(79)
+    ctx = (3 * 64 + 20, 64 + 5)
+    tot = sum(ctx)
+    wl = W.Workload("append_crafted", 2, 8, 2, ctx, "bf16", (50, 50), "per_request", 79, "append case")
+    K = np.zeros((tot, 2, 128), np.uint16)
+    V = np.zeros((tot, 2, 128), np.uint16)
+    kind_at = 0
+    for arr in (K, V):
+        for h in range(2):
+            for t0 in range(0, tot, 16):
+                rows = min(16, tot - t0)
+                x = _crafted_segment(rng, SEGMENT_KINDS[kind_at % len(SEGMENT_KINDS)], rows)
+                kind_at += 1
+                arr[t0:t0 + rows, h, :] = W.f32_to_bf16_bits(x.astype(np.float32))
+    q = W.f32_to_bf16_bits(rng.standard_normal((2, 8, 128)).astype(np.float32))
+    cu = np.array([0, ctx[0], tot], np.int64)
+    inp = W.Inputs(wl, K, V, q, None, cu, np.array([50, 50], np.int32))
+    st, n, _ = _grow(mkv, inp, (100, 10), 120, None)
+    assert list(n) == list(ctx)
+    ref = oracle.compress_all(inp)
+    raw = read_store(st, "bf16")
+    # every segment keeps all 128 channels here: the sealed segments fill the payload to its capacity
+    assert raw["total"] <= int(st.view().payload_capacity)
+    got = raw["streams"]
+    for key, r in ref.items():
+        assert np.array_equal(got[key].c, r.c), key
+        assert np.array_equal(got[key].mask, r.mask), key
+        assert np.array_equal(got[key].vals, r.vals), key

@@ -417,3 +417,42 @@ def test_random_pool_lifecycle(mkv_lib):
             check()
     check()
     assert min(done.values()) > 0, done
+
+
+def test_pool_appends_of_constructed_vectors_match_the_oracle(mkv_lib):
+    """Appendable pool without bases, grown by appends of the parity tests' constructed vectors (full-range
+    magnitudes, ties, flat, zero, exact-threshold, subnormal, out-of-float32-range squares; many segments keep
+    all 128 channels, so sealed segments take their full reserved size): every segment of the view equals the
+    oracle's compression of the extended contexts bit for bit."""
+    import torch
+    from _helpers import storage_to_torch
+    from test_gpu_parity import SEGMENT_KINDS, _crafted_segment
+    mkv = mkv_lib
+    rng = np.random.default_rng(81)
+    ctx = [2 * 64 + 30, 64 + 3, 40]
+    n0 = [70, 10, 0]
+    tot = sum(ctx)
+    K = np.zeros((tot, 4, 128), np.uint16)
+    V = np.zeros((tot, 4, 128), np.uint16)
+    kind_at = 0
+    for arr in (K, V):
+        for h in range(4):
+            for t0 in range(0, tot, 16):
+                rows = min(16, tot - t0)
+                x = _crafted_segment(rng, SEGMENT_KINDS[kind_at % len(SEGMENT_KINDS)], rows)
+                kind_at += 1
+                arr[t0:t0 + rows, h, :] = W.f32_to_bf16_bits(x.astype(np.float32))
+    cu = np.concatenate([[0], np.cumsum(ctx)]).astype(np.int64)
+    R = Reqs.__new__(Reqs)
+    R.inp = W.Inputs(_wl(tuple(ctx), 81), K, V, None, None, cu, np.full(len(ctx), 40, np.int32))
+    R.K, R.V = storage_to_torch(K, "bf16", "cuda"), storage_to_torch(V, "bf16", "cuda")
+    R.basis, R.cu, R.dtype, R.torch = None, cu, "bf16", torch
+    pool = _pool(mkv, n_pages=64, page_bytes=40960, slots=32, has_basis=False, appendable=True)
+    ids, n = _grow_in_pool(mkv, R, n0, max(ctx), pool)
+    assert list(n) == ctx
+    ref = oracle.compress_all(R.inp)
+    got = read_store(pool.view(ids), "bf16")["streams"]
+    for key, r in ref.items():
+        assert np.array_equal(got[key].c, r.c), key
+        assert np.array_equal(got[key].mask, r.mask), key
+        assert np.array_equal(got[key].vals, r.vals), key
