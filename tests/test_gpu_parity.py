@@ -232,10 +232,16 @@ def test_many_requests(mkv):
     _decode_compare(mkv, inp, store, q, ref)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 @pytest.mark.parametrize("keep", [(128,), (128, 64), (128, 64, 32, 16)])
-def test_other_strategy_sets(mkv, keep):
-    wl = _custom([400, 77], [64, 20])
+def test_other_strategy_sets(mkv, keep, dtype):
+    wl = _custom([400, 77], [64, 20], dtype=dtype)
     inp = W.generate(wl, basis="sperm")
+    if dtype == "fp32" and len(keep) > 3:   # fp32 stores take at most three kept counts: refused up front
+        with pytest.raises(mkv.MkvError) as e:
+            _compress_gpu(mkv, inp, keep)
+        assert e.value.status == mkv.MKV_E_UNSUPPORTED
+        return
     pol = oracle.Policy(keep=keep)
     ref = oracle.compress_all(inp, pol)
     store, q = _compress_gpu(mkv, inp, keep)
