@@ -419,7 +419,8 @@ def test_random_pool_lifecycle(mkv_lib):
     assert min(done.values()) > 0, done
 
 
-def test_pool_appends_of_constructed_vectors_match_the_oracle(mkv_lib):
+@pytest.mark.parametrize("page_bytes", [16384, 40960])
+def test_pool_appends_of_constructed_vectors_match_the_oracle(mkv_lib, page_bytes):
     """Appendable pool without bases, grown by appends of the parity tests' constructed vectors (full-range
     magnitudes, ties, flat, zero, exact-threshold, subnormal, out-of-float32-range squares; many segments keep
     all 128 channels, so sealed segments take their full reserved size): every segment of the view equals the
@@ -447,7 +448,7 @@ def test_pool_appends_of_constructed_vectors_match_the_oracle(mkv_lib):
     R.inp = W.Inputs(_wl(tuple(ctx), 81), K, V, None, None, cu, np.full(len(ctx), 40, np.int32))
     R.K, R.V = storage_to_torch(K, "bf16", "cuda"), storage_to_torch(V, "bf16", "cuda")
     R.basis, R.cu, R.dtype, R.torch = None, cu, "bf16", torch
-    pool = _pool(mkv, n_pages=64, page_bytes=40960, slots=32, has_basis=False, appendable=True)
+    pool = _pool(mkv, n_pages=160, page_bytes=page_bytes, slots=32, has_basis=False, appendable=True)
     ids, n = _grow_in_pool(mkv, R, n0, max(ctx), pool)
     assert list(n) == ctx
     ref = oracle.compress_all(R.inp)
