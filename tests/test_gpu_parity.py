@@ -420,3 +420,25 @@ def test_compress_constructed_vectors_bit_exact(mkv, dtype):
     got = read_store(store, inp.dtype)
     _assert_streams_equal(got["streams"], ref)
     assert got["total"] == _closed_form_bytes(ref, inp.dtype) == store.payload_bytes()
+
+
+def test_selection_output_is_optional_and_padded(mkv):
+    """Decode without the selection output gives the same attention output bit for bit; a selection row wider
+    than the budget holds the same ascending tokens followed by -1."""
+    import torch
+    wl = _custom([700, 150, 0], [90, 150, 5], Hq=8, Hkv=2, seed=23)
+    inp = W.generate(wl, basis="svd")
+    store, q = _compress_gpu(mkv, inp)
+    o1, s1 = mkv.mkv_decode_attn(store, q, inp.T)
+    o2, s2 = mkv.mkv_decode_attn(store, q, inp.T, return_sel=False)
+    o3, s3 = mkv.mkv_decode_attn(store, q, inp.T, sel_stride=s1.shape[-1] + 37)
+    torch.cuda.synchronize()
+    assert s2 is None
+    assert torch.equal(o1, o2) and torch.equal(o1, o3)
+    w = s1.shape[-1]
+    assert torch.equal(s3[..., :w], s1)
+    assert bool((s3[..., w:] == -1).all())
+    n = np.diff(inp.cu_seqlens)
+    for r in range(wl.batch):   # -1 past each request's own selection in the narrow row too
+        te = min(int(inp.T[r]), int(n[r]))
+        assert bool((s1[r, :, te:] == -1).all())
