@@ -442,3 +442,23 @@ def test_selection_output_is_optional_and_padded(mkv):
     for r in range(wl.batch):   # -1 past each request's own selection in the narrow row too
         te = min(int(inp.T[r]), int(n[r]))
         assert bool((s1[r, :, te:] == -1).all())
+
+
+def test_calls_on_a_side_stream(mkv):
+    """Compression and decode enqueued on a stream other than the current one give the default stream's
+    results bit for bit once that stream is synchronised."""
+    import torch
+    wl = _custom([500, 260], [64, 100], Hq=8, Hkv=2, seed=29)
+    inp = W.generate(wl, basis="svd")
+    K, V, q, basis = inputs_to_torch(inp)
+    a = mkv.mkv_compress(K, V, inp.cu_seqlens, basis)
+    oa, sa = mkv.mkv_decode_attn(a, q, inp.T)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        b = mkv.mkv_compress(K, V, inp.cu_seqlens, basis, stream=side)
+        ob, sb = mkv.mkv_decode_attn(b, q, inp.T, stream=side)
+    side.synchronize()
+    assert b.payload_bytes(stream=side) == a.payload_bytes()
+    assert torch.equal(oa, ob) and torch.equal(sa, sb)
