@@ -7,8 +7,12 @@ built once per run by the library's compression call, which is timed as its own 
 "compress".  The printed JSON line reports context tokens per second (sum of the requests' contexts divided by
 the step time), the roofline of the dominant kernel (the score gather-dot, HBM-bound) from HIP events recorded
 around its launches inside the timed region, and the CPU oracle timed on a bounded sample of the same workload.
+The other workloads of the target (one 1048576-token request, the 16-request ragged mix) and the single-layer
+Llama-3.1-8B shape are measured with the same compress and decode legs and reported under "workloads", each with
+the uncompressed baseline on its inputs.
 
 Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload batch8_128k] [--cpu-seconds 12]
+                       [--extras million,ragged16,llama_layer]
 """
 from __future__ import annotations
 
@@ -50,6 +54,8 @@ def parse():
                     help="skip the layer-batched extra (32 layers x 32768 tokens in one call)")
     ap.add_argument("--no-pool", dest="pool", action="store_false",
                     help="skip the paged-pool extra (the same requests added to a pool, decoded through a view)")
+    ap.add_argument("--extras", default="million,ragged16,llama_layer",
+                    help="other workloads measured with the same compress and decode legs (comma list, '' for none)")
     return ap.parse_args()
 
 
@@ -98,37 +104,14 @@ def store_bytes(codes: np.ndarray, cu, Hkv: int, keep, bv: int):
     return row[:S], row[S:], ns, S
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
-              f"run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
-    w = W.get(args.workload)
-    t_gen = time.time()
-    inp = W.generate(w, basis="svd", workers=args.workers)
-    t_gen = time.time() - t_gen
-    # layer-batched extra: the 32 layers of a Llama-3.1-8B-shaped model at 32768 tokens as one store (generated
-    # here, before the GPU is touched, like the main inputs)
-    lw = W.Workload("llama_32_layers", 32, 32, 8, (32768,) * 32, "bf16", (2048,) * 32, "per_request", 50,
-                    "the 32 layers of one 32768-token request, one store")
-    linp = W.generate(lw, basis="svd", workers=args.workers) if args.layers else None
-    # the oracle's CPU baseline runs before the GPU is touched (its process pool forks this process)
-    cpu_base = None if args.no_cpu_baseline else cpu_baseline(inp, args.cpu_seconds, args.workers)
-
-    import torch
-    import kv_cache_compression_svd_amd as mkv
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    from _helpers import inputs_to_torch
-
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    K, V, q, basis = inputs_to_torch(inp, dev)
+def decode_leg(mkv, torch, dev, inp, args, K, V, q, basis, detailed: bool):
+    """Compresses the workload once (timed as its own leg), then times decode steps: warmup, an optional
+    per-kernel breakdown and unprofiled region (detailed), and the timed region of exactly ``args.steps`` steps
+    with HIP events around the score kernel only.  Returns (result dict, handles for further extras)."""
+    w = inp.workload
     bv = 2 if w.dtype == "bf16" else 4
     policy = mkv.mkv_default_policy()
     keep = policy.keeps()
-
-    # ---- compress leg (timed on its own) ----
     sb, tb = mkv.mkv_compress_bytes(K, V, inp.cu_seqlens, policy)
     store_buf = torch.empty(sb, dtype=torch.uint8, device=dev)
     scratch = torch.empty(tb, dtype=torch.uint8, device=dev)
@@ -146,6 +129,7 @@ def main():
     torch.cuda.synchronize()
     c_kern = mkv.mkv_profile_stop()
     compress_ms = e0.elapsed_time(e1) / c_reps
+    del scratch
     payload = store.payload_bytes()
     info = store.view()
     S = int(info.segments_per_tensor)
@@ -158,12 +142,13 @@ def main():
     n_basis_bytes = w.batch * w.n_kv_heads * 2 * 128 * 128 * 4
     compress_alg_bytes = dense + payload + 9 * 2 * S + n_basis_bytes
     rot_flops = 2.0 * 2 * total_tokens * w.n_kv_heads * 128 * 128
+    # segment mix of the stored K and V (share of segments at each kept count)
+    mix = {str(keep[c]): float(np.mean(codes.astype(np.int64) == c)) for c in range(len(keep))}
 
-    # ---- decode: warmup, then exactly K timed steps ----
     T = inp.T
     out = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
     te = np.minimum(T, np.diff(inp.cu_seqlens))
-    sel = torch.empty((w.batch, w.n_kv_heads, int(te.max())), dtype=torch.int32, device=dev)
+    sel = torch.empty((w.batch, w.n_kv_heads, max(int(te.max()), 1)), dtype=torch.int32, device=dev)
     ws = torch.empty(mkv.mkv_decode_workspace_bytes(store, w.n_q_heads, T), dtype=torch.uint8, device=dev)
 
     def step():
@@ -172,18 +157,21 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # per-kernel breakdown (an extra): events around every kernel, which lengthens the step a little
-    mkv.mkv_profile_start()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    kern = mkv.mkv_profile_stop()
-    # unprofiled region (an extra)
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    clean_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    res = {}
+    if detailed:
+        # per-kernel breakdown: events around every kernel, which lengthens the step a little
+        mkv.mkv_profile_start()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        kern = mkv.mkv_profile_stop()
+        res["kernels_avg_ms"] = {k: v[0] / max(v[1], 1) for k, v in kern.items()}
+        # unprofiled region
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        res["ms_per_step_unprofiled"] = (time.perf_counter() - t0) * 1e3 / args.steps
     # timed region: events around the score kernel only (its roofline), nothing else added to the stream
     torch.cuda.synchronize()
     mkv.mkv_profile_start(kernels=["score"])
@@ -193,6 +181,131 @@ def main():
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
     score_kern = mkv.mkv_profile_stop()
+
+    sel_np = sel.cpu().numpy()
+    n = np.diff(inp.cu_seqlens)
+    S_r = (n + 63) // 64
+    seg_base = np.concatenate([[0], np.cumsum(S_r)[:-1]])
+    v_sel_bytes = 0
+    v_segs = 0
+    for r in range(w.batch):
+        for h in range(w.n_kv_heads):
+            j = sel_np[r, h, :te[r]]
+            gs = w.n_kv_heads * seg_base[r] + h * S_r[r] + (j >> 6)
+            v_sel_bytes += int(v_rows[gs].sum())
+            v_segs += int(np.unique(gs).size)
+    q_bytes = w.batch * w.n_q_heads * 128 * bv
+    out_bytes = w.batch * w.n_q_heads * 128 * 4
+    step_alg = k_payload + v_sel_bytes + 9 * (S + v_segs) + q_bytes + out_bytes + n_basis_bytes
+    score_ms, score_n = score_kern.get("score", (float("nan"), 0))
+    score_avg = score_ms / max(score_n, 1)
+    score_alg = k_payload + 9 * S + w.batch * w.n_kv_heads * 128 * 4
+    achieved = score_alg / (score_avg * 1e-3) / 1e9
+    res.update({
+        "ms_per_step": ms,
+        "context_tokens_per_s": total_tokens / (ms * 1e-3),
+        "score": {"achieved_GBps": achieved, "frac": achieved / HBM_PEAK_GBPS, "alg_bytes_per_launch": score_alg,
+                  "avg_launch_ms": score_avg},
+        "step_alg_bytes": step_alg,
+        "step_alg_GBps": step_alg / (ms * 1e-3) / 1e9,
+        "step_frac_of_hbm_peak": step_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "store": {"payload_bytes": payload, "dense_kv_bytes": dense, "compression_ratio": dense / payload,
+                  "k_payload_bytes": k_payload, "v_selected_bytes": v_sel_bytes, "segment_mix": mix},
+        "compress": {"ms": compress_ms, "context_tokens_per_s": total_tokens / (compress_ms * 1e-3),
+                     "alg_bytes": compress_alg_bytes, "alg_GBps": compress_alg_bytes / (compress_ms * 1e-3) / 1e9,
+                     "alg_frac_of_hbm_peak": compress_alg_bytes / (compress_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                     "rotation_TFLOPs": rot_flops / (compress_ms * 1e-3) / 1e12,
+                     "rotation_frac_of_bf16_mfma_peak": rot_flops / (compress_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                     "kernels_avg_ms": {k: v[0] / max(v[1], 1) for k, v in c_kern.items()}},
+    })
+    handles = {"store": store, "store_buf": store_buf, "out": out, "sel": sel, "step": step, "stream": stream,
+               "payload": payload, "dense": dense, "total_tokens": total_tokens, "bv": bv, "policy": policy,
+               "T": T}
+    return res, handles
+
+
+def dense_leg(mkv, torch, dev, inp, args, K, V, q, compressed_ms):
+    """The uncompressed baseline on the same inputs (bf16 only): the whole call timed, HIP events around its
+    attention kernel."""
+    w = inp.workload
+    bv = 2
+    total_tokens = int(inp.cu_seqlens[-1])
+    dense = 2 * total_tokens * w.n_kv_heads * 128 * bv
+    dws = torch.empty(mkv.mkv_dense_decode_workspace_bytes(K, V, inp.cu_seqlens, w.n_q_heads), dtype=torch.uint8,
+                      device=dev)
+    dout = torch.empty((w.batch, w.n_q_heads, 128), dtype=torch.float32, device=dev)
+
+    def dstep():
+        mkv.mkv_dense_decode_attn(K, V, inp.cu_seqlens, q, out=dout, ws=dws)
+
+    for _ in range(args.warmup):
+        dstep()
+    torch.cuda.synchronize()
+    mkv.mkv_profile_start(kernels=["dense_attend"])
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dstep()
+    torch.cuda.synchronize()
+    dms = (time.perf_counter() - t0) * 1e3 / args.steps
+    dk = mkv.mkv_profile_stop()
+    d_attend_ms = dk["dense_attend"][0] / max(dk["dense_attend"][1], 1)
+    dense_bytes = dense + w.batch * w.n_q_heads * 128 * (bv + 4)
+    return {"ms_per_step": dms, "context_tokens_per_s": total_tokens / (dms * 1e-3),
+            "alg_bytes": dense_bytes, "attend_kernel_ms": d_attend_ms,
+            "attend_kernel_GBps": dense_bytes / (d_attend_ms * 1e-3) / 1e9,
+            "attend_kernel_frac_of_hbm_peak": dense_bytes / (d_attend_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+            "attend_kernel_traffic": read_traffic("dense_attend", w.name),
+            "compressed_speedup": dms / compressed_ms}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}); "
+              f"run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    w = W.get(args.workload)
+    t_gen = time.time()
+    inp = W.generate(w, basis="svd", workers=args.workers)
+    t_gen = time.time() - t_gen
+    # the other workloads the target names (1 x 1M, the ragged mix) and the single-layer Llama shape, measured
+    # as extras with the same legs; generated here, before the GPU is touched, with the forked workers
+    extra_names = [x for x in args.extras.split(",") if x and x != w.name] if args.extras else []
+    extra_inp = {}
+    for name in extra_names:
+        t1 = time.time()
+        extra_inp[name] = (W.generate(W.get(name), basis="svd", workers=args.workers), time.time() - t1)
+    # layer-batched extra: the 32 layers of a Llama-3.1-8B-shaped model at 32768 tokens as one store (generated
+    # here, before the GPU is touched, like the main inputs)
+    lw = W.Workload("llama_32_layers", 32, 32, 8, (32768,) * 32, "bf16", (2048,) * 32, "per_request", 50,
+                    "the 32 layers of one 32768-token request, one store")
+    linp = W.generate(lw, basis="svd", workers=args.workers) if args.layers else None
+    # the oracle's CPU baseline runs before the GPU is touched (its process pool forks this process)
+    cpu_base = None if args.no_cpu_baseline else cpu_baseline(inp, args.cpu_seconds, args.workers)
+
+    import torch
+    import kv_cache_compression_svd_amd as mkv
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from _helpers import inputs_to_torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    K, V, q, basis = inputs_to_torch(inp, dev)
+    main_res, H = decode_leg(mkv, torch, dev, inp, args, K, V, q, basis, detailed=True)
+    ms = main_res["ms_per_step"]
+    store, step, stream = H["store"], H["step"], H["stream"]
+    out, sel, T, policy = H["out"], H["sel"], H["T"], H["policy"]
+    payload, dense, total_tokens, bv = H["payload"], H["dense"], H["total_tokens"], H["bv"]
 
     # per-call latency (an extra): events on the stream around each call, back to back and with the 256 MB
     # MALL flushed before every call by reading a 512 MB buffer outside the events (a read leaves clean lines;
@@ -218,33 +331,7 @@ def main():
     del flush_buf
 
     # uncompressed baseline on the same inputs (an extra): bf16 only
-    dense_base = None
-    if w.dtype == "bf16":
-        dws = torch.empty(mkv.mkv_dense_decode_workspace_bytes(K, V, inp.cu_seqlens, w.n_q_heads), dtype=torch.uint8,
-                          device=dev)
-        dout = torch.empty_like(out)
-
-        def dstep():
-            mkv.mkv_dense_decode_attn(K, V, inp.cu_seqlens, q, out=dout, ws=dws)
-
-        for _ in range(args.warmup):
-            dstep()
-        torch.cuda.synchronize()
-        mkv.mkv_profile_start(kernels=["dense_attend"])
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            dstep()
-        torch.cuda.synchronize()
-        dms = (time.perf_counter() - t0) * 1e3 / args.steps
-        dk = mkv.mkv_profile_stop()
-        d_attend_ms = dk["dense_attend"][0] / max(dk["dense_attend"][1], 1)
-        dense_bytes = dense + w.batch * w.n_q_heads * 128 * (bv + 4)
-        dense_base = {"ms_per_step": dms, "context_tokens_per_s": total_tokens / (dms * 1e-3),
-                      "alg_bytes": dense_bytes, "attend_kernel_ms": d_attend_ms,
-                      "attend_kernel_GBps": dense_bytes / (d_attend_ms * 1e-3) / 1e9,
-                      "attend_kernel_frac_of_hbm_peak": dense_bytes / (d_attend_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-                      "attend_kernel_traffic": read_traffic("dense_attend", args.workload),
-                      "compressed_speedup": dms / ms}
+    dense_base = dense_leg(mkv, torch, dev, inp, args, K, V, q, ms) if w.dtype == "bf16" else None
 
     # Gram matrices for basis refresh on the same inputs (an extra): bf16 only
     gram_res = None
@@ -269,6 +356,7 @@ def main():
                     "gram_kernel_TFLOPs": gram_flops / (g_kern_ms * 1e-3) / 1e12,
                     "gram_kernel_traffic": read_traffic("gram", args.workload),
                     "reduce_ms": gk["gram_reduce"][0] / max(gk["gram_reduce"][1], 1)}
+        del gout
 
     layer_res = layer_batched(mkv, torch, dev, linp, args) if linp is not None else None
 
@@ -350,28 +438,26 @@ def main():
             pool_res["ms_per_append_call"] = (time.perf_counter() - t0) * 1e3 / n_app
         del view, pool
 
-    sel_np = sel.cpu().numpy()
-    # V payload actually gathered: rows of the selected tokens
-    n = np.diff(inp.cu_seqlens)
-    S_r = (n + 63) // 64
-    seg_base = np.concatenate([[0], np.cumsum(S_r)[:-1]])
-    v_sel_bytes = 0
-    v_segs = 0
-    for r in range(w.batch):
-        for h in range(w.n_kv_heads):
-            j = sel_np[r, h, :te[r]]
-            gs = w.n_kv_heads * seg_base[r] + h * S_r[r] + (j >> 6)
-            v_sel_bytes += int(v_rows[gs].sum())
-            v_segs += int(np.unique(gs).size)
-    q_bytes = w.batch * w.n_q_heads * 128 * bv
-    out_bytes = w.batch * w.n_q_heads * 128 * 4
-    step_alg = k_payload + v_sel_bytes + 9 * (S + v_segs) + q_bytes + out_bytes + n_basis_bytes
-    score_ms, score_n = score_kern.get("score", (float("nan"), 0))
-    score_avg = score_ms / max(score_n, 1)
-    score_alg = k_payload + 9 * S + w.batch * w.n_kv_heads * 128 * 4
-    achieved = score_alg / (score_avg * 1e-3) / 1e9
-    traffic = read_traffic("score", args.workload)
+    # the other workloads: their own inputs, compress and decode legs (and the uncompressed baseline)
+    del K, V, q, basis, store, H, step, out, sel
+    torch.cuda.empty_cache()
+    extras = {}
+    for name in extra_names:
+        einp, gen_s = extra_inp.pop(name)
+        eK, eV, eq, eb = inputs_to_torch(einp, dev)
+        r, eh = decode_leg(mkv, torch, dev, einp, args, eK, eV, eq, eb, detailed=True)
+        ew = einp.workload
+        r["config"] = {"batch": ew.batch, "context": list(ew.ctx) if len(set(ew.ctx)) > 1 or ew.batch == 1 else
+                       f"{ew.batch} x {ew.ctx[0]}", "q_heads": ew.n_q_heads, "kv_heads": ew.n_kv_heads,
+                       "T": int(ew.T[0]) if len(set(ew.T)) == 1 else list(ew.T), "dtype": ew.dtype}
+        r["input_generation_s"] = gen_s
+        if ew.dtype == "bf16":
+            r["dense_baseline"] = dense_leg(mkv, torch, dev, einp, args, eK, eV, eq, r["ms_per_step"])
+        extras[name] = r
+        del eK, eV, eq, eb, eh, einp
+        torch.cuda.empty_cache()
 
+    traffic = read_traffic("score", args.workload)
     result = {
         "metric": METRIC,
         "value": total_tokens / (ms * 1e-3),
@@ -388,30 +474,27 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "context": list(w.ctx) if w.batch <= 4 else
                    f"{w.batch} x {w.ctx[0]}" if len(set(w.ctx)) == 1 else list(w.ctx),
                    "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": 128,
-                   "T": int(w.T[0]) if len(set(w.T)) == 1 else list(w.T), "seg_len": 64, "keep": list(keep),
-                   "energy_frac": 0.9, "accumulate": "fp32", "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "hbm", "kernel": "score", "achieved": achieved, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": traffic, "alg_bytes_per_launch": score_alg,
-                     "avg_launch_ms": score_avg},
-        "step_alg_bytes": step_alg,
-        "step_alg_GBps": step_alg / (ms * 1e-3) / 1e9,
-        "step_frac_of_hbm_peak": step_alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "ms_per_step_unprofiled": clean_ms,
+                   "T": int(w.T[0]) if len(set(w.T)) == 1 else list(w.T), "seg_len": 64,
+                   "keep": list(policy.keeps()), "energy_frac": 0.9, "accumulate": "fp32",
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "kernel": "score", "achieved": main_res["score"]["achieved_GBps"],
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": main_res["score"]["frac"],
+                     "traffic": traffic, "alg_bytes_per_launch": main_res["score"]["alg_bytes_per_launch"],
+                     "avg_launch_ms": main_res["score"]["avg_launch_ms"]},
+        "step_alg_bytes": main_res["step_alg_bytes"],
+        "step_alg_GBps": main_res["step_alg_GBps"],
+        "step_frac_of_hbm_peak": main_res["step_frac_of_hbm_peak"],
+        "ms_per_step_unprofiled": main_res["ms_per_step_unprofiled"],
         "call_latency": call_latency,
-        "kernels_avg_ms": {k: v[0] / max(v[1], 1) for k, v in kern.items()},
-        "store": {"payload_bytes": payload, "dense_kv_bytes": dense, "compression_ratio": dense / payload,
-                  "k_payload_bytes": k_payload, "v_selected_bytes": v_sel_bytes},
-        "compress": {"ms": compress_ms, "context_tokens_per_s": total_tokens / (compress_ms * 1e-3),
-                     "alg_bytes": compress_alg_bytes, "alg_GBps": compress_alg_bytes / (compress_ms * 1e-3) / 1e9,
-                     "rotation_TFLOPs": rot_flops / (compress_ms * 1e-3) / 1e12,
-                     "rotation_frac_of_bf16_mfma_peak": rot_flops / (compress_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
-                     "kernels_avg_ms": {k: v[0] / max(v[1], 1) for k, v in c_kern.items()}},
+        "kernels_avg_ms": main_res["kernels_avg_ms"],
+        "store": main_res["store"],
+        "compress": main_res["compress"],
         "dense_baseline": dense_base,
         "gram": gram_res,
         "layer_batched": layer_res,
         "append": append_res,
         "pool": pool_res,
+        "workloads": extras,
         "input_generation_s": t_gen,
     }
     if cpu_base is not None:
@@ -500,7 +583,7 @@ def cpu_baseline(inp, seconds: float, procs: int):
     pooled = sum(n * k / tt for n, k, tt in got) / w.n_kv_heads
     best = max(single, pooled)
     return {"value": best, "unit": "context tokens/s", "cores": len(units) if pooled >= single else threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(), "host_cpu_count": os.cpu_count(),
             "single_process": {"value": single, "blas_threads": threads, "reps": reps, "seconds": t},
             "process_pool": {"value": pooled, "processes": len(units), "blas_threads_each": 1,
                              "units": [list(u) for u in units]},

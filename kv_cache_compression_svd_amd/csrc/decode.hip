@@ -609,9 +609,11 @@ hipError_t launch_sel_emit(const DecArgs& a, int n_streams, hipStream_t s) {
 // sparse exact attention over the selected tokens
 // =====================================================================================================
 // One selected token's row, as seen by the 8 lanes of its group: each lane owns c/8 consecutive slots.  A wave
-// loads one shape for all its tokens, sized by the largest kept count among them (LW value words per lane,
-// enough for that count), plus 8 index bytes from a 4-byte aligned address.  Bytes past a lane's own slots
-// are ignored; the store keeps slack after the payload for these over-reads.
+// loads one value shape for all its tokens, sized by the largest kept count among them (LW value words per lane,
+// enough for that count), and each lane loads exactly its own index bytes.  Value bytes past a lane's own slots
+// are ignored: they belong to the token's later rows or to the segment's index block, except in a segment of a
+// few rows at c <= 32, where the last row's widest load ends at most 40 bytes past the segment; every store and
+// pool buffer keeps 256 bytes after its last payload byte for that.
 template <int LW>
 struct RowBuf {
     uint32_t v[LW];
@@ -628,8 +630,6 @@ __device__ __forceinline__ void load_row(RowBuf<LW>& rb, const uint8_t* payload,
                                          bool ok) {
     const int nsl_shift = lc - 3;                       // log2 of slots per lane
     const uint8_t* va = ok ? payload + rm.vaddr + (size_t)(sl << nsl_shift) * BV : payload;
-    const uint64_t ib = rm.iaddr + (uint64_t)(sl << nsl_shift);
-    const uint8_t* ia = ok ? payload + (ib & ~3ull) : payload;
     if constexpr (LW >= 4) {
 #pragma unroll
         for (int j = 0; j < LW / 4; ++j) {
@@ -640,11 +640,22 @@ __device__ __forceinline__ void load_row(RowBuf<LW>& rb, const uint8_t* payload,
         const u32x2 x = *reinterpret_cast<const u32x2*>(va);
         rb.v[0] = x.x; rb.v[1] = x.y;
     }
-    const u32x2 y = *reinterpret_cast<const u32x2*>(ia);
-    const int sh = ok ? (int)(ib & 3) * 8 : 0;
-    // drop the misaligned leading bytes (only c = 16 has them)
-    rb.ix[0] = sh ? ((y.x >> sh) | (y.y << (32 - sh))) : y.x;
-    rb.ix[1] = sh ? (y.y >> sh) : y.y;
+    // index bytes: exactly this lane's slots (8 at c = 64, 4 at c = 32, 2 at c = 16, naturally aligned), none
+    // when every channel is stored
+    rb.ix[0] = 0u;
+    rb.ix[1] = 0u;
+    if (ok && lc < 7) {
+        const uint8_t* ia = payload + rm.iaddr + (uint64_t)(sl << nsl_shift);
+        if (lc == 6) {
+            const u32x2 y = *reinterpret_cast<const u32x2*>(ia);
+            rb.ix[0] = y.x;
+            rb.ix[1] = y.y;
+        } else if (lc == 5) {
+            rb.ix[0] = *reinterpret_cast<const uint32_t*>(ia);
+        } else {
+            rb.ix[0] = *reinterpret_cast<const uint16_t*>(ia);
+        }
+    }
 }
 
 template <int BV, int LW>

@@ -325,3 +325,70 @@ def check_out(out: np.ndarray, ref: np.ndarray, rel=2e-3):
         err = np.linalg.norm(out[h] - ref[h])
         assert err <= rel * max(nr, 1e-30), f"head {h}: rel-L2 {err / max(nr, 1e-30):.3e} > {rel}"
         assert np.max(np.abs(out[h] - ref[h])) <= rel * max(np.max(np.abs(ref[h])), 1e-30), f"head {h}: elementwise"
+
+
+# ---- SVD-basis compression: every difference from the oracle needs a reason ----------------------------------
+# With a true SVD basis the GPU rotates in float32 (MFMA) and the oracle in float64, so a stored value may differ
+# by one storage ulp.  A differing segment code or kept set is accepted only where such a difference can move the
+# decision: the bound is taken from the value differences actually observed (both sides read back).
+def ulp(x, dtype: str) -> np.ndarray:
+    """Spacing of the storage dtype at |x| (the spacing at 1.0 for x = 0)."""
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.exp2(e - (7 if dtype == "bf16" else 23))
+
+
+def observed_ulps(got_vals: np.ndarray, ref_vals: np.ndarray, both: np.ndarray, dtype: str) -> float:
+    """Largest |GPU value - oracle value| over the channels both sides kept, in ulps of the oracle value."""
+    if not np.any(both):
+        return 0.0
+    d = np.abs(got_vals[both] - ref_vals[both]) / ulp(ref_vals[both], dtype)
+    return float(d.max())
+
+
+def energy_flip_bound(xhat: np.ndarray, m: float, dtype: str, frac: float = 0.9) -> np.ndarray:
+    """Per vector of xhat [n][d]: the largest |E_c/E_all - frac| at which moving every element by at most m ulp
+    can flip the decision E_c >= frac * E_all, for any c.  Each square moves by at most 2|x|u + u^2 (u = m ulp);
+    E_c (a maximum over c-subsets) and E_all each move by at most the sum of those, so frac * E_all - E_c moves
+    by at most (1 + frac) times it."""
+    u = m * ulp(xhat, dtype)
+    dsq = np.sum(2.0 * np.abs(xhat) * u + u * u, axis=1)
+    e_all = np.sum(xhat * xhat, axis=1)
+    return (1.0 + frac) * dsq / np.where(e_all > 0, e_all, 1.0)
+
+
+def code_difference_reason(xhat: np.ndarray, code_got: int, code_ref: int, keep, m: float, dtype: str,
+                           frac: float = 0.9):
+    """Index of a vector of the segment xhat [ns][d] whose decision at the count that separates the two codes
+    lies inside the observed rotation error, on the side that explains the difference; None if there is none.
+    GPU code above the oracle's (fewer channels): some vector is inadmissible for the oracle at that count.
+    GPU code below: some vector the oracle admits must have been refused by the GPU."""
+    import oracle
+    c = keep[max(code_got, code_ref)]
+    e_all = np.sum(xhat * xhat, axis=1)
+    ratio = oracle.kept_energy(xhat, oracle.channel_order(xhat), c) / np.where(e_all > 0, e_all, 1.0)
+    bound = energy_flip_bound(xhat, m, dtype, frac)
+    side = (ratio < frac) if code_got > code_ref else (ratio >= frac)
+    ok = np.nonzero(side & (np.abs(ratio - frac) <= bound) & (e_all > 0))[0]
+    return int(ok[0]) if ok.size else None
+
+
+def channel_swap_reason(xhat_row: np.ndarray, got_mask: np.ndarray, ref_mask: np.ndarray, c: int, m: float,
+                        dtype: str) -> bool:
+    """A token whose kept set differs at the same count c: every swapped channel's oracle magnitude must lie
+    within 2 m ulp of the oracle's c-th largest magnitude (a GPU ranking of a above b with |x_a| <= t <= |x_b|
+    needs |x_b| - |x_a| <= m (ulp_a + ulp_b))."""
+    mags = np.abs(xhat_row)
+    tc = np.sort(mags)[::-1][c - 1]
+    swapped = np.nonzero(got_mask != ref_mask)[0]
+    return bool(np.all(np.abs(mags[swapped] - tc) <= 2.0 * m * ulp(np.array([tc]), dtype)[0] + 1e-300))
+
+
+def record_parity(test: str, case: str, **counts):
+    """Appends the counts of a parity test to the JSON-lines file named by MKV_PARITY_LOG (if set)."""
+    import json
+    import os
+    path = os.environ.get("MKV_PARITY_LOG")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps({"test": test, "case": case, **counts}) + "\n")

@@ -13,8 +13,9 @@ import pytest
 
 import oracle
 import workloads as W
-from _helpers import (check_decode_unit, check_out, check_selection, inputs_to_torch, prerotated_inputs,
-                      read_store, upload_oracle_store)
+from _helpers import (channel_swap_reason, check_decode_unit, check_out, check_selection, code_difference_reason,
+                      inputs_to_torch, observed_ulps, prerotated_inputs, read_store, record_parity,
+                      upload_oracle_store)
 
 pytestmark = pytest.mark.gpu
 
@@ -91,43 +92,44 @@ def test_compress_p2_signed_permutation_bit_exact(mkv, name, div):
     assert got["total"] == _closed_form_bytes(ref, inp.dtype)
 
 
-def _ulp(x, dtype):
-    ax = np.abs(x)
-    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
-    bits = 7 if dtype == "bf16" else 23
-    return np.exp2(e - bits)
-
-
 @pytest.mark.parametrize("name,div", CASES, ids=IDS)
 def test_compress_p3_svd_basis(mkv, name, div):
+    """SVD basis: stored values within one storage ulp of the oracle's; every segment whose code differs must
+    hold a vector whose oracle energy ratio lies within the flip bound implied by the observed value
+    differences, on the side that explains the difference; every token whose kept set differs at an equal
+    code must swap only channels within 2 m ulp of the oracle's c-th magnitude (m: observed ulps)."""
     inp = W.generate(_wl(name, div), basis="svd")
+    keep = (128, 64, 32)
     ref = oracle.compress_all(inp)
     st, _ = _compress_gpu(mkv, inp)
     got = read_store(st, inp.dtype)["streams"]
+    m = 0.0
+    for key, r in ref.items():
+        g = got[key]
+        m = max(m, observed_ulps(g.vals, r.vals, g.mask & r.mask, inp.dtype))
+    assert m <= 1.0 + 1e-9, f"stored values differ by {m} ulp"
     seg_total = seg_diff = tok_total = tok_diff = 0
     for key, r in ref.items():
         g = got[key]
+        rr, hh, X = key
+        x = W.to_f64((inp.K if X == 0 else inp.V)[inp.cu_seqlens[rr]:inp.cu_seqlens[rr + 1], hh, :], inp.dtype)
+        xhat = oracle.rotate_round(x, inp.basis[rr, hh, X], inp.dtype)
         seg_total += r.c.size
-        seg_diff += int(np.sum(g.c != r.c))
-        # values where both kept the channel: within one storage ulp of the oracle's
-        both = g.mask & r.mask
-        assert np.all(np.abs(g.vals[both] - r.vals[both]) <= _ulp(r.vals[both], inp.dtype) * 1.0001), key
+        for s in np.nonzero(g.codes != r.codes)[0]:
+            seg_diff += 1
+            rows = xhat[64 * s: 64 * s + 64]
+            why = code_difference_reason(rows, int(g.codes[s]), int(r.codes[s]), keep, m, inp.dtype)
+            assert why is not None, f"segment {s} of {key}: code {g.codes[s]} vs oracle {r.codes[s]} unexplained"
         same_c = np.repeat(g.c == r.c, 64)[: r.n]
         rows = np.nonzero(same_c & np.any(g.mask != r.mask, axis=1))[0]
         tok_total += int(same_c.sum())
         tok_diff += rows.size
         for j in rows:
-            # a differing kept set must sit on a magnitude boundary the rotation error can move:
-            # the swapped channels' oracle magnitudes lie within 2 ulp of the oracle's c-th magnitude
             c = int(r.c[j // 64])
-            mags = np.abs(oracle.rotate_round(
-                W.to_f64((inp.K if key[2] == 0 else inp.V)[inp.cu_seqlens[key[0]] + j, key[1], :][None, :],
-                         inp.dtype), inp.basis[key[0], key[1], key[2]], inp.dtype))[0]
-            tc = np.sort(mags)[::-1][c - 1]
-            swapped = np.nonzero(g.mask[j] != r.mask[j])[0]
-            assert np.all(np.abs(mags[swapped] - tc) <= 2 * _ulp(np.array([tc]), inp.dtype)[0] + 1e-300), (key, j)
-    print(f"P3 {name}/{div}: segments with other codes {seg_diff}/{seg_total}, tokens with other channel "
-          f"sets {tok_diff}/{tok_total}")
+            assert channel_swap_reason(xhat[j], g.mask[j], r.mask[j], c, m, inp.dtype), (key, j)
+    record_parity("compress_p3_svd_basis", f"{name}/{div}", observed_ulps=m, segments=seg_total,
+                  segments_other_code=seg_diff, tokens=tok_total, tokens_other_channels=tok_diff)
+    # every difference is explained above; these caps only guard against a systematic drift
     assert seg_diff <= max(2, 0.01 * seg_total)
     assert tok_diff <= max(4, 0.02 * tok_total)
 

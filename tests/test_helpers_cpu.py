@@ -38,3 +38,49 @@ def test_valid_selections_enumerates_the_tie_band():
     assert [x.tolist() for x in valid_selections(s, 3)] == [[0, 1, 6]]      # the 3rd score stands alone
     assert valid_selections(np.zeros(100), 50) is None                       # C(100, 50) selections
     assert valid_selections(s, 0)[0].size == 0
+
+
+def _near_threshold_segment(rng, target_gap):
+    """64 bf16-exact vectors that keep 64 channels comfortably, except vector 5 whose 64-channel energy ratio
+    sits target_gap away from 0.9 (positive: admissible)."""
+    x = np.zeros((64, 128))
+    x[:, :16] = rng.choice([-1.0, 1.0], (64, 16)) * 4.0       # big channels: ratio well above 0.9 at 32 and 64
+    x[:, 16:] = rng.choice([-1.0, 1.0], (64, 112)) * 0.0625
+    # vector 5: 64 channels of a, 64 of b with 64 a^2 / (64 a^2 + 64 b^2) = 0.9 + gap
+    a = 1.0
+    b2 = a * a * (1.0 / (0.9 + target_gap) - 1.0)
+    x[5, :64] = a
+    x[5, 64:] = np.sqrt(b2)
+    return oracle.rne(x, "bf16")
+
+
+def test_code_difference_needs_a_vector_inside_the_flip_bound():
+    """The P3 justification accepts a differing code only with a vector near the energy target on the side that
+    explains it: vector 5 sits just below 0.9 at 64 channels, so a GPU that kept 64 (code 1) where the oracle
+    kept 128 (code 0) is explained at m = 1 ulp but not at m = 0, and never the other way round."""
+    from _helpers import code_difference_reason, energy_flip_bound
+    rng = np.random.default_rng(3)
+    seg = _near_threshold_segment(rng, -2e-4)
+    order = oracle.channel_order(seg)
+    ratio = oracle.kept_energy(seg, order, 64)[5] / np.sum(seg[5] ** 2)
+    assert ratio < 0.9 and abs(ratio - 0.9) <= energy_flip_bound(seg, 1.0, "bf16")[5]
+    assert oracle.vector_min_keep(seg)[5] == 128
+    assert code_difference_reason(seg, 1, 0, (128, 64, 32), 1.0, "bf16") == 5
+    assert code_difference_reason(seg, 1, 0, (128, 64, 32), 0.0, "bf16") is None
+    assert code_difference_reason(seg, 0, 1, (128, 64, 32), 1.0, "bf16") is None   # wrong side of the target
+    far = _near_threshold_segment(rng, -0.05)
+    assert code_difference_reason(far, 1, 0, (128, 64, 32), 1.0, "bf16") is None
+
+
+def test_channel_swap_needs_magnitudes_at_the_cut():
+    from _helpers import channel_swap_reason
+    x = oracle.rne(np.linspace(1.0, 3.0, 128), "bf16")[::-1].copy()   # descending, bf16-exact
+    ref = np.zeros(128, bool)
+    ref[np.argsort(-np.abs(x), kind="stable")[:64]] = True
+    got = ref.copy()
+    i_in, i_out = 63, 64          # swap the channels on either side of the cut
+    got[i_in], got[i_out] = False, True
+    assert channel_swap_reason(x, got, ref, 64, 1.0, "bf16") == (abs(x[i_in] - x[i_out]) <= 2 * 2.0 ** -6)
+    got2 = ref.copy()
+    got2[0], got2[127] = False, True   # swap the largest for the smallest: never explained
+    assert not channel_swap_reason(x, got2, ref, 64, 1.0, "bf16")
