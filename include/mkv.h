@@ -17,7 +17,8 @@
  *   - [host] pointers are CPU memory read during the call only; [dev] pointers are HIP device memory of the
  *     current device.
  *   - The caller allocates all device memory (store, scratch, workspace, outputs); the library never calls
- *     hipMalloc/hipFree.  Sizes come from the *_bytes calls.
+ *     hipMalloc/hipFree.  Sizes come from the *_bytes calls.  (One exception for callers that cannot allocate:
+ *     mkv_decode_attn_noalloc uses a workspace array held in the library's own code object.)
  *   - Device work is enqueued on the given stream and is asynchronous unless a call says it synchronises.
  *   - Every argument check runs on the host before anything is enqueued; on failure nothing is launched, the
  *     call returns MKV_E_ARG or MKV_E_UNSUPPORTED and mkv_last_error() says why.  A failed launch returns
@@ -193,6 +194,18 @@ mkv_status mkv_decode_workspace_bytes(const mkv_store* store, int32_t n_q_heads,
 mkv_status mkv_decode_attn(const mkv_store* store, const void* q, int32_t n_q_heads, const int32_t* T,
                            float* out, int32_t* sel, int32_t sel_stride, void* ws, size_t ws_bytes,
                            mkv_stream_t stream);
+
+/* mkv_decode_attn without a caller workspace, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  The workspace is a device-resident array
+ * inside the library, mkv_decode_noalloc_max_bytes() = 128 MiB on each device the library is loaded on (held
+ * until the process ends; that covers 8 x 131072 or 1 x 1048576 tokens at 8 KV heads); a call whose
+ * mkv_decode_workspace_bytes exceeds it fails with MKV_E_ARG before anything is enqueued.  No device memory is
+ * allocated or freed.  Every call on one device uses that device's one array, so calls that overlap on one GPU
+ * (different streams or threads without ordering) race; calls ordered on one stream do not.  The array's
+ * contents are scratch: each call clears what it needs.  Arguments and results as for mkv_decode_attn. */
+size_t mkv_decode_noalloc_max_bytes(void);
+mkv_status mkv_decode_attn_noalloc(const mkv_store* store, const void* q, int32_t n_q_heads, const int32_t* T,
+                                   float* out, int32_t* sel, int32_t sel_stride, mkv_stream_t stream);
 
 /* ---- paged pools -------------------------------------------------------------------------------------------
  * A pool holds the compressed caches of many requests of one layer in one buffer, for serving: requests are

@@ -93,6 +93,9 @@ SIGNATURES = {
     "mkv_decode_workspace_bytes": (c_int32, [c_void_p, c_int32, POINTER(c_int32), POINTER(c_size_t)]),
     "mkv_decode_attn": (c_int32, [c_void_p, c_void_p, c_int32, POINTER(c_int32), c_void_p, c_void_p, c_int32,
                                   c_void_p, c_size_t, c_void_p]),
+    "mkv_decode_noalloc_max_bytes": (c_size_t, []),
+    "mkv_decode_attn_noalloc": (c_int32, [c_void_p, c_void_p, c_int32, POINTER(c_int32), c_void_p, c_void_p,
+                                          c_int32, c_void_p]),
     "mkv_dense_decode_workspace_bytes": (c_int32, [c_void_p, c_int32, POINTER(c_size_t)]),
     "mkv_dense_decode_attn": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_void_p, c_size_t, c_void_p]),
     "mkv_gram_workspace_bytes": (c_int32, [c_void_p, POINTER(c_size_t)]),
@@ -467,6 +470,27 @@ def mkv_decode_attn(store: Store, q, T, out=None, sel=None, sel_stride=None, ws=
         ws = torch.empty(mkv_decode_workspace_bytes(store, Hq, t), dtype=torch.uint8, device=q.device)
     _check(lib().mkv_decode_attn(store.handle, _ptr(q), int(Hq), tp, _ptr(out), _ptr(sel), int(stride), _ptr(ws),
                                  c_size_t(ws.numel()), _stream_ptr(stream)))
+    return out, sel
+
+
+def mkv_decode_noalloc_max_bytes() -> int:
+    return int(lib().mkv_decode_noalloc_max_bytes())
+
+
+def mkv_decode_attn_noalloc(store: Store, q, T, out, sel=None, stream=None):
+    """mkv_decode_attn on the library's device-resident workspace: no device memory is allocated by this call
+    (out, and sel if given, are the caller's).  Returns (out, sel)."""
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM or not q.is_contiguous() or not q.is_cuda:
+        raise ValueError("q must be a contiguous CUDA tensor [batch][n_q_heads][128]")
+    if _dtype_code(q) != store.dtype:
+        raise TypeError("q must have the store's dtype")
+    B, Hq = q.shape[0], q.shape[1]
+    if B != store.batch:
+        raise ValueError(f"q has batch {B}, the store {store.batch}")
+    _, tp = _T_array(T, B)
+    stride = sel.shape[-1] if sel is not None else 0
+    _check(lib().mkv_decode_attn_noalloc(store.handle, _ptr(q), int(Hq), tp, _ptr(out), _ptr(sel), int(stride),
+                                         _stream_ptr(stream)))
     return out, sel
 
 

@@ -1151,17 +1151,12 @@ mkv_status mkv_decode_workspace_bytes(const mkv_store* s, int32_t n_q_heads, con
     return MKV_OK;
 }
 
-mkv_status mkv_decode_attn(const mkv_store* s, const void* q, int32_t n_q_heads, const int32_t* T, float* out,
-                           int32_t* sel, int32_t sel_stride, void* ws, size_t ws_bytes, mkv_stream_t stream_) {
-    hipStream_t stream = reinterpret_cast<hipStream_t>(stream_);
-    DecPlan P;
-    mkv_status st = plan_decode(s, n_q_heads, T, &P);
-    if (st) return st;
-    if (!q || !out) return fail(MKV_E_ARG, "q and out must be non-NULL");
-    if (!ws) return fail(MKV_E_ARG, "ws is NULL");
-    if (!aligned(ws)) return fail(MKV_E_ARG, "ws must be 256-byte aligned");
-    if (ws_bytes < P.bytes) return fail(MKV_E_ARG, "ws_bytes %zu < required %llu", ws_bytes, (unsigned long long)P.bytes);
-    if (sel && sel_stride < P.max_T) return fail(MKV_E_ARG, "sel_stride %d < largest selection %d", sel_stride, P.max_T);
+namespace {
+
+// The decode step over a planned workspace (every argument already checked).
+mkv_status decode_run(const mkv_store* s, const void* q, const DecPlan& P, float* out, int32_t* sel,
+                      int32_t sel_stride, void* ws, hipStream_t stream) {
+    mkv_status st;
     const Shape& sh = s->sh;
     uint8_t* w = static_cast<uint8_t*>(ws);
     DecArgs a;
@@ -1220,6 +1215,44 @@ mkv_status mkv_decode_attn(const mkv_store* s, const void* q, int32_t n_q_heads,
     if ((st = run(K_ATTEND, stream, [&] { return launch_attend(a, (int)P.n_ablk, stream); }))) return st;
     if ((st = run(K_COMBINE, stream, [&] { return launch_combine(a, streams, stream); }))) return st;
     return MKV_OK;
+}
+
+mkv_status check_decode_args(const DecPlan& P, const void* q, float* out, int32_t* sel, int32_t sel_stride) {
+    if (!q || !out) return fail(MKV_E_ARG, "q and out must be non-NULL");
+    if (sel && sel_stride < P.max_T) return fail(MKV_E_ARG, "sel_stride %d < largest selection %d", sel_stride, P.max_T);
+    return MKV_OK;
+}
+
+}  // namespace
+
+mkv_status mkv_decode_attn(const mkv_store* s, const void* q, int32_t n_q_heads, const int32_t* T, float* out,
+                           int32_t* sel, int32_t sel_stride, void* ws, size_t ws_bytes, mkv_stream_t stream_) {
+    DecPlan P;
+    mkv_status st = plan_decode(s, n_q_heads, T, &P);
+    if (st) return st;
+    if ((st = check_decode_args(P, q, out, sel, sel_stride))) return st;
+    if (!ws) return fail(MKV_E_ARG, "ws is NULL");
+    if (!aligned(ws)) return fail(MKV_E_ARG, "ws must be 256-byte aligned");
+    if (ws_bytes < P.bytes) return fail(MKV_E_ARG, "ws_bytes %zu < required %llu", ws_bytes, (unsigned long long)P.bytes);
+    return decode_run(s, q, P, out, sel, sel_stride, ws, reinterpret_cast<hipStream_t>(stream_));
+}
+
+size_t mkv_decode_noalloc_max_bytes(void) { return kStaticWorkspaceBytes; }
+
+mkv_status mkv_decode_attn_noalloc(const mkv_store* s, const void* q, int32_t n_q_heads, const int32_t* T,
+                                   float* out, int32_t* sel, int32_t sel_stride, mkv_stream_t stream_) {
+    DecPlan P;
+    mkv_status st = plan_decode(s, n_q_heads, T, &P);
+    if (st) return st;
+    if ((st = check_decode_args(P, q, out, sel, sel_stride))) return st;
+    if (P.bytes > kStaticWorkspaceBytes)
+        return fail(MKV_E_ARG, "this decode needs %llu bytes of workspace, above the %llu bytes the library keeps on "
+                    "each device; call mkv_decode_attn with a caller workspace", (unsigned long long)P.bytes,
+                    (unsigned long long)kStaticWorkspaceBytes);
+    void* ws = nullptr;
+    const hipError_t e = static_workspace(&ws);
+    if (e != hipSuccess) return fail(MKV_E_DEVICE, "device-resident workspace unavailable: %s", hipGetErrorString(e));
+    return decode_run(s, q, P, out, sel, sel_stride, ws, reinterpret_cast<hipStream_t>(stream_));
 }
 
 // ---- uncompressed baseline --------------------------------------------------------------------------------

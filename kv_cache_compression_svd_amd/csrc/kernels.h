@@ -166,4 +166,9 @@ struct GramArgs {
 hipError_t launch_gram(const GramArgs& a, int n_blocks, hipStream_t s);
 hipError_t launch_gram_reduce(const GramArgs& a, hipStream_t s);
 
+// ---- device-resident decode workspace (noalloc.hip) ------------------------------------------------------
+constexpr uint64_t kStaticWorkspaceBytes = 128ull << 20;   // 128 MiB per device
+// Device address of the current device's copy (looked up on the first call per device, then kept).
+hipError_t static_workspace(void** ptr);
+
 }  // namespace mkv

@@ -289,3 +289,27 @@ def test_appendable_pool_layout_and_refusals():
     L.mkv_pool_stats(h, ctypes.byref(info))
     assert (info.free_pages, info.free_segment_slots, info.live_requests) == (8, 10, 0)
     L.mkv_pool_destroy(h)
+
+
+def test_noalloc_decode_refuses_workspaces_above_its_maximum():
+    """A decode whose workspace would exceed the device-resident array is refused on the host, before anything is
+    enqueued: the store is only attached (its buffer address is recorded, never read), so no GPU is needed."""
+    L = mkv.lib()
+    cap = int(L.mkv_decode_noalloc_max_bytes())
+    assert cap == 128 << 20
+    n = 1 << 22                                   # 4M tokens x 8 KV heads: keys and lists far above the maximum
+    d, cu = _desc(batch=1, heads=8, cu=(0, n))
+    p = mkv.mkv_default_policy()
+    st, sb, tb = _bytes(d, p)
+    assert st == mkv.MKV_OK
+    h = ctypes.c_void_p()
+    fake = ctypes.c_void_p(1 << 40)               # an aligned address that is never dereferenced here
+    assert L.mkv_store_attach(ctypes.byref(d), ctypes.byref(p), 0, fake, sb, ctypes.byref(h)) == mkv.MKV_OK
+    T = (ctypes.c_int32 * 1)(4096)
+    ws = ctypes.c_size_t()
+    assert L.mkv_decode_workspace_bytes(h, 32, T, ctypes.byref(ws)) == mkv.MKV_OK
+    assert ws.value > cap
+    st = L.mkv_decode_attn_noalloc(h, fake, 32, T, fake, None, 0, None)
+    assert st == mkv.MKV_E_ARG
+    assert "workspace" in mkv.mkv_last_error()
+    assert L.mkv_store_destroy(h) == mkv.MKV_OK
