@@ -23,7 +23,7 @@ __global__ void k_upload(Upload u) {
 }
 
 hipError_t launch_upload(const Upload& u, hipStream_t s) {
-    hipLaunchKernelGGL(k_upload, dim3(1), dim3(256), 0, s, u);
+    launch_kernel(k_upload, dim3(1), dim3(256), 0, s, u);
     return hipGetLastError();
 }
 
@@ -683,7 +683,7 @@ __global__ __launch_bounds__(512) void k_cmp_append(CmpArgs a, AppendArgs x) {
 
 hipError_t launch_cmp_append(const CmpArgs& a, const AppendArgs& x, int n_requests, hipStream_t s) {
     if (n_requests == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_cmp_append, dim3(n_requests * 2 * x.Hkv), dim3(512), 0, s, a, x);
+    launch_kernel(k_cmp_append, dim3(n_requests * 2 * x.Hkv), dim3(512), 0, s, a, x);
     return hipGetLastError();
 }
 
@@ -806,14 +806,14 @@ static hipError_t launch_cmp(const CmpArgs& a, int dtype, hipStream_t s) {
     const dim3 grid(2 * a.nblk), block(256);
     if (a.nblk == 0) return hipSuccess;
     if (dtype == 1) {
-        hipLaunchKernelGGL(k_cmp_bf16<PACK>, grid, dim3(512), 0, s, a);
+        launch_kernel(k_cmp_bf16<PACK>, grid, dim3(512), 0, s, a);
     } else {
         static bool attr_set = false;
         if (!attr_set) {
             hipFuncSetAttribute((const void*)k_cmp_f32<PACK>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kF32Lds);
             attr_set = true;
         }
-        hipLaunchKernelGGL(k_cmp_f32<PACK>, grid, block, kF32Lds, s, a);
+        launch_kernel(k_cmp_f32<PACK>, grid, block, kF32Lds, s, a);
     }
     return hipGetLastError();
 }
@@ -852,7 +852,7 @@ __global__ __launch_bounds__(1024) void k_cmp_scan(uint64_t* a, int64_t n, uint6
 }
 
 hipError_t launch_cmp_scan(uint64_t* wg_total, int64_t count, uint64_t* total, hipStream_t s) {
-    hipLaunchKernelGGL(k_cmp_scan, dim3(1), dim3(1024), 0, s, wg_total, count, total);
+    launch_kernel(k_cmp_scan, dim3(1), dim3(1024), 0, s, wg_total, count, total);
     return hipGetLastError();
 }
 
@@ -915,13 +915,13 @@ __global__ __launch_bounds__(256) void k_pool_fix(PoolArgs p) {
 
 hipError_t launch_pool_place(const PoolArgs& p, int n_streams, hipStream_t s) {
     if (n_streams == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_pool_place, dim3(n_streams), dim3(64), 0, s, p);
+    launch_kernel(k_pool_place, dim3(n_streams), dim3(64), 0, s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_pool_fix(const PoolArgs& p, int n_streams, hipStream_t s) {
     if (n_streams == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_pool_fix, dim3(n_streams), dim3(256), 0, s, p);
+    launch_kernel(k_pool_fix, dim3(n_streams), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void k_dec_prep(DecArgs a, Upload tab) {
 }
 
 hipError_t launch_dec_prep(const DecArgs& a, const Upload& tab, hipStream_t s) {
-    hipLaunchKernelGGL(k_dec_prep, dim3(4 * a.B * a.Hkv), dim3(256), 0, s, a, tab);
+    launch_kernel(k_dec_prep, dim3(4 * a.B * a.Hkv), dim3(256), 0, s, a, tab);
     return hipGetLastError();
 }
 
@@ -319,12 +319,12 @@ __global__ __launch_bounds__(256) void k_score(DecArgs a) {
         }
     }
     __syncthreads();
-    // keys out (256 contiguous bytes per segment) and the workgroup histogram
+    // keys out (256 contiguous bytes per segment, streamed past the caches) and the workgroup histogram
     for (int j = tid; j < nloc * MKV_SEG; j += 256) {
         const int tok = slot_segment(i, j >> 6, stride) * MKV_SEG + (j & 63);
         if (tok < n) {
             const uint32_t key = skeys[j];
-            a.keys[keybase + tok] = key;
+            __builtin_nontemporal_store(key, &a.keys[keybase + tok]);
             atomicAdd(&sh[key >> 20], 1u);
             atomicAdd(&shc[key >> 26], 1u);
         }
@@ -346,8 +346,8 @@ __global__ __launch_bounds__(256) void k_score(DecArgs a) {
 
 hipError_t launch_score(const DecArgs& a, int n_blocks, hipStream_t s) {
     if (n_blocks == 0) return hipSuccess;
-    if (a.dtype == 1) hipLaunchKernelGGL(k_score<2>, dim3(n_blocks), dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(k_score<4>, dim3(n_blocks), dim3(256), 0, s, a);
+    if (a.dtype == 1) launch_kernel(k_score<2>, dim3(n_blocks), dim3(256), 0, s, a);
+    else launch_kernel(k_score<4>, dim3(n_blocks), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -596,12 +596,12 @@ __global__ __launch_bounds__(1024) void k_sel_emit(DecArgs a) {
 
 hipError_t launch_sel_collect(const DecArgs& a, int n_blocks, hipStream_t s) {
     if (n_blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_sel_collect, dim3(n_blocks), dim3(256), 0, s, a);
+    launch_kernel(k_sel_collect, dim3(n_blocks), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 hipError_t launch_sel_emit(const DecArgs& a, int n_streams, hipStream_t s) {
     if (n_streams == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_sel_emit, dim3(n_streams * a.etiles), dim3(1024), 0, s, a);
+    launch_kernel(k_sel_emit, dim3(n_streams * a.etiles), dim3(1024), 0, s, a);
     return hipGetLastError();
 }
 
@@ -1005,10 +1005,10 @@ __global__ __launch_bounds__(256) void k_combine(DecArgs a) {
 template <int BV>
 static void launch_attend_g(const DecArgs& a, int n_blocks, hipStream_t s) {
     switch (a.G) {
-        case 1: hipLaunchKernelGGL((k_attend<BV, 1>), dim3(n_blocks), dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL((k_attend<BV, 2>), dim3(n_blocks), dim3(256), 0, s, a); break;
-        case 4: hipLaunchKernelGGL((k_attend<BV, 4>), dim3(n_blocks), dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL((k_attend<BV, 8>), dim3(n_blocks), dim3(256), 0, s, a); break;
+        case 1: launch_kernel((k_attend<BV, 1>), dim3(n_blocks), dim3(256), 0, s, a); break;
+        case 2: launch_kernel((k_attend<BV, 2>), dim3(n_blocks), dim3(256), 0, s, a); break;
+        case 4: launch_kernel((k_attend<BV, 4>), dim3(n_blocks), dim3(256), 0, s, a); break;
+        default: launch_kernel((k_attend<BV, 8>), dim3(n_blocks), dim3(256), 0, s, a); break;
     }
 }
 
@@ -1023,10 +1023,10 @@ hipError_t launch_combine(const DecArgs& a, int n_streams, hipStream_t s) {
     if (n_streams == 0) return hipSuccess;
     const dim3 grid(4 * n_streams), block(256);   // four workgroups per stream, one per quarter of the channels
     switch (a.G) {
-        case 1: hipLaunchKernelGGL(k_combine<1>, grid, block, 0, s, a); break;
-        case 2: hipLaunchKernelGGL(k_combine<2>, grid, block, 0, s, a); break;
-        case 4: hipLaunchKernelGGL(k_combine<4>, grid, block, 0, s, a); break;
-        default: hipLaunchKernelGGL(k_combine<8>, grid, block, 0, s, a); break;
+        case 1: launch_kernel(k_combine<1>, grid, block, 0, s, a); break;
+        case 2: launch_kernel(k_combine<2>, grid, block, 0, s, a); break;
+        case 4: launch_kernel(k_combine<4>, grid, block, 0, s, a); break;
+        default: launch_kernel(k_combine<8>, grid, block, 0, s, a); break;
     }
     return hipGetLastError();
 }

@@ -165,10 +165,10 @@ __global__ __launch_bounds__(256) void k_dense_attend(DenseArgs a) {
 hipError_t launch_dense_attend(const DenseArgs& a, int n_blocks, hipStream_t s) {
     if (n_blocks == 0) return hipSuccess;
     switch (a.G) {
-        case 1: hipLaunchKernelGGL(k_dense_attend<1>, dim3(n_blocks), dim3(256), 0, s, a); break;
-        case 2: hipLaunchKernelGGL(k_dense_attend<2>, dim3(n_blocks), dim3(256), 0, s, a); break;
-        case 4: hipLaunchKernelGGL(k_dense_attend<4>, dim3(n_blocks), dim3(256), 0, s, a); break;
-        default: hipLaunchKernelGGL(k_dense_attend<8>, dim3(n_blocks), dim3(256), 0, s, a); break;
+        case 1: launch_kernel(k_dense_attend<1>, dim3(n_blocks), dim3(256), 0, s, a); break;
+        case 2: launch_kernel(k_dense_attend<2>, dim3(n_blocks), dim3(256), 0, s, a); break;
+        case 4: launch_kernel(k_dense_attend<4>, dim3(n_blocks), dim3(256), 0, s, a); break;
+        default: launch_kernel(k_dense_attend<8>, dim3(n_blocks), dim3(256), 0, s, a); break;
     }
     return hipGetLastError();
 }

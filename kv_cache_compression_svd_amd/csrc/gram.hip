@@ -129,12 +129,12 @@ __global__ __launch_bounds__(256) void k_gram_reduce(GramArgs a) {
 
 hipError_t launch_gram(const GramArgs& a, int n_blocks, hipStream_t s) {
     if (n_blocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(k_gram, dim3(n_blocks), dim3(256), 0, s, a);
+    launch_kernel(k_gram, dim3(n_blocks), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
 hipError_t launch_gram_reduce(const GramArgs& a, hipStream_t s) {
-    hipLaunchKernelGGL(k_gram_reduce, dim3(16 * 2 * a.B * a.Hkv), dim3(256), 0, s, a);
+    launch_kernel(k_gram_reduce, dim3(16 * 2 * a.B * a.Hkv), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

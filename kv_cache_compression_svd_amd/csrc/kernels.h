@@ -1,9 +1,30 @@
 // Internal interface between the host entry points (api.cpp) and the gfx950 kernels.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace mkv {
+
+// Kernel timing: while the host times a launch it sets these events (thread-local, for exactly one launch), and the
+// launch hands them to the dispatch itself (hipExtLaunchKernel), so timing adds no marker packets to the stream.
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+    bool used = false;
+};
+LaunchEvents& launch_events();
+
+template <typename... KArgs, typename... Args>
+inline void launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t lds, hipStream_t s,
+                          Args... args) {
+    LaunchEvents& ev = launch_events();
+    if (ev.start && !ev.used) {
+        ev.used = true;
+        hipExtLaunchKernelGGL(kernel, grid, block, lds, s, ev.start, ev.stop, 0u, args...);
+    } else {
+        hipLaunchKernelGGL(kernel, grid, block, lds, s, args...);
+    }
+}
 
 constexpr int kUploadWords = 448;       // int32 words a table upload carries in its kernel arguments
 constexpr int kHistBins = 4096;         // first radix level of the top-T select: key bits [31:20]
