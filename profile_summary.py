@@ -5,6 +5,10 @@
       per-kernel launches, total and average duration
   python3 profile_summary.py pmc <run_results.db> [kernel-substring]
       per-kernel average of each collected counter per dispatch
+  python3 profile_summary.py sq <run_results.db> <kernel-substring>
+      per-dispatch totals of SQ counters (one row per shader engine, 32 on MI355X) and GRBM_GUI_ACTIVE (one row
+      per XCD, 8), with the vector-ALU busy fraction (a wave64 VALU instruction occupies a 16-lane SIMD for 4
+      cycles; 1024 SIMDs), the share of wave cycles spent waiting, and LDS bank-conflict cycles per LDS instruction
 """
 import sqlite3
 import sys
@@ -28,6 +32,34 @@ def pmc(db, pat=None):
     for name, cn, v, n in rows:
         if pat is None or pat in name:
             print(f"{name[:64]:64s} {cn:>12s} {v:18.1f} {n:10d}")
+
+
+def sq(db, pat):
+    c = sqlite3.connect(db)
+    rows = list(c.execute("select name, counter_name, avg(counter_value), count(*) from pmc_events "
+                          "group by name, counter_name order by name"))
+    rows = [r for r in rows if pat in r[0]]
+    if not rows:
+        raise SystemExit(f"{db}: no kernel matching {pat!r}")
+    name = rows[0][0]
+    vals = {}
+    for n, cn, v, cnt in rows:
+        if n != name:
+            continue
+        per = 32 if cn.startswith("SQ_") else 8 if cn.startswith("GRBM_") else 1
+        vals[cn] = (v * per if cn.startswith("SQ_") else v, cnt // per)
+    print(f"kernel: {name}")
+    for cn, (tot, nd) in sorted(vals.items()):
+        print(f"{cn}: {tot:.4g}  (per dispatch, {nd} dispatches)")
+    if "SQ_INSTS_VALU" in vals and "GRBM_GUI_ACTIVE" in vals:
+        busy = vals["SQ_INSTS_VALU"][0] * 4 / (vals["GRBM_GUI_ACTIVE"][0] * 1024)
+        print(f"derived valu_busy_fraction: {busy:.3f}  (SQ_INSTS_VALU x 4 cycles / (GRBM_GUI_ACTIVE x 1024 SIMDs))")
+    if "SQ_WAIT_INST_ANY" in vals and "SQ_WAVE_CYCLES" in vals:
+        print(f"derived wait_fraction: {vals['SQ_WAIT_INST_ANY'][0] / vals['SQ_WAVE_CYCLES'][0]:.3f}  "
+              f"(SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES)")
+    if "SQ_LDS_BANK_CONFLICT" in vals and "SQ_INSTS_LDS" in vals and vals["SQ_INSTS_LDS"][0] > 0:
+        print(f"derived lds_conflict_cycles_per_lds_inst: "
+              f"{vals['SQ_LDS_BANK_CONFLICT'][0] / vals['SQ_INSTS_LDS'][0]:.2f}")
 
 
 def _avg(db, counter, pat):
@@ -67,5 +99,7 @@ if __name__ == "__main__":
         trace(sys.argv[2])
     elif mode == "pmc":
         pmc(sys.argv[2], sys.argv[3] if len(sys.argv) > 3 else None)
+    elif mode == "sq":
+        sq(sys.argv[2], sys.argv[3])
     elif mode == "traffic":
         traffic(sys.argv[2], *sys.argv[3:7], int(sys.argv[7]), sys.argv[8])

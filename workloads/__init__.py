@@ -235,9 +235,14 @@ def generate(w: Workload, basis: str = "svd", heads=None, workers: int = 1) -> I
     if par:
         import multiprocessing as mp
         _FORK_STATE = (w, cu, K, V, q, sig, bas, basis, heads)
+        pool = mp.get_context("fork").Pool(min(workers, B))
         try:
-            with mp.get_context("fork").Pool(min(workers, B)) as pool:
-                list(pool.imap_unordered(_fork_worker, range(B)))
+            list(pool.imap_unordered(_fork_worker, range(B)))
+            pool.close()    # workers exit on their own: no termination signal reaches them
+            pool.join()
+        except BaseException:
+            pool.terminate()
+            raise
         finally:
             _FORK_STATE = None
     else:
