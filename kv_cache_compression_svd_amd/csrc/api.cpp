@@ -1074,7 +1074,7 @@ mkv_status mkv_pool_request(const mkv_pool* p, int32_t id, int64_t* n_tokens, in
 namespace {
 
 struct DecPlan {
-    int32_t G = 0, Hq = 0, spw = 0, sgx = 0, max_T = 0, hcopies = 1, etiles = 1;
+    int32_t G = 0, Hq = 0, spw = 0, sgx = 0, max_T = 0, hcopies = 1, etiles = 1, achunk = kAttnChunk;
     std::vector<int32_t> tab;    // n | segbase | scap | tokbase | T | kblk | ablk | basis slot
     int64_t n_sblk = 0, n_kblk = 0, n_ablk = 0;
     uint64_t o_tab, o_state, o_hist, o_qp, o_qbar, o_keys, o_L, o_sel, o_part, bytes;
@@ -1117,12 +1117,26 @@ mkv_status plan_decode(const mkv_store* s, int32_t n_q_heads, const int32_t* T, 
         tT[r] = (int32_t)te;
         tbs[r] = sh.bslot[r];
         tkb[r] = (int32_t)kb;
-        tab_[r] = (int32_t)ab;
         sgx = std::max<int64_t>(sgx, cdiv(cdiv(n, MKV_SEG_LEN), P->spw));
         kb += (int64_t)sh.Hkv * cdiv(n, kKeysPerBlock);
-        ab += (int64_t)sh.Hkv * cdiv(te, kAttnChunk);
         P->max_T = std::max<int32_t>(P->max_T, (int32_t)te);
         P->etiles = std::max<int32_t>(P->etiles, (int32_t)cdiv(n, kEmitTileTokens));
+    }
+    // selected tokens per attention workgroup: halved from 256 (down to 64) while the grid would not fill the
+    // resident slots, so that small selections spread over more, shorter workgroups, as long as the combine
+    // kernel merges at most 64 partials per head (its time grows with their number: at 1 x 1M tokens, 128
+    // partials cost more there than the shorter attention workgroups save)
+    auto attn_blocks = [&](int64_t chunk) {
+        int64_t n_ab = 0;
+        for (int r = 0; r < B; ++r) n_ab += (int64_t)sh.Hkv * cdiv(tT[r], chunk);
+        return n_ab;
+    };
+    P->achunk = kAttnChunk;
+    while (P->achunk > 64 && attn_blocks(P->achunk) < kAttnSlots && cdiv(P->max_T, P->achunk / 2) <= 64)
+        P->achunk /= 2;
+    for (int r = 0; r < B; ++r) {
+        tab_[r] = (int32_t)ab;
+        ab += (int64_t)sh.Hkv * cdiv(tT[r], P->achunk);
     }
     tkb[B] = (int32_t)kb;
     tab_[B] = (int32_t)ab;
@@ -1209,7 +1223,7 @@ mkv_status decode_run(const mkv_store* s, const void* q, const DecPlan& P, float
     a.state = reinterpret_cast<uint32_t*>(w + P.o_state);
     a.L = reinterpret_cast<uint2*>(w + P.o_L);
     a.part = reinterpret_cast<float*>(w + P.o_part);
-    a.achunk = kAttnChunk;
+    a.achunk = P.achunk;
 
     // per-request tables: the first kUploadWords words ride on the prep kernel, the rest on upload launches
     int32_t* tdst = reinterpret_cast<int32_t*>(w + P.o_tab);

@@ -14,9 +14,9 @@
 //   emit     one workgroup per stream resolves the exact T-th key among the candidates (two more 10-bit radix
 //            levels) and writes the selected tokens in ascending order through an LDS bitmap; ties go to the
 //            lower token index.
-//   attend   256 selected tokens per workgroup (64 per wave): exact logits of the group's query heads against the
-//            sparse keys, a softmax per wave and head, weighted sum of the sparse values; emits (max, sum, partial
-//            output) per head.
+//   attend   256, 128 or 64 selected tokens per workgroup (a quarter per wave; fewer when the selection is small):
+//            exact logits of the group's query heads against the sparse keys, a softmax per wave and head,
+//            weighted sum of the sparse values; emits (max, sum, partial output) per head.
 //   combine  log-sum-exp merge of the partials, then out_h = o'_h @ B_V^T.
 #include "common.cuh"
 #include "kernels.h"
@@ -709,20 +709,20 @@ struct AttnLds {
     int mc[4][64];                // log2 c of K | log2 c of V << 8 | valid << 16
 };
 
-// One wave's 64 tokens: logits, softmax and the weighted value sum.  LW value words per lane cover the wave's
-// largest kept count; NF passes (of 8 tokens) are in flight at a time, and the first value passes are issued
-// before the softmax so that their latency overlaps it.
-template <int BV, int G, int LW>
+// One wave's 8 * NP tokens (NP passes of 8): logits, softmax and the weighted value sum.  LW value words per
+// lane cover the wave's largest kept count; NF passes are in flight at a time, and the first value passes are
+// issued before the softmax so that their latency overlaps it.
+template <int BV, int G, int LW, int NP>
 __device__ __forceinline__ void attend_wave(AttnLds<G>& L, const uint8_t* payload, int wid, int lane, float (&acc)[G][2],
                                             float (&mW)[G], float (&lW)[G]) {
     constexpr int SLOTS = LW * 4 / BV;                       // value slots a lane holds
-    constexpr int NF = LW <= 4 ? 4 : 2;                     // passes in flight (within 128 VGPRs at G = 4)
+    constexpr int NF = (LW <= 4 ? 4 : 2) < NP ? (LW <= 4 ? 4 : 2) : NP;   // passes in flight (128 VGPRs at G = 4)
     constexpr bool NARROW = LW == 2 * BV;                   // kept counts <= 64: every slot is indexed
     const int t8 = lane >> 3, sl = lane & 7;
     const float scale = 1.4426950408889634f * 0.08838834764831845f;   // log2(e) / sqrt(128)
 
 #pragma unroll
-    for (int grp = 0; grp < 8 / NF; ++grp) {
+    for (int grp = 0; grp < NP / NF; ++grp) {
         RowBuf<LW> kr[NF];
         int wd[NF];
 #pragma unroll
@@ -786,19 +786,19 @@ __device__ __forceinline__ void attend_wave(AttnLds<G>& L, const uint8_t* payloa
     // ---- softmax over the wave's tokens, one lane per token ----
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-        const float x = L.ps[wid][lane][h];
+        const float x = lane < 8 * NP ? L.ps[wid][lane][h] : -INFINITY;
         const float M = wave_max(x);
         const float e = (M == -INFINITY) ? 0.f : exp2f(x - M);
         mW[h] = M;
         lW[h] = wave_sum(e);
-        L.ps[wid][lane][h] = e;
+        if (lane < 8 * NP) L.ps[wid][lane][h] = e;
     }
     wave_lds_sync();
 
     // ---- weighted sum of the sparse value rows; lane owns channels 2*lane, 2*lane+1 ----
     float* dense = L.vb[wid][t8];
 #pragma unroll
-    for (int grp = 0; grp < 8 / NF; ++grp) {
+    for (int grp = 0; grp < NP / NF; ++grp) {
         if (grp > 0) issue_v(grp);
 #pragma unroll
         for (int q = 0; q < NF; ++q) {
@@ -833,13 +833,16 @@ __device__ __forceinline__ void attend_wave(AttnLds<G>& L, const uint8_t* payloa
     }
 }
 
-template <int BV, int G>
+// Grid: one workgroup per chunk of 32 * NP selected tokens of a stream (8 * NP per wave); fewer passes per wave
+// give more, shorter workgroups when there are few selected tokens in all.
+template <int BV, int G, int NP>
 __global__ __launch_bounds__(256) void k_attend(DecArgs a) {
+    constexpr int CHUNK = 32 * NP;
     __shared__ __attribute__((aligned(16))) AttnLds<G> L;
     const int b = blockIdx.x;
     const int r = find_slot(a.t_ablk, a.B, b);
     const int n = a.t_n[r], T = a.t_T[r];
-    const int nach = (T + kAttnChunk - 1) / kAttnChunk;
+    const int nach = (T + CHUNK - 1) / CHUNK;
     const int local = b - a.t_ablk[r];
     const int g = local / nach, chunk = local - g * nach;
     const int stream = r * a.Hkv + g, Hq = a.G * a.Hkv;
@@ -851,8 +854,8 @@ __global__ __launch_bounds__(256) void k_attend(DecArgs a) {
     int lcmax;
     {   // this lane's token: list entry, segments, row addresses
         const int32_t* list = a.sel_int + (size_t)stream * a.sel_int_stride;
-        const int li = chunk * kAttnChunk + wid * 64 + lane;
-        const int j = (li < T) ? list[li] : -1;
+        const int li = chunk * CHUNK + wid * (8 * NP) + lane;
+        const int j = (lane < 8 * NP && li < T) ? list[li] : -1;
         int word;
         RowMeta k_{0, 0}, v_{0, 0};
         if (j >= 0) {
@@ -882,8 +885,8 @@ __global__ __launch_bounds__(256) void k_attend(DecArgs a) {
 #pragma unroll
     for (int h = 0; h < G; ++h) { acc[h][0] = 0.f; acc[h][1] = 0.f; }
     // value words per lane: c/8 slots of BV bytes for the wave's largest c (at least 8 bytes)
-    if (!wide) attend_wave<BV, G, 2 * BV>(L, a.payload, wid, lane, acc, mW, lW);
-    else attend_wave<BV, G, 4 * BV>(L, a.payload, wid, lane, acc, mW, lW);
+    if (!wide) attend_wave<BV, G, 2 * BV, NP>(L, a.payload, wid, lane, acc, mW, lW);
+    else attend_wave<BV, G, 4 * BV, NP>(L, a.payload, wid, lane, acc, mW, lW);
 
     if (lane == 0) {
 #pragma unroll
@@ -955,6 +958,18 @@ __global__ __launch_bounds__(256) void k_combine(DecArgs a) {
                 Ls += f * l;
                 const int cnt = min(64, nach - c0);
                 int k = 0;
+                for (; k + 16 <= cnt; k += 16) {
+                    float2 v[16];
+#pragma unroll
+                    for (int u = 0; u < 16; ++u)
+                        v[u] = *reinterpret_cast<const float2*>(a.part + ((size_t)(first + c0 + k + u) * G + h) * PW + 2 + 2 * lane);
+#pragma unroll
+                    for (int u = 0; u < 16; ++u) {
+                        const float fk = lane_f(f, k + u);
+                        O0 = fmaf(fk, v[u].x, O0);
+                        O1 = fmaf(fk, v[u].y, O1);
+                    }
+                }
                 for (; k + 8 <= cnt; k += 8) {
                     float2 v[8];
 #pragma unroll
@@ -1002,20 +1017,30 @@ __global__ __launch_bounds__(256) void k_combine(DecArgs a) {
     }
 }
 
-template <int BV>
+template <int BV, int NP>
 static void launch_attend_g(const DecArgs& a, int n_blocks, hipStream_t s) {
     switch (a.G) {
-        case 1: launch_kernel((k_attend<BV, 1>), dim3(n_blocks), dim3(256), 0, s, a); break;
-        case 2: launch_kernel((k_attend<BV, 2>), dim3(n_blocks), dim3(256), 0, s, a); break;
-        case 4: launch_kernel((k_attend<BV, 4>), dim3(n_blocks), dim3(256), 0, s, a); break;
-        default: launch_kernel((k_attend<BV, 8>), dim3(n_blocks), dim3(256), 0, s, a); break;
+        case 1: launch_kernel((k_attend<BV, 1, NP>), dim3(n_blocks), dim3(256), 0, s, a); break;
+        case 2: launch_kernel((k_attend<BV, 2, NP>), dim3(n_blocks), dim3(256), 0, s, a); break;
+        case 4: launch_kernel((k_attend<BV, 4, NP>), dim3(n_blocks), dim3(256), 0, s, a); break;
+        default: launch_kernel((k_attend<BV, 8, NP>), dim3(n_blocks), dim3(256), 0, s, a); break;
+    }
+}
+
+template <int BV>
+static void launch_attend_np(const DecArgs& a, int n_blocks, hipStream_t s) {
+    switch (a.achunk) {
+        case 64: launch_attend_g<BV, 2>(a, n_blocks, s); break;
+        case 128: launch_attend_g<BV, 4>(a, n_blocks, s); break;
+        default: launch_attend_g<BV, 8>(a, n_blocks, s); break;
     }
 }
 
 hipError_t launch_attend(const DecArgs& a, int n_blocks, hipStream_t s) {
     if (n_blocks == 0) return hipSuccess;
-    if (a.dtype == 1) launch_attend_g<2>(a, n_blocks, s);
-    else launch_attend_g<4>(a, n_blocks, s);
+    if (a.achunk != 64 && a.achunk != 128 && a.achunk != 256) return hipErrorInvalidValue;
+    if (a.dtype == 1) launch_attend_np<2>(a, n_blocks, s);
+    else launch_attend_np<4>(a, n_blocks, s);
     return hipGetLastError();
 }
 

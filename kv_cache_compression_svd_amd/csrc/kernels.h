@@ -32,7 +32,8 @@ constexpr int kMaxHistCopies = 8;      // copies of each stream's histograms (sp
 constexpr int kCoarseOff = 64;          // coarse histograms (top 6 key bits, 64 bins per copy) inside the state words
 constexpr int kStateWords = kCoarseOff + 64 * kMaxHistCopies;   // per (request, KV head) selection state
 constexpr int kKeysPerBlock = 4096;     // keys per workgroup in the selection passes
-constexpr int kAttnChunk = 256;         // selected tokens per attention workgroup
+constexpr int kAttnChunk = 256;         // selected tokens per attention workgroup (at most; 128 or 64 for small grids)
+constexpr int kAttnSlots = 1024;        // attention workgroups resident at once (4 per CU)
 constexpr int kEmitTileTokens = 32768;  // tokens per workgroup of the selection's emit kernel
 constexpr int kDenseChunk = 512;        // tokens per workgroup of the uncompressed baseline
 constexpr int kGramChunk = 16384;       // tokens per workgroup of the Gram matrices
@@ -148,7 +149,7 @@ struct DecArgs {
     int32_t etiles;             // emit workgroups per stream: tiles of 32768 tokens of the longest context
     uint2* L;                   // same indexing as keys: taken tokens, then candidates, as (token index, key)
     float* part;                // [n_ablk][G][130]
-    int32_t achunk;             // tokens per attention partial (the combine kernel's chunk)
+    int32_t achunk;             // tokens per attention partial: 256, 128 or 64 (the combine kernel's chunk)
 };
 
 hipError_t launch_dec_prep(const DecArgs& a, const Upload& tab, hipStream_t s);
