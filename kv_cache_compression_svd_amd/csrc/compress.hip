@@ -271,8 +271,10 @@ __device__ __forceinline__ uint32_t vector_threshold8(const uint32_t* mw, uint32
 // for the first count; smaller counts are searched above the previous threshold.
 // Called by every thread of the workgroup (64 vectors of one segment): before searching level k >= 2 the
 // workgroup checks whether some valid vector already cannot reach it, either because it failed level k-1 or
-// because the top keep[k] energy is bounded by E_{k-1} - (keep[k-1] - keep[k]) * t_{k-1}^2 (each of the dropped
-// values is at least t_{k-1}) and that bound is below the target.  Then no vector's result at level k can
+// because an upper bound on its top keep[k] energy is below the target.  Two bounds, both from level k-1:
+// E_{k-1} - (keep[k-1] - keep[k]) * t_{k-1}^2 (each of the dropped values is at least t_{k-1}), and, with
+// u = 2 t_{k-1} and m = the number of values >= u, E(values >= u) + (keep[k] - m) * u^2 when m <= keep[k] (the
+// top keep[k] are those m values and keep[k] - m values below u).  Then no vector's result at level k can
 // change the segment's code, and the search stops for the whole workgroup.  s_fail: per-level flags, zero on
 // entry.
 __device__ __forceinline__ int vector_decide8(const uint32_t* w, const CmpArgs& a, uint32_t* thr, bool valid,
@@ -295,12 +297,12 @@ __device__ __forceinline__ int vector_decide8(const uint32_t* w, const CmpArgs& 
     const uint32_t mx = max8u(max((uint32_t)mx2.x, (uint32_t)mx2.y));
     uint32_t lo_end = min8u(min((uint32_t)mn2.x, (uint32_t)mn2.y));
     int best = 0;
-    double ec_prev = e_all, tv_prev = 0.0;
+    double ec_prev = e_all, tv_prev = 0.0, ub2_prev = INFINITY;
     for (int k = 1; k < a.n_keep; ++k) {
         const int c = a.keep[k];
         if (k >= 2) {
             // the margin keeps fp64 rounding of the bound from ever flagging a vector that reaches level k
-            const double ub = ec_prev - (double)(a.keep[k - 1] - c) * (tv_prev * tv_prev);
+            const double ub = fmin(ec_prev - (double)(a.keep[k - 1] - c) * (tv_prev * tv_prev), ub2_prev);
             if (valid && (best < k - 1 || ub + 1e-10 * e_all < bound)) s_fail[k] = 1;
             __syncthreads();
             if (s_fail[k]) break;
@@ -309,17 +311,26 @@ __device__ __forceinline__ int vector_decide8(const uint32_t* w, const CmpArgs& 
         // kept energy from the magnitudes, squared in float64 (exact for every bf16 value, subnormals and values
         // beyond 2^64 included); recomputed from the magnitude words rather than kept from the total (the signed
         // words): holding the 16 float64 values across the search costs registers
-        double part = 0.0;
-        int gt = 0;
+        // u: the magnitude pattern one exponent step above t (a larger value; at least twice t for normal t)
+        const uint32_t u = t + 128u;
+        double part = 0.0, eu = 0.0;
+        int gt = 0, mu = 0;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const uint32_t lo = mw[j] & 0xFFFFu, hi = mw[j] >> 16;
             const double xl = bf16_to_f32(lo), xh = bf16_to_f32(hi);
             if (lo > t) { part += xl * xl; ++gt; }
             if (hi > t) { part += xh * xh; ++gt; }
+            if (lo >= u) { eu += xl * xl; ++mu; }
+            if (hi >= u) { eu += xh * xh; ++mu; }
         }
         const double tv = bf16_to_f32(t);
         const double ec = sum8d(part) + (double)(c - sum8i(gt)) * (tv * tv);
+        if (k + 1 < a.n_keep) {
+            const int cn = a.keep[k + 1], m = sum8i(mu);
+            const double es = sum8d(eu), uv = bf16_to_f32(u);
+            ub2_prev = (u < 0x7F80u && m <= cn) ? es + (double)(cn - m) * (uv * uv) : INFINITY;
+        }
         thr[k] = t;
         if (ec >= bound) best = k;
         lo_end = t;
