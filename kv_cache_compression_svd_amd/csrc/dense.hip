@@ -57,7 +57,8 @@ __global__ __launch_bounds__(256) void k_dense_attend(DenseArgs a) {
     const int tw0 = wid * TPW + grp;
     auto ld = [&](const uint16_t* P, int it) -> u32x4 {
         const int t = min(tw0 + 4 * it, cnt - 1);
-        return *reinterpret_cast<const u32x4*>(P + (size_t)t * rs);
+        // read once: non-temporal, so that the stream does not displace the step's small tables from the caches
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(P + (size_t)t * rs));
     };
 
     // ---- logits ----

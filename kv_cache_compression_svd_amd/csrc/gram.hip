@@ -32,7 +32,7 @@ __device__ __forceinline__ void gram_load(GramLoad& L, const uint16_t* X, size_t
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
         const int t = min(tile0 + 4 * t4 + a, cnt - 1);
-        L.w[a] = *reinterpret_cast<const u32x4*>(X + (size_t)t * rs + 8 * c8);
+        L.w[a] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(X + (size_t)t * rs + 8 * c8));   // read once
     }
 }
 
