@@ -17,6 +17,7 @@ Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload batch8_1
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -298,6 +299,12 @@ def main():
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from _helpers import inputs_to_torch
 
+    # The timed loops run Python between kernel launches; a full garbage collection inside one (tens of ms with
+    # torch loaded) stalls the launches and would be charged to the GPU.  Collect once here, keep what exists
+    # out of later collections, and leave the collector off for the GPU legs (this process is short-lived).
+    gc.collect()
+    gc.freeze()
+    gc.disable()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     K, V, q, basis = inputs_to_torch(inp, dev)
