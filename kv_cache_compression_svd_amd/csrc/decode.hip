@@ -567,29 +567,25 @@ __global__ __launch_bounds__(1024) void k_sel_emit(DecArgs a) {
             }
         }
         auto taken = [&](const uint2 e) { return all || e.y > kstar || (e.y == kstar && (int)e.x <= cut); };
-        // selected tokens before this tile: they come first in the stream's ascending row
-        uint32_t before = 0;
-        if (tile > 0) {
-            uint32_t c = 0;
-            for (uint32_t i = tid; i < ngt; i += 1024) c += (int)L[i].x < t0 ? 1u : 0u;
-            for (uint32_t i = tid; i < ncand; i += 1024) {
-                const uint2 e = cand[i];
-                c += ((int)e.x < t0 && taken(e)) ? 1u : 0u;
-            }
-            block_exscan(c, tmp, &before);
-        }
+        // one pass over both lists: count the selected tokens before this tile (they come first in the stream's
+        // ascending row) and mark the tile's own in the LDS bitmap
         bm[tid] = 0u;
         __syncthreads();
+        uint32_t c = 0;
         for (uint32_t i = tid; i < ngt; i += 1024) {
-            const uint32_t x = L[i].x;
-            if ((int)x >= t0 && (int)x < t0 + kTileBits) atomicOr(&bm[(x - t0) >> 5], 1u << ((x - t0) & 31));
+            const int x = (int)L[i].x;
+            if (x < t0) ++c;
+            else if (x < t0 + kTileBits) atomicOr(&bm[(x - t0) >> 5], 1u << ((x - t0) & 31));
         }
         for (uint32_t i = tid; i < ncand; i += 1024) {
             const uint2 e = cand[i];
-            if (taken(e) && (int)e.x >= t0 && (int)e.x < t0 + kTileBits)
-                atomicOr(&bm[(e.x - t0) >> 5], 1u << ((e.x - t0) & 31));
+            if (!taken(e)) continue;
+            const int x = (int)e.x;
+            if (x < t0) ++c;
+            else if (x < t0 + kTileBits) atomicOr(&bm[(x - t0) >> 5], 1u << ((x - t0) & 31));
         }
-        __syncthreads();
+        uint32_t before = 0;
+        block_exscan(c, tmp, &before);   // its barriers also order the bitmap writes before emit_tile's reads
         emit_tile(bm, t0, before, a.sel_int + (size_t)stream * a.sel_int_stride, urow, tmp);
     }
     if (urow && tile == 0) {
