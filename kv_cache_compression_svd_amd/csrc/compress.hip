@@ -584,7 +584,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
                 const int nq = ns * 16;   // 16-byte pieces of ns rows of 256 bytes
                 for (int qd = tid; qd < nq; qd += 512) {
                     const int row = qd >> 4, col = (qd & 15) * 8;
-                    *reinterpret_cast<u32x4*>(dst + (size_t)qd * 16) = *reinterpret_cast<const u32x4*>(&R[row * XS + col]);
+                    // written once and not read again in this pass: non-temporal
+                    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&R[row * XS + col]), reinterpret_cast<u32x4*>(dst + (size_t)qd * 16));
                 }
             } else {
                 if (valid) {
@@ -594,7 +595,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
                 __syncthreads();
                 const int nq = ns * c * 3 / 16;
                 for (int qd = tid; qd < nq; qd += 512)
-                    *reinterpret_cast<u32x4*>(dst + (size_t)qd * 16) = *reinterpret_cast<const u32x4*>(stg + (size_t)qd * 16);
+                    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stg + (size_t)qd * 16), reinterpret_cast<u32x4*>(dst + (size_t)qd * 16));
             }
         }
         if (more) store_tile(xs[cur ^ 1]);
@@ -802,7 +803,7 @@ __global__ __launch_bounds__(256) void k_cmp_f32(CmpArgs a) {
                 __syncthreads();
                 const int nq = ns * c * 5 / 16;
                 for (int qd = tid; qd < nq; qd += 256)
-                    *reinterpret_cast<u32x4*>(dst + (size_t)qd * 16) = *reinterpret_cast<const u32x4*>(stg + (size_t)qd * 16);
+                    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stg + (size_t)qd * 16), reinterpret_cast<u32x4*>(dst + (size_t)qd * 16));
             }
         }
         __syncthreads();
