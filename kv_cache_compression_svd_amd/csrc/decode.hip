@@ -469,6 +469,22 @@ __device__ __forceinline__ void find_bin1024(const uint32_t* h, uint32_t need, u
     __syncthreads();
 }
 
+// Lists at least this long are read four entries per thread at a time (the loads' latencies overlap); shorter
+// ones one entry at a time (the batching's extra loads and code cost more there: measured on a 32768-token layer
+// and the ragged mix)
+constexpr uint32_t kBatchedList = 8192;
+
+// Entries i0, i0 + 1024, i0 + 2048, i0 + 3072 of a list of n >= 1 entries (indices past the end re-read the last
+// entry, which the caller skips), loaded together so that their latencies overlap.
+__device__ __forceinline__ void load4_entries(const uint2* list, uint32_t i0, uint32_t n, uint2 (&e)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) e[u] = list[min(i0 + u * 1024, n - 1)];
+}
+__device__ __forceinline__ void load4_keys(const uint2* list, uint32_t i0, uint32_t n, uint32_t (&k)[4]) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) k[u] = list[min(i0 + u * 1024, n - 1)].y;
+}
+
 // Tokens per bitmap tile of the emit kernel: one 32-bit word per thread of a 1024-thread workgroup.
 constexpr int kTileWords = 1024;
 constexpr int kTileBits = kTileWords * 32;
@@ -519,16 +535,36 @@ __global__ __launch_bounds__(1024) void k_sel_emit(DecArgs a) {
         if (!all) {
             h[tid] = 0u;
             __syncthreads();
-            for (uint32_t i = tid; i < ncand; i += 1024) atomicAdd(&h[(cand[i].y >> 10) & 1023u], 1u);
+            if (ncand >= kBatchedList) {
+                for (uint32_t i0 = tid; i0 < ncand; i0 += 4 * 1024) {
+                    uint32_t kv[4];
+                    load4_keys(cand, i0, ncand, kv);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (i0 + u * 1024 < ncand) atomicAdd(&h[(kv[u] >> 10) & 1023u], 1u);
+                }
+            } else {
+                for (uint32_t i = tid; i < ncand; i += 1024) atomicAdd(&h[(cand[i].y >> 10) & 1023u], 1u);
+            }
             __syncthreads();
             find_bin1024(h, need, tmp, res);
             const uint32_t b2 = res[0], need2 = res[1];
             const uint32_t pre22 = (p1 << 10) | b2;
             h[tid] = 0u;
             __syncthreads();
-            for (uint32_t i = tid; i < ncand; i += 1024) {
-                const uint32_t key = cand[i].y;
-                if ((key >> 10) == pre22) atomicAdd(&h[key & 1023u], 1u);
+            if (ncand >= kBatchedList) {
+                for (uint32_t i0 = tid; i0 < ncand; i0 += 4 * 1024) {
+                    uint32_t kv[4];
+                    load4_keys(cand, i0, ncand, kv);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (i0 + u * 1024 < ncand && (kv[u] >> 10) == pre22) atomicAdd(&h[kv[u] & 1023u], 1u);
+                }
+            } else {
+                for (uint32_t i = tid; i < ncand; i += 1024) {
+                    const uint32_t key = cand[i].y;
+                    if ((key >> 10) == pre22) atomicAdd(&h[key & 1023u], 1u);
+                }
             }
             __syncthreads();
             find_bin1024(h, need2, tmp, res);
@@ -572,17 +608,32 @@ __global__ __launch_bounds__(1024) void k_sel_emit(DecArgs a) {
         bm[tid] = 0u;
         __syncthreads();
         uint32_t c = 0;
-        for (uint32_t i = tid; i < ngt; i += 1024) {
-            const int x = (int)L[i].x;
-            if (x < t0) ++c;
-            else if (x < t0 + kTileBits) atomicOr(&bm[(x - t0) >> 5], 1u << ((x - t0) & 31));
-        }
-        for (uint32_t i = tid; i < ncand; i += 1024) {
-            const uint2 e = cand[i];
-            if (!taken(e)) continue;
+        auto mark = [&](const uint2 e) {
             const int x = (int)e.x;
             if (x < t0) ++c;
             else if (x < t0 + kTileBits) atomicOr(&bm[(x - t0) >> 5], 1u << ((x - t0) & 31));
+        };
+        if (ngt + ncand >= kBatchedList) {
+            for (uint32_t i0 = tid; i0 < ngt; i0 += 4 * 1024) {
+                uint2 e[4];
+                load4_entries(L, i0, ngt, e);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (i0 + u * 1024 < ngt) mark(e[u]);
+            }
+            for (uint32_t i0 = tid; i0 < ncand; i0 += 4 * 1024) {
+                uint2 e[4];
+                load4_entries(cand, i0, ncand, e);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (i0 + u * 1024 < ncand && taken(e[u])) mark(e[u]);
+            }
+        } else {
+            for (uint32_t i = tid; i < ngt; i += 1024) mark(L[i]);
+            for (uint32_t i = tid; i < ncand; i += 1024) {
+                const uint2 e = cand[i];
+                if (taken(e)) mark(e);
+            }
         }
         uint32_t before = 0;
         block_exscan(c, tmp, &before);   // its barriers also order the bitmap writes before emit_tile's reads
