@@ -246,7 +246,8 @@ def dense_leg(mkv, torch, dev, inp, args, K, V, q, compressed_ms):
     for _ in range(args.warmup):
         dstep()
     torch.cuda.synchronize()
-    mkv.mkv_profile_start(kernels=["dense_attend"])
+    # events on the attention kernel of the first quarter of the steps, as for the compressed step
+    mkv.mkv_profile_start(max_launches=max(1, args.steps // 4), kernels=["dense_attend"])
     t0 = time.perf_counter()
     for _ in range(args.steps):
         dstep()
