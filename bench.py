@@ -6,7 +6,8 @@ key, top-T selection, exact sparse attention, output rotation) for one layer of 
 built once per run by the library's compression call, which is timed as its own leg and reported under
 "compress".  The printed JSON line reports context tokens per second (sum of the requests' contexts divided by
 the step time), the roofline of the dominant kernel (the score gather-dot, HBM-bound) from HIP events recorded
-around its launches inside the timed region, and the CPU oracle timed on a bounded sample of the same workload.
+around its launches in the first quarter of the timed region, and the CPU oracle timed on a bounded sample of the
+same workload.
 The other workloads of the target (one 1048576-token request, the 16-request ragged mix) and the single-layer
 Llama-3.1-8B shape are measured with the same compress and decode legs and reported under "workloads", each with
 the uncompressed baseline on its inputs.
@@ -108,7 +109,8 @@ def store_bytes(codes: np.ndarray, cu, Hkv: int, keep, bv: int):
 def decode_leg(mkv, torch, dev, inp, args, K, V, q, basis, detailed: bool):
     """Compresses the workload once (timed as its own leg), then times decode steps: warmup, an optional
     per-kernel breakdown and unprofiled region (detailed), and the timed region of exactly ``args.steps`` steps
-    with HIP events around the score kernel only.  Returns (result dict, handles for further extras)."""
+    with HIP events around the score kernel of its first quarter.  Returns (result dict, handles for further
+    extras)."""
     w = inp.workload
     bv = 2 if w.dtype == "bf16" else 4
     policy = mkv.mkv_default_policy()
@@ -231,7 +233,7 @@ def decode_leg(mkv, torch, dev, inp, args, K, V, q, basis, detailed: bool):
 
 def dense_leg(mkv, torch, dev, inp, args, K, V, q, compressed_ms):
     """The uncompressed baseline on the same inputs (bf16 only): the whole call timed, HIP events around its
-    attention kernel."""
+    attention kernel in the first quarter of the steps."""
     w = inp.workload
     bv = 2
     total_tokens = int(inp.cu_seqlens[-1])
