@@ -335,7 +335,9 @@ __global__ __launch_bounds__(256) void k_score(DecArgs a) {
     }
     __syncthreads();
     // flush the non-empty fine and coarse bins into one of the stream's histogram copies
-    const int copy = (int)(blockIdx.x & (uint32_t)(a.hcopies - 1));
+    // copy: by the XCD the workgroup runs on (hardware register XCC_ID), so that each XCD's workgroups update
+    // their own copy
+    const int copy = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & (a.hcopies - 1);
     uint32_t* gh = a.hist + ((size_t)stream * a.hcopies + copy) * kHistBins;
 #pragma unroll 4
     for (int j = tid; j < kHistBins; j += 256) {
