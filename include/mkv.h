@@ -101,7 +101,11 @@ mkv_status mkv_compress_bytes(const mkv_kv_desc* kv, const mkv_seg_policy* polic
  * S = n_kv_heads * sum_r S_r, where cap_r is request r's token capacity (its context n_r, unless the store is
  * growable; slots past the context are unused).  Segment g has a uint8 code (index into policy.keep, c = keep[code]) and a uint64
  * byte offset into the payload; its payload is [n_s][c] values of the storage dtype, followed, when c < 128, by
- * [n_s][c] uint8 channel indices; each token's channels are in ascending order and values follow that order. */
+ * [n_s][c] uint8 channel indices; each token's channels are in ascending order and values follow that order.
+ * Segments never overlap and lie inside payload_capacity; the payload total counts their bytes.  Placement: a
+ * bf16 store without capacities is compressed in one pass, each workgroup writing its run of consecutive
+ * segments of one stream back to back from the run's first slot at full size (slot g at byte g * 64*128*2, so
+ * unused bytes lie between runs); other stores hold all segments back to back in slot order. */
 mkv_status mkv_compress(const mkv_kv_desc* kv, const float* basis, const mkv_seg_policy* policy,
                         void* store_buf, size_t store_bytes, void* scratch, size_t scratch_bytes,
                         mkv_stream_t stream, mkv_store** out);

@@ -39,13 +39,13 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 enum KernelId {
     K_UPLOAD = 0, K_CMP_DECIDE, K_CMP_SCAN, K_CMP_PACK, K_DEC_PREP, K_SCORE, K_SEL_COLLECT, K_SEL_EMIT,
     K_ATTEND, K_COMBINE, K_DENSE_ATTEND, K_DENSE_COMBINE, K_GRAM, K_GRAM_REDUCE, K_APPEND, K_POOL_PLACE, K_POOL_FIX,
-    K_COUNT
+    K_CMP_FUSED, K_COUNT
 };
 static_assert(K_COUNT <= MKV_PROFILE_KERNELS, "kernel ids must fit the profiling arrays and mask");
 const char* kKernelNames[K_COUNT] = {"upload", "compress_decide", "compress_scan", "compress_pack", "decode_prep",
                                      "score", "select_collect", "select_emit", "attend", "combine",
                                      "dense_attend", "dense_combine", "gram", "gram_reduce", "append", "pool_place",
-                                     "pool_fix"};
+                                     "pool_fix", "compress"};
 
 struct Profiler {
     std::mutex mu;
@@ -210,6 +210,10 @@ StoreLayout store_layout(const Shape& sh) {
     L.basis = align_up(L.seg_off + 16 * (uint64_t)sh.S);
     L.payload = align_up(L.basis + (uint64_t)sh.B * sh.Hkv * 2 * MKV_HEAD_DIM * MKV_HEAD_DIM * sizeof(float));
     L.capacity = 2ull * sh.Hkv * (uint64_t)sh.total_cap * MKV_HEAD_DIM * dtype_bytes(sh.dtype);
+    // one-pass bf16 compression starts each workgroup's run of segments at the run's first slot at full size
+    // (64 tokens x 128 channels): room for every slot at full size
+    if (!sh.growable && sh.dtype == MKV_BF16)
+        L.capacity = std::max<uint64_t>(L.capacity, 2ull * (uint64_t)sh.S * MKV_SEG_LEN * MKV_HEAD_DIM * 2);
     // growable stores: the first compression packs each stream's unfinished last segment into the payload like
     // any other; the appends that extend it re-pack it into the stream's open area and seal it at the payload's
     // end, so that first copy stays behind unused.  Room for one such segment (at most 63 rows, all channels)
@@ -232,7 +236,7 @@ struct CmpPlan {
 };
 CmpPlan cmp_plan(const Shape& sh) {
     CmpPlan P;
-    P.spw = std::max<int64_t>(1, std::min<int64_t>(64, (2 * sh.S) / 4096));
+    P.spw = std::max<int64_t>(1, std::min<int64_t>(16, (2 * sh.S) / 4096));
     for (int r = 0; r < sh.B; ++r)
         P.nblk += (int64_t)sh.Hkv * cdiv(cdiv(sh.cu[r + 1] - sh.cu[r], MKV_SEG_LEN), P.spw);
     return P;
@@ -401,6 +405,13 @@ static mkv_status compress(const mkv_kv_desc* kv, const float* basis, const mkv_
     }
     const int dt = sh.dtype == MKV_BF16 ? 1 : 0;
     uint64_t* total = reinterpret_cast<uint64_t*>(base);
+    if (dt == 1 && !sh.growable) {
+        // one pass: the payload counter starts at zero (a kernel writes it, so that the call records no memset)
+        if ((st = upload_words(reinterpret_cast<int32_t*>(base), std::vector<int32_t>(2, 0), 0, stream))) return st;
+        a.total = total;
+        if ((st = run(K_CMP_FUSED, stream, [&] { return launch_cmp_fused(a, stream); }))) return st;
+        return make_handle(sh, policy, basis ? 1 : 0, store_buf, out);
+    }
     if ((st = run(K_CMP_DECIDE, stream, [&] { return launch_cmp_decide(a, dt, stream); }))) return st;
     if ((st = run(K_CMP_SCAN, stream, [&] { return launch_cmp_scan(a.wg_total, 2 * nblk, total, stream); }))) return st;
     if ((st = run(K_CMP_PACK, stream, [&] { return launch_cmp_pack(a, dt, stream); }))) return st;

@@ -2,12 +2,18 @@
 // element selection after an SVD rotation, one compression strategy per KV-cache segment; Observation &
 // Approach 2: the sparse cache is packed into a dense format in GPU memory).
 //
-// Two passes over each 64-token segment tile of one (request, KV head, tensor) stream:
-//   decide: rotate (MFMA), find per-vector magnitude thresholds of the c largest channels, test the energy
-//           rule in float64, pick the segment's kept-channel count; each workgroup records its payload bytes;
-//   scan:   exclusive scan of the workgroup totals -> each workgroup's payload offset;
-//   pack:   rotate again, keep the channels above each vector's threshold (ties: lower channel first), write
-//           each segment as one contiguous block (values, then uint8 channel indices) and its offset.
+// Each workgroup walks a run of consecutive 64-token segment tiles of one (request, KV head, tensor) stream.
+// bf16 stores of fixed size take one pass:
+//   rotate (MFMA), find per-vector magnitude thresholds of the c largest channels, test the energy rule in
+//   float64, pick the segment's kept-channel count, keep the channels above each vector's threshold (ties:
+//   lower channel first) and write the segment as one contiguous block (values, then uint8 channel indices)
+//   right after the run's previous segment.  Each run starts at the payload position of its first segment
+//   slot at full size (64 x 128 values), so runs never overlap and need no scan; the bytes between the end of
+//   a run and the next run's start stay unused.
+// Growable stores, paged pools and float32 stores take two passes, which pack every run back to back:
+//   decide: the same decisions, storing the thresholds; each workgroup records its payload bytes;
+//   scan:   exclusive scan of the workgroup totals -> each workgroup's payload offset (pools: pages instead);
+//   pack:   rotate again and write the segments as above at the scanned offsets.
 // The rotation of bf16 data multiplies the bf16 tile by the fp32 basis split into three bf16 parts
 // (hi + mid + lo carries 24 significant bits), accumulating in fp32; fp32 data is rotated in float64 on the
 // vector ALUs.
@@ -388,6 +394,8 @@ __device__ __forceinline__ int segment_code8(int best, bool valid, int* s_code) 
 // in LDS, the next one loaded while the current one is rotated and selected.
 // =====================================================================================================
 constexpr int XS = 136;   // LDS row stride in u16 (272 B: 16-B aligned, skews banks between rows)
+// kernel modes: the decide pass, the pack pass, or both in one pass (segment runs at their slot positions)
+constexpr int kCmpDecide = 0, kCmpPack = 1, kCmpFused = 2;
 
 // MFMA B fragments of basis columns [16 wid, 16 wid + 16): the float32 basis split into three bf16 parts
 // (hi + mid + lo), so that the bf16 products summed in float32 reproduce the float32 basis.  The same
@@ -435,9 +443,16 @@ __device__ __forceinline__ void rotate_tile(const uint16_t* X, uint16_t* xh, con
 
 // Four waves per SIMD (128 registers) so that two workgroups share a CU and one's MFMA rotation overlaps the
 // other's threshold search; the compiler keeps part of the basis fragments in scratch to fit.
-template <bool PACK>
+template <int MODE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_cmp_bf16(CmpArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][64 * XS];
+    constexpr bool PACK = MODE == kCmpPack, DECIDE = MODE != kCmpPack, WRITE = MODE != kCmpDecide;
+    // decide and one-pass modes keep the lo parts of the basis fragments in LDS (8 waves x 4 KB) instead of
+    // registers, and then use one tile buffer: with a basis the input tile is read only by the rotation, so the
+    // next tile can land in the same buffer at the end of the segment.  Without a basis (the decision reads the
+    // input tile itself) the lo area is the second tile buffer; the pack pass keeps two buffers and registers.
+    constexpr bool LO_LDS = MODE != kCmpPack;
+    __shared__ __attribute__((aligned(16))) uint16_t xs0[64 * XS];
+    __shared__ __attribute__((aligned(16))) uint16_t xsB[LO_LDS ? 8 * 4 * 64 * 8 : 64 * XS];
     __shared__ __attribute__((aligned(16))) uint16_t xh[64 * XS];
     __shared__ __attribute__((aligned(16))) uint8_t stg[64 * 64 * 3];
     __shared__ int s_code[8];
@@ -468,7 +483,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
                 bmid[ks][i] = __builtin_bit_cast(__bf16, (unsigned short)mb);
                 blo[ks][i] = __builtin_bit_cast(__bf16, (unsigned short)lb);
             }
+        if (LO_LDS) {   // each wave's own 4 KB, read back by the same lanes only
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) reinterpret_cast<bf16x8*>(xsB)[(wid * 4 + ks) * 64 + lane] = blo[ks];
+        }
     }
+    const bool dbl = !LO_LDS || !Bm;   // two tile buffers
+    uint16_t* const xb0 = xs0;
+    uint16_t* const xb1 = dbl ? xsB : xs0;
     // tile rows: thread -> row tid/8, 16 channels (32 bytes) starting at 16 * (tid % 8)
     const int lrow = tid >> 3, lq = tid & 7;
     u32x4 r0 = {0, 0, 0, 0}, r1 = {0, 0, 0, 0};
@@ -491,11 +513,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     };
     if (t.s0 < t.s1) {
         load_tile(t.s0);
-        store_tile(xs[0]);
+        store_tile(xb0);
     }
     if (tid < 8) s_fail[tid >> 2][tid & 3] = 0;
-    uint64_t wg_bytes = 0;                                  // decide: payload bytes of this workgroup
-    uint64_t wg_off = PACK ? a.wg_total[blockIdx.x] : 0;    // pack: offset of this workgroup's first segment
+    uint64_t wg_bytes = 0;   // decide, one pass: payload bytes of this workgroup
+    // offset of this workgroup's first segment: scanned (pack) or its full-size slot position (one pass)
+    uint64_t wg_off = PACK ? a.wg_total[blockIdx.x]
+                    : MODE == kCmpFused ? (uint64_t)(t.seg0 + t.s0) * (MKV_SEG * MKV_D * 2) : 0;
     // pack: the segment code and this thread's vector's thresholds are loaded one segment ahead, so that their
     // latency overlaps the previous segment
     int code_n = 0;
@@ -522,8 +546,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
             load_tile(s + 1);
             if (PACK) load_meta(s + 1);
         }
-        const uint16_t* X = xs[cur];
+        const uint16_t* X = cur ? xb1 : xb0;
         if (Bm) {
+            if (LO_LDS) {
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) blo[ks] = reinterpret_cast<const bf16x8*>(xsB)[(wid * 4 + ks) * 64 + lane];
+            }
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt) {
                 f32x4 am = {0, 0, 0, 0}, ac = {0, 0, 0, 0};
@@ -546,17 +574,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         const int v = tid >> 3, p = tid & 7;
         const bool valid = v < ns;
         uint32_t w[8];
-        {
+        auto read_vector = [&]() {
             const u32x4* rp = reinterpret_cast<const u32x4*>(&R[v * XS + p * 16]);
             const u32x4 x0 = rp[0], x1 = rp[1];
             w[0] = x0.x; w[1] = x0.y; w[2] = x0.z; w[3] = x0.w;
             w[4] = x1.x; w[5] = x1.y; w[6] = x1.z; w[7] = x1.w;
-        }
-        if (!PACK) {
+        };
+        read_vector();
+        int code_f = 0;
+        uint32_t thr_f = 0;
+        if (DECIDE) {
             uint32_t thr[4] = {0, 0, 0, 0};
             const int best = vector_decide8(w, a, thr, valid, s_fail[cur]);
-            const int code = segment_code8(best, valid, s_code);
-            if (valid && p == 0) {
+            const int code = uni(segment_code8(best, valid, s_code));   // the same in every thread
+            if (MODE == kCmpDecide && valid && p == 0) {
                 uint16_t* tp = a.thr + thr_index(a, t, tokS + v);
                 for (int k = 1; k < a.n_keep; ++k) tp[k] = (uint16_t)thr[k];
             }
@@ -565,8 +596,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
                 a.codes[gs] = (uint8_t)code;
                 wg_bytes += (uint64_t)ns * c * (2 + (c < MKV_D ? 1 : 0));
             }
-        } else {
-            const int code = code_c;
+            code_f = code;
+            thr_f = code == 1 ? thr[1] : code == 2 ? thr[2] : thr[3];
+            // the vector again from LDS (past the barrier in segment_code8) rather than held across the search
+            if (MODE == kCmpFused) read_vector();
+        }
+        if (WRITE) {
+            const int code = PACK ? code_c : code_f;
             const int c = a.keep[code];
             uint8_t* dst = a.payload + (a.preplaced ? a.seg_off[gs] : wg_off);
             if (!a.preplaced && tid == 0) a.seg_off[gs] = wg_off;
@@ -589,7 +625,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
                 }
             } else {
                 if (valid) {
-                    const uint32_t tt = ((code & 2) ? thr_c.y : thr_c.x) >> (16 * (code & 1)) & 0xFFFFu;
+                    const uint32_t tt = PACK ? ((code & 2) ? thr_c.y : thr_c.x) >> (16 * (code & 1)) & 0xFFFFu : thr_f;
                     vector_pack8(w, tt, c, v, p, ns, stg);
                 }
                 __syncthreads();
@@ -598,9 +634,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
                     __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(stg + (size_t)qd * 16), reinterpret_cast<u32x4*>(dst + (size_t)qd * 16));
             }
         }
-        if (more) store_tile(xs[cur ^ 1]);
+        if (more) store_tile(cur ? xb0 : xb1);
     }
-    if (!PACK && tid == 0) a.wg_total[blockIdx.x] = wg_bytes;
+    if (MODE == kCmpDecide && tid == 0) a.wg_total[blockIdx.x] = wg_bytes;
+    if (MODE == kCmpFused && tid == 0 && wg_bytes) atomicAdd(reinterpret_cast<unsigned long long*>(a.total), wg_bytes);
 }
 
 // =====================================================================================================
@@ -818,7 +855,7 @@ static hipError_t launch_cmp(const CmpArgs& a, int dtype, hipStream_t s) {
     const dim3 grid(2 * a.nblk), block(256);
     if (a.nblk == 0) return hipSuccess;
     if (dtype == 1) {
-        launch_kernel(k_cmp_bf16<PACK>, grid, dim3(512), 0, s, a);
+        launch_kernel(k_cmp_bf16<PACK ? kCmpPack : kCmpDecide>, grid, dim3(512), 0, s, a);
     } else {
         static bool attr_set = false;
         if (!attr_set) {
@@ -832,6 +869,11 @@ static hipError_t launch_cmp(const CmpArgs& a, int dtype, hipStream_t s) {
 
 hipError_t launch_cmp_decide(const CmpArgs& a, int dtype, hipStream_t s) { return launch_cmp<false>(a, dtype, s); }
 hipError_t launch_cmp_pack(const CmpArgs& a, int dtype, hipStream_t s) { return launch_cmp<true>(a, dtype, s); }
+hipError_t launch_cmp_fused(const CmpArgs& a, hipStream_t s) {
+    if (a.nblk == 0) return hipSuccess;
+    launch_kernel(k_cmp_bf16<kCmpFused>, dim3(2 * a.nblk), dim3(512), 0, s, a);
+    return hipGetLastError();
+}
 
 // =====================================================================================================
 // exclusive scan of the workgroup payload totals (one workgroup, tiles of 1024)

@@ -68,6 +68,7 @@ struct CmpArgs {
                                 // open slot (the request's index, or its id in a pool)
     int64_t open_elems;         // elements per stream in open_rows
     int32_t preplaced;          // pack: seg_off already holds every segment's payload offset (paged pools)
+    uint64_t* total;            // one pass: payload bytes in use (zero before the launch; each workgroup adds)
 };
 
 // Paged pools: placement of the segments of the requests being added (tab as in CmpArgs).
@@ -110,6 +111,7 @@ hipError_t launch_cmp_append(const CmpArgs& a, const AppendArgs& x, int n_reques
 hipError_t launch_cmp_decide(const CmpArgs& a, int dtype, hipStream_t s);
 hipError_t launch_cmp_scan(uint64_t* wg_total, int64_t count, uint64_t* total, hipStream_t s);
 hipError_t launch_cmp_pack(const CmpArgs& a, int dtype, hipStream_t s);
+hipError_t launch_cmp_fused(const CmpArgs& a, hipStream_t s);
 hipError_t launch_pool_place(const PoolArgs& p, int n_streams, hipStream_t s);
 hipError_t launch_pool_fix(const PoolArgs& p, int n_streams, hipStream_t s);
 

@@ -86,6 +86,29 @@ def slot_layout(info):
     return S_r, seg_base
 
 
+def check_run_layout(seg_off, sizes, store, bv: int):
+    """Segment offsets of a store built by mkv_compress: no two segments overlap and all lie inside the payload;
+    bf16 stores of fixed size (one-pass compression) place each segment at its slot's full-size position
+    (64 x 128 values per slot) or right after the previous slot's segment (a run of one workgroup); the others
+    (two passes) place them back to back in slot order."""
+    info = store.view()
+    off = np.asarray(seg_off, dtype=np.int64)
+    sz = np.asarray(sizes, dtype=np.int64)
+    live = sz > 0
+    if bv == 2 and not info.growable:
+        g = np.arange(off.size, dtype=np.int64)
+        at_slot = off == g * (SEG * D * 2)
+        after_prev = np.zeros(off.size, dtype=bool)
+        after_prev[1:] = off[1:] == off[:-1] + sz[:-1]
+        assert np.all((at_slot | after_prev)[live]), "a segment is neither at its slot nor after its predecessor"
+    else:
+        np.testing.assert_array_equal(off, np.concatenate([[0], np.cumsum(sz)[:-1]]))
+    lo, hi = off[live], off[live] + sz[live]
+    o = np.argsort(lo, kind="stable")
+    assert np.all(lo[o][1:] >= hi[o][:-1]), "segments overlap"
+    assert hi.max(initial=0) <= int(info.payload_capacity)
+
+
 def _stream_from(payload, codes, seg_off, pay_base, keep, r, h, X, S, Hkv, cu, dtype, layout=None) -> Stream:
     """Stream (r, h, X) of a store: cu gives the tokens in use, layout = (S_r, seg_base) the segment slots
     (None: slots follow cu)."""

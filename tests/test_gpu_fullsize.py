@@ -3,8 +3,9 @@
 Each workload (one 4096-token fp32 head, one 32768-token layer, 8 x 131072, 1 x 1048576, the 16 ragged
 requests) is generated, compressed and decoded whole on the GPU with the calls bench.py makes.  The oracle is
 too slow for whole stores at these sizes, so it checks:
-  - every segment: the payload size its code implies, the offsets as the running sum of those sizes, and the
-    store's recorded total;
+  - every segment: the payload size its code implies, offsets that follow the documented placement (runs of
+    consecutive segments from a slot's full-size position for bf16, back to back for fp32) with no overlaps
+    inside the payload, and the store's recorded total;
   - sampled segments (the first, the last and random ones of sampled streams): the oracle compresses the
     segment's 64 input rows on its own (segments are independent) and the rules of the SVD-basis parity test
     apply: values within one storage ulp, a differing channel set only on a magnitude boundary the rotation
@@ -21,7 +22,7 @@ import pytest
 
 import oracle
 import workloads as W
-from _helpers import (SEG, StoreReader, channel_swap_reason, check_decode_unit, check_out, code_difference_reason,
+from _helpers import (SEG, StoreReader, check_run_layout, channel_swap_reason, check_decode_unit, check_out, code_difference_reason,
                       inputs_to_torch, observed_ulps, record_parity, seg_counts)
 
 pytestmark = pytest.mark.gpu
@@ -102,13 +103,13 @@ def test_full_size_sampled_parity(mkv, full_inputs, name):
     out = out.cpu().numpy().astype(np.float64)
     sel = sel.cpu().numpy()
 
-    # every segment: sizes implied by the codes, offsets as their running sum, the recorded total
+    # every segment: sizes implied by the codes; the segments of each run of a stream back to back from the run's
+    # first slot at full size (64 x 128 values), runs apart, all inside the payload; the recorded total
     rd = StoreReader(store, inp.dtype)
     bv = 2 if inp.dtype == "bf16" else 4
     assert np.all(rd.codes < len(rd.keep))
     sizes = rd.segment_bytes(bv)
-    offs = np.concatenate([[0], np.cumsum(sizes)[:-1]]).astype(np.uint64)
-    np.testing.assert_array_equal(rd.seg_off, offs)
+    check_run_layout(rd.seg_off, sizes, store, bv)
     assert rd.total == int(sizes.sum()) == store.payload_bytes()
 
     n, S_r, _ = seg_counts(inp.cu_seqlens)
