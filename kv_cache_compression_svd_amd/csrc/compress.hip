@@ -420,6 +420,16 @@ __device__ __forceinline__ void basis_frags(const float* Bm, int wid, int lane, 
         }
 }
 
+// Two float32 values rounded to bf16 (nearest, ties to even) and packed low | high << 16: the casts compile to
+// gfx950's conversion instruction, which rounds the same way as f32_to_bf16_rne for every finite value.
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+    bf16x2v r;
+    r.x = (__bf16)lo;
+    r.y = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, r);
+}
+
 // Output channels [16 wid, 16 wid + 16) of a 64 x 128 tile: xh = round_bf16(X @ B) (LDS, row stride XS).
 __device__ __forceinline__ void rotate_tile(const uint16_t* X, uint16_t* xh, const bf16x8 (&bh)[4],
                                             const bf16x8 (&bmid)[4], const bf16x8 (&blo)[4], int wid, int lane) {
@@ -429,15 +439,16 @@ __device__ __forceinline__ void rotate_tile(const uint16_t* X, uint16_t* xh, con
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const bf16x8 A = *reinterpret_cast<const bf16x8*>(&X[(16 * mt + (lane & 15)) * XS + 32 * ks + (lane >> 4) * 8]);
-            am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bh[ks], am, 0, 0, 0);
-            ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, blo[ks], ac, 0, 0, 0);
-            ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bmid[ks], ac, 0, 0, 0);
+            am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh[ks], A, am, 0, 0, 0);
+            ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(blo[ks], A, ac, 0, 0, 0);
+            ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bmid[ks], A, ac, 0, 0, 0);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = 16 * mt + (lane >> 4) * 4 + i;
-            xh[row * XS + 16 * wid + (lane & 15)] = (uint16_t)f32_to_bf16_rne(am[i] + ac[i]);
-        }
+        // the product is taken transposed (basis rows times tile columns): this lane holds channels
+        // 16 wid + 4 (lane / 16) .. + 3 of row 16 mt + lane % 16, stored as one 8-byte write
+        u32x2 pk;
+        pk.x = pack2_bf16(am[0] + ac[0], am[1] + ac[1]);
+        pk.y = pack2_bf16(am[2] + ac[2], am[3] + ac[3]);
+        *reinterpret_cast<u32x2*>(&xh[(16 * mt + (lane & 15)) * XS + 16 * wid + 4 * (lane >> 4)]) = pk;
     }
 }
 
@@ -558,15 +569,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
                     const bf16x8 A = *reinterpret_cast<const bf16x8*>(&X[(16 * mt + (lane & 15)) * XS + 32 * ks + (lane >> 4) * 8]);
-                    am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bh[ks], am, 0, 0, 0);
-                    ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, blo[ks], ac, 0, 0, 0);
-                    ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, bmid[ks], ac, 0, 0, 0);
+                    am = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh[ks], A, am, 0, 0, 0);
+                    ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(blo[ks], A, ac, 0, 0, 0);
+                    ac = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bmid[ks], A, ac, 0, 0, 0);
                 }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = 16 * mt + (lane >> 4) * 4 + i;
-                    xh[row * XS + 16 * wid + (lane & 15)] = (uint16_t)f32_to_bf16_rne(am[i] + ac[i]);
-                }
+                // the product is taken transposed (basis rows times tile columns): this lane holds channels
+                // 16 wid + 4 (lane / 16) .. + 3 of row 16 mt + lane % 16, stored as one 8-byte write
+                u32x2 pk;
+                pk.x = pack2_bf16(am[0] + ac[0], am[1] + ac[1]);
+                pk.y = pack2_bf16(am[2] + ac[2], am[3] + ac[3]);
+                *reinterpret_cast<u32x2*>(&xh[(16 * mt + (lane & 15)) * XS + 16 * wid + 4 * (lane >> 4)]) = pk;
             }
             __syncthreads();
         }
