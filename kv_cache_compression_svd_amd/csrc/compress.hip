@@ -250,12 +250,20 @@ __device__ __forceinline__ int swar_count_ge(const uint32_t (&kw)[4], uint32_t t
 
 // Magnitude pattern of the c-th largest of the vector's 128 values, given lo_end with at least c values >= lo_end
 // and the largest value mx: the largest t with count(m >= t) >= c, found by halving the integer range
-// [lo_end, mx].  The range of L bits is cut into phases of up to 7 bits (the top phase takes what is left over):
-// each phase turns the magnitudes into 7-bit keys relative to the range's low end and searches the key bit by bit,
-// counting four keys per 32-bit word; values above the phase's range saturate at key 127 and still count.
+// [lo_end, lo_end + 2^L) with L bits, enough for every vector of the wave (a wider range than a vector needs
+// gives the same t, since no t above mx has c values at or above it; one L per wave keeps the loops uniform).
+// The range is cut into phases of up to 7 bits (the top phase takes what is left over): each phase turns the
+// magnitudes into 7-bit keys relative to the range's low end and searches the key bit by bit, counting four keys
+// per 32-bit word; values above the phase's range saturate at key 127 and still count.
 __device__ __forceinline__ uint32_t vector_threshold8(const uint32_t* mw, uint32_t lo_end, uint32_t mx, int c) {
     uint32_t base = lo_end;
-    const uint32_t wdt = mx - lo_end;
+    uint32_t wdt = mx - lo_end;
+    wdt = max(wdt, (uint32_t)dpp_i<0xB1>((int)wdt));
+    wdt = max(wdt, (uint32_t)dpp_i<0x4E>((int)wdt));
+    wdt = max(wdt, (uint32_t)dpp_i<0x141>((int)wdt));
+    wdt = max(wdt, (uint32_t)dpp_i<0x140>((int)wdt));   // the largest of each row of 16 lanes
+    wdt = max(max((uint32_t)__builtin_amdgcn_readlane((int)wdt, 0), (uint32_t)__builtin_amdgcn_readlane((int)wdt, 16)),
+              max((uint32_t)__builtin_amdgcn_readlane((int)wdt, 32), (uint32_t)__builtin_amdgcn_readlane((int)wdt, 48)));
     int L = wdt ? 32 - __clz(wdt) : 0;
     while (L > 0) {
         const int sh = ((L - 1) / 7) * 7;
