@@ -82,8 +82,8 @@ typedef struct mkv_store mkv_store;   /* opaque host handle */
 /* Fills *policy with the default strategy set: seg_len 64, keep {128, 64, 32}, energy_frac 0.9. */
 void mkv_default_policy(mkv_seg_policy* policy);
 
-/* Worst-case store size (every segment at 128 channels) and the scratch size mkv_compress needs.
- * Host-only; enqueues nothing. */
+/* Worst-case store size (every segment at 128 channels; for bf16, every segment slot at 64 tokens) and the
+ * scratch size mkv_compress needs.  Host-only; enqueues nothing. */
 mkv_status mkv_compress_bytes(const mkv_kv_desc* kv, const mkv_seg_policy* policy,
                               size_t* store_bytes, size_t* scratch_bytes);
 
