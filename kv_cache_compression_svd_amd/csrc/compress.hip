@@ -461,7 +461,8 @@ __device__ __forceinline__ void rotate_tile(const uint16_t* X, uint16_t* xh, con
 }
 
 // Four waves per SIMD (128 registers) so that two workgroups share a CU and one's MFMA rotation overlaps the
-// other's threshold search; the compiler keeps part of the basis fragments in scratch to fit.
+// other's threshold search; with the lo basis parts in LDS (decide and one-pass modes) a few registers still
+// spill to scratch, with all three parts in registers (pack pass) none.
 template <int MODE>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void k_cmp_bf16(CmpArgs a) {
     constexpr bool PACK = MODE == kCmpPack, DECIDE = MODE != kCmpPack, WRITE = MODE != kCmpDecide;
