@@ -3,12 +3,16 @@
 The piecewise store reader of the full-size GPU tests: an oracle store laid out in the library's documented
 format (in host memory; attaching only records pointers) reads back stream by stream as the oracle's own
 streams, and the segment sizes and offsets it derives match the layout.  The near-tie selection enumerator:
-the selections it accepts on constructed scores."""
+the selections it accepts on constructed scores.  The placement check of the full-size tests: constructed
+offsets it accepts and rejects."""
+import types
+
 import numpy as np
+import pytest
 
 import oracle
 import workloads as W
-from _helpers import StoreReader, upload_oracle_store, valid_selections
+from _helpers import StoreReader, check_run_layout, upload_oracle_store, valid_selections
 
 
 def test_reader_round_trips_an_oracle_store():
@@ -84,3 +88,37 @@ def test_channel_swap_needs_magnitudes_at_the_cut():
     got2 = ref.copy()
     got2[0], got2[127] = False, True   # swap the largest for the smallest: never explained
     assert not channel_swap_reason(x, got2, ref, 64, 1.0, "bf16")
+
+
+class _InfoOnly:
+    """Stands in for a store: check_run_layout reads only view().growable and view().payload_capacity."""
+
+    def __init__(self, growable, capacity):
+        self._info = types.SimpleNamespace(growable=growable, payload_capacity=capacity)
+
+    def view(self):
+        return self._info
+
+
+def test_run_layout_check():
+    slot = 64 * 128 * 2
+    sizes = np.array([12288, 12288, 6144, 0, 12288, 12288])
+    # one run from slot 0 (three segments back to back), slot 3 unused, a second run from slot 4
+    offs = np.array([0, 12288, 24576, 0, 4 * slot, 4 * slot + 12288])
+    store = _InfoOnly(0, 6 * slot)
+    check_run_layout(offs, sizes, store, 2)
+    ok = offs.copy()
+    ok[5] = 5 * slot                    # a run may start at any slot
+    check_run_layout(ok, sizes, store, 2)
+    bad = offs.copy()
+    bad[1] = 6000                       # neither at its slot nor after its predecessor (and overlapping)
+    with pytest.raises(AssertionError):
+        check_run_layout(bad, sizes, store, 2)
+    with pytest.raises(AssertionError):  # past the payload
+        check_run_layout(offs, sizes, _InfoOnly(0, 5 * slot), 2)
+    # two-pass stores (float32 or growable): back to back in slot order
+    packed = np.concatenate([[0], np.cumsum(sizes)[:-1]])
+    check_run_layout(packed, sizes, _InfoOnly(1, 6 * slot), 2)
+    check_run_layout(packed, sizes, store, 4)
+    with pytest.raises(AssertionError):
+        check_run_layout(offs, sizes, store, 4)
