@@ -1299,6 +1299,7 @@ struct DensePlan {
     int32_t G = 0;
     std::vector<int32_t> tab;    // n | tok0 | T (= n) | first workgroup [B+1]
     int64_t n_blk = 0;
+    int32_t cpw = 1;             // 512-token chunks per workgroup
     uint64_t o_tab = 0, o_part = 0, bytes = 0;
 };
 
@@ -1313,6 +1314,11 @@ mkv_status plan_dense(const mkv_kv_desc* kv, int32_t n_q_heads, bool need_data, 
         return fail(MKV_E_UNSUPPORTED, "query heads per KV head must be 1, 2, 4 or 8 (got %d)", P->G);
     const int B = sh->B;
     P->tab.assign(4 * B + 1, 0);
+    // chunks per workgroup: up to 8 while the grid keeps about 2048 workgroups (8 per CU), so that long
+    // contexts leave few partials for the combine
+    int64_t chunks = 0;
+    for (int r = 0; r < B; ++r) chunks += (int64_t)sh->Hkv * cdiv(sh->cu[r + 1] - sh->cu[r], kDenseChunk);
+    P->cpw = (int32_t)std::max<int64_t>(1, std::min<int64_t>(8, chunks / 2048));
     int64_t blk = 0;
     for (int r = 0; r < B; ++r) {
         const int64_t n = sh->cu[r + 1] - sh->cu[r];
@@ -1320,7 +1326,7 @@ mkv_status plan_dense(const mkv_kv_desc* kv, int32_t n_q_heads, bool need_data, 
         P->tab[B + r] = (int32_t)sh->cu[r];
         P->tab[2 * B + r] = (int32_t)n;
         P->tab[3 * B + r] = (int32_t)blk;
-        blk += (int64_t)sh->Hkv * cdiv(n, kDenseChunk);
+        blk += (int64_t)sh->Hkv * cdiv(n, (int64_t)kDenseChunk * P->cpw);
     }
     P->tab[4 * B] = (int32_t)blk;
     if (blk > INT32_MAX) return fail(MKV_E_UNSUPPORTED, "too many workgroups");
@@ -1362,6 +1368,7 @@ mkv_status mkv_dense_decode_attn(const mkv_kv_desc* kv, const void* q, int32_t n
     d.B = B;
     d.Hkv = sh.Hkv;
     d.G = P.G;
+    d.cpw = P.cpw;
     d.K = static_cast<const uint16_t*>(kv->K);
     d.V = static_cast<const uint16_t*>(kv->V);
     d.q = static_cast<const uint16_t*>(q);
@@ -1380,7 +1387,7 @@ mkv_status mkv_dense_decode_attn(const mkv_kv_desc* kv, const void* q, int32_t n
     a.t_T = tb + 2 * B;
     a.t_ablk = tb + 3 * B;
     a.part = d.part;
-    a.achunk = kDenseChunk;
+    a.achunk = kDenseChunk * P.cpw;   // tokens per partial
     if ((st = run(K_DENSE_COMBINE, stream, [&] { return launch_combine(a, B * sh.Hkv, stream); }))) return st;
     return MKV_OK;
 }

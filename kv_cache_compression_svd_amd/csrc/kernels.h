@@ -164,12 +164,13 @@ hipError_t launch_combine(const DecArgs& a, int n_streams, hipStream_t s);
 // ---- uncompressed baseline ------------------------------------------------------------------------------
 struct DenseArgs {
     int32_t B, Hkv, G;
+    int32_t cpw;                // chunks of kDenseChunk tokens per workgroup (1..8)
     const uint16_t* K;          // bf16 [tokens][Hkv][128]
     const uint16_t* V;
     const uint16_t* q;          // bf16 [B][Hq][128]
     const int32_t* t_n;         // per request: context
     const int32_t* t_tok0;      // per request: first token
-    const int32_t* t_dblk;      // [B+1] first workgroup of each request (Hkv * chunks per request)
+    const int32_t* t_dblk;      // [B+1] first workgroup of each request (Hkv * workgroups per request)
     float* part;                // [blocks][G][130]
 };
 
