@@ -245,10 +245,19 @@ CmpPlan cmp_plan(const Shape& sh) {
 struct ScratchLayout {
     uint64_t tab, thr, wg, bytes;
 };
-ScratchLayout scratch_layout(const Shape& sh) {
+// bf16 stores of fixed size are compressed in one pass, which keeps no thresholds and no workgroup totals
+bool one_pass(const Shape& sh) { return sh.dtype == MKV_BF16 && !sh.growable; }
+// Scratch of a compression: request tables | per-vector thresholds | one payload total per decide workgroup
+// (two passes only).  Paged pools always take the two-pass layout (one_pass_ok false).
+ScratchLayout scratch_layout(const Shape& sh, bool one_pass_ok = false) {
     ScratchLayout L;
     L.tab = 0;
     L.thr = align_up(sizeof(int32_t) * (6ull * sh.B + 1));
+    if (one_pass_ok && one_pass(sh)) {
+        L.wg = L.thr;
+        L.bytes = L.thr;
+        return L;
+    }
     L.wg = align_up(L.thr + 2ull * sh.total * sh.Hkv * 4 * sizeof(uint16_t));
     L.bytes = L.wg + 2ull * std::max<int64_t>(cmp_plan(sh).nblk, 1) * sizeof(uint64_t);
     return L;
@@ -308,7 +317,7 @@ static mkv_status compress_bytes(const mkv_kv_desc* kv, const mkv_seg_policy* po
     if (st) return st;
     if (!store_bytes || !scratch_bytes) return fail(MKV_E_ARG, "output pointers are NULL");
     *store_bytes = store_layout(sh).bytes;
-    *scratch_bytes = scratch_layout(sh).bytes;
+    *scratch_bytes = scratch_layout(sh, true).bytes;
     return MKV_OK;
 }
 
@@ -349,7 +358,7 @@ static mkv_status compress(const mkv_kv_desc* kv, const float* basis, const mkv_
     if (!store_buf || !scratch) return fail(MKV_E_ARG, "store_buf and scratch must be non-NULL");
     if (!aligned(store_buf) || !aligned(scratch)) return fail(MKV_E_ARG, "store_buf and scratch must be 256-byte aligned");
     const StoreLayout L = store_layout(sh);
-    const ScratchLayout SL = scratch_layout(sh);
+    const ScratchLayout SL = scratch_layout(sh, true);
     if (store_bytes < L.bytes) return fail(MKV_E_ARG, "store_bytes %zu < required %llu", store_bytes, (unsigned long long)L.bytes);
     if (scratch_bytes < SL.bytes) return fail(MKV_E_ARG, "scratch_bytes %zu < required %llu", scratch_bytes, (unsigned long long)SL.bytes);
 
@@ -394,8 +403,8 @@ static mkv_status compress(const mkv_kv_desc* kv, const float* basis, const mkv_
     a.codes = base + L.codes;
     a.seg_off = reinterpret_cast<uint64_t*>(base + L.seg_off);
     a.payload = base + L.payload;
-    a.thr = reinterpret_cast<uint16_t*>(scr + SL.thr);
-    a.wg_total = reinterpret_cast<uint64_t*>(scr + SL.wg);
+    a.thr = one_pass(sh) ? nullptr : reinterpret_cast<uint16_t*>(scr + SL.thr);
+    a.wg_total = one_pass(sh) ? nullptr : reinterpret_cast<uint64_t*>(scr + SL.wg);
     for (int k = 0; k < 4; ++k) a.keep[k] = k < policy->n_keep ? policy->keep[k] : 0;
     a.n_keep = policy->n_keep;
     a.frac = policy->energy_frac;
@@ -405,7 +414,7 @@ static mkv_status compress(const mkv_kv_desc* kv, const float* basis, const mkv_
     }
     const int dt = sh.dtype == MKV_BF16 ? 1 : 0;
     uint64_t* total = reinterpret_cast<uint64_t*>(base);
-    if (dt == 1 && !sh.growable) {
+    if (one_pass(sh)) {
         // one pass: the payload counter starts at zero (a kernel writes it, so that the call records no memset)
         if ((st = upload_words(reinterpret_cast<int32_t*>(base), std::vector<int32_t>(2, 0), 0, stream))) return st;
         a.total = total;

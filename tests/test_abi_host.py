@@ -59,9 +59,17 @@ def test_sizes_match_layout():
     b = align(seg_off + 16 * S)
     p = align(b + basis)
     assert sb.value == p + payload + 256    # slack after the payload
-    # scratch: request tables | per-vector thresholds | one payload total per compression workgroup
+    # scratch of a one-pass (bf16, fixed-size) compression: the request tables only
+    assert tb.value == align(4 * (6 * 2 + 1))
+    # float32 (two passes): request tables | per-vector thresholds | one payload total per decide workgroup;
+    # the payload holds every token at 128 channels
+    d32, _ = _desc(batch=2, cu=(0, 100, 300), dtype=mkv.MKV_FP32)
+    st, sb32, tb32 = _bytes(d32, mkv.mkv_default_policy())
+    assert st == mkv.MKV_OK
     nblk = 8 * (2 + 4)                  # one segment per workgroup at this size
-    assert tb.value == align(align(4 * (4 * 2 + 1)) + 2 * 300 * 8 * 4 * 2) + 2 * nblk * 8
+    assert tb32.value == align(align(4 * (6 * 2 + 1)) + 2 * 300 * 8 * 4 * 2) + 2 * nblk * 8
+    b32 = align(seg_off + 16 * S)
+    assert sb32.value == align(b32 + basis) + 2 * 8 * 300 * 128 * 4 + 256
 
 
 @pytest.mark.parametrize("field,value,code", [
